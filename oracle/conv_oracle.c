@@ -1,0 +1,365 @@
+/*
+ * conv_oracle.c -- plain, slow, CPU reference for the fused NHWC conv2d layer
+ * and the four-tile mosaic packer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg do. It shares no code, header, table or constant with the
+ * HIP library.
+ *
+ * What it computes (sources: the nanoinfer README page, section on the naive
+ * nested-loop convolution kept as the reference kernel, and its statement
+ * that a 1x1 stride-1 unpadded convolution is a GEMM on the untouched input;
+ * the zerolat.eu YOLOv4 report, section 7 "Accuracy recovery" table for the
+ * Mish definition and section 4 for the 2x2 mosaic placement):
+ *
+ *   pre[n,ho,wo,co] = B[co] + sum_{kh,kw,ci} X[n, ho*sh-ph+kh, wo*sw-pw+kw,
+ *                                               g*Cg + ci] * W[co,kh,kw,ci]
+ *   with g = co / (Cout/groups), Cg = Cin/groups, X = 0 outside the image.
+ *   (cross-correlation, no kernel flip; zero padding, pad_h on top and
+ *   bottom, pad_w on left and right; output Ho = (H+2ph-KH)/sh + 1.)
+ *
+ * Float inputs (fp32, or bf16 values widened exactly to fp32) accumulate in
+ * double; the activation is applied in double and the result is NOT rounded
+ * to the output type. The absolute-value convolution
+ *   A = |B| + sum |X*W|
+ * is returned beside it so the caller can form a relative error that stays
+ * defined under cancellation.
+ *
+ * int8 inputs accumulate exactly in int64; R32 = acc + bias (checked to fit
+ * int32). The int32 checkpoint output is R32. The int8 output is
+ *   v = fl32( fl32(R32) * s[co] )    (IEEE float32: one RNE convert, one RNE
+ *                                      multiply, no fused multiply-add)
+ *   m = act(v)                        (ReLU/ReLU6 exact in float32, Mish in
+ *                                      double from v)
+ *   Q = clamp(round_half_even(m), -127, 127)
+ *
+ * The loops are written in the order of the definition; OpenMP only splits
+ * independent output rows across threads, which changes no arithmetic.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no -ffast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_RELU6 = 2, ACT_MISH = 3 };
+
+enum {
+  ORC_OK = 0,
+  ORC_E_SHAPE = -2,
+  ORC_E_RANGE = -8 /* int8 accumulator + bias does not fit int32 */
+};
+
+typedef struct {
+  int64_t n, h, w, cin, cout;
+  int64_t kh, kw, sh, sw, ph, pw, groups;
+  int64_t ho, wo;
+} geom_t;
+
+static int make_geom(geom_t *g, int64_t n, int64_t h, int64_t w, int64_t cin,
+                     int64_t cout, int64_t kh, int64_t kw, int64_t sh,
+                     int64_t sw, int64_t ph, int64_t pw, int64_t groups) {
+  if (n <= 0 || h <= 0 || w <= 0 || cin <= 0 || cout <= 0 || kh <= 0 ||
+      kw <= 0 || sh <= 0 || sw <= 0 || ph < 0 || pw < 0 || groups <= 0)
+    return ORC_E_SHAPE;
+  if (cin % groups || cout % groups) return ORC_E_SHAPE;
+  int64_t hp = h + 2 * ph - kh, wp = w + 2 * pw - kw;
+  if (hp < 0 || wp < 0) return ORC_E_SHAPE;
+  g->n = n; g->h = h; g->w = w; g->cin = cin; g->cout = cout;
+  g->kh = kh; g->kw = kw; g->sh = sh; g->sw = sw; g->ph = ph; g->pw = pw;
+  g->groups = groups;
+  g->ho = hp / sh + 1;
+  g->wo = wp / sw + 1;
+  return ORC_OK;
+}
+
+/* Mish(x) = x * tanh(softplus(x)), softplus(x) = ln(1 + e^x), written as
+ * max(x,0) + log1p(exp(-|x|)) so that exp never overflows. */
+double oracle_mish(double x) {
+  double sp = (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+  return x * tanh(sp);
+}
+
+double oracle_act(double x, int act) {
+  switch (act) {
+    case ACT_RELU: return x > 0.0 ? x : 0.0;
+    case ACT_RELU6: return x > 0.0 ? (x < 6.0 ? x : 6.0) : 0.0;
+    case ACT_MISH: return oracle_mish(x);
+    default: return x;
+  }
+}
+
+/* One output element of the float convolution: returns pre-activation in
+ * double and the absolute-value sum through *abs_out. */
+static double conv_point_float(const geom_t *g, const float *x, const float *wt,
+                               const float *b, int64_t n, int64_t ho,
+                               int64_t wo, int64_t co, double *abs_out) {
+  const int64_t cg = g->cin / g->groups;
+  const int64_t og = g->cout / g->groups;
+  const int64_t grp = co / og;
+  double acc = 0.0, aacc = 0.0;
+  if (b) {
+    acc = (double)b[co];
+    aacc = fabs((double)b[co]);
+  }
+  for (int64_t kh = 0; kh < g->kh; ++kh) {
+    int64_t hi = ho * g->sh - g->ph + kh;
+    if (hi < 0 || hi >= g->h) continue;
+    for (int64_t kw = 0; kw < g->kw; ++kw) {
+      int64_t wi = wo * g->sw - g->pw + kw;
+      if (wi < 0 || wi >= g->w) continue;
+      const float *xp = x + ((n * g->h + hi) * g->w + wi) * g->cin + grp * cg;
+      const float *wp = wt + ((co * g->kh + kh) * g->kw + kw) * cg;
+      for (int64_t ci = 0; ci < cg; ++ci) {
+        double p = (double)xp[ci] * (double)wp[ci];
+        acc += p;
+        aacc += fabs(p);
+      }
+    }
+  }
+  *abs_out = aacc;
+  return acc;
+}
+
+static int set_threads(int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  return omp_get_max_threads();
+#else
+  (void)nthreads;
+  return 1;
+#endif
+}
+
+/* Full float convolution. r (required) gets act(pre); a (optional) gets the
+ * absolute-value convolution. Both are [n][ho][wo][cout] doubles. */
+int oracle_conv_float(const float *x, const float *wt, const float *b,
+                      int64_t n, int64_t h, int64_t w, int64_t cin,
+                      int64_t cout, int64_t kh, int64_t kw, int64_t sh,
+                      int64_t sw, int64_t ph, int64_t pw, int64_t groups,
+                      int act, double *r, double *a, int nthreads) {
+  geom_t g;
+  int st = make_geom(&g, n, h, w, cin, cout, kh, kw, sh, sw, ph, pw, groups);
+  if (st) return st;
+  set_threads(nthreads);
+  int64_t rows = g.n * g.ho;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t row = 0; row < rows; ++row) {
+    int64_t nn = row / g.ho, ho = row % g.ho;
+    for (int64_t wo = 0; wo < g.wo; ++wo)
+      for (int64_t co = 0; co < g.cout; ++co) {
+        double ab;
+        double pre = conv_point_float(&g, x, wt, b, nn, ho, wo, co, &ab);
+        int64_t o = ((nn * g.ho + ho) * g.wo + wo) * g.cout + co;
+        r[o] = oracle_act(pre, act);
+        if (a) a[o] = ab;
+      }
+  }
+  return ORC_OK;
+}
+
+/* Same definition evaluated only at the flat output indices idx[0..cnt). */
+int oracle_conv_float_at(const float *x, const float *wt, const float *b,
+                         int64_t n, int64_t h, int64_t w, int64_t cin,
+                         int64_t cout, int64_t kh, int64_t kw, int64_t sh,
+                         int64_t sw, int64_t ph, int64_t pw, int64_t groups,
+                         int act, const int64_t *idx, int64_t cnt, double *r,
+                         double *a, int nthreads) {
+  geom_t g;
+  int st = make_geom(&g, n, h, w, cin, cout, kh, kw, sh, sw, ph, pw, groups);
+  if (st) return st;
+  int64_t total = g.n * g.ho * g.wo * g.cout;
+  for (int64_t i = 0; i < cnt; ++i)
+    if (idx[i] < 0 || idx[i] >= total) return ORC_E_SHAPE;
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t i = 0; i < cnt; ++i) {
+    int64_t o = idx[i];
+    int64_t co = o % g.cout, t = o / g.cout;
+    int64_t wo = t % g.wo;
+    t /= g.wo;
+    int64_t ho = t % g.ho, nn = t / g.ho;
+    double ab;
+    double pre = conv_point_float(&g, x, wt, b, nn, ho, wo, co, &ab);
+    r[i] = oracle_act(pre, act);
+    if (a) a[i] = ab;
+  }
+  return ORC_OK;
+}
+
+/* ---------------------------------------------------------------- int8 -- */
+
+static int64_t conv_point_i8(const geom_t *g, const int8_t *x, const int8_t *wt,
+                             int64_t n, int64_t ho, int64_t wo, int64_t co) {
+  const int64_t cg = g->cin / g->groups;
+  const int64_t og = g->cout / g->groups;
+  const int64_t grp = co / og;
+  int64_t acc = 0;
+  for (int64_t kh = 0; kh < g->kh; ++kh) {
+    int64_t hi = ho * g->sh - g->ph + kh;
+    if (hi < 0 || hi >= g->h) continue;
+    for (int64_t kw = 0; kw < g->kw; ++kw) {
+      int64_t wi = wo * g->sw - g->pw + kw;
+      if (wi < 0 || wi >= g->w) continue;
+      const int8_t *xp = x + ((n * g->h + hi) * g->w + wi) * g->cin + grp * cg;
+      const int8_t *wp = wt + ((co * g->kh + kh) * g->kw + kw) * cg;
+      for (int64_t ci = 0; ci < cg; ++ci) acc += (int64_t)xp[ci] * (int64_t)wp[ci];
+    }
+  }
+  return acc;
+}
+
+/* Requantise one int32 value. Returns the int8 code; *m_out gets the value
+ * the rounding was applied to (as double), so the caller can find elements
+ * that sit on a rounding tie. */
+int oracle_requant(int32_t r32, float s, int act, double *m_out) {
+  volatile float f = (float)r32; /* RNE int -> float */
+  volatile float v = f * s;      /* one RNE float multiply */
+  double m;
+  switch (act) {
+    case ACT_RELU: {
+      float t = v > 0.0f ? v : 0.0f;
+      m = (double)t;
+      break;
+    }
+    case ACT_RELU6: {
+      float t = v > 0.0f ? (v < 6.0f ? v : 6.0f) : 0.0f;
+      m = (double)t;
+      break;
+    }
+    case ACT_MISH: m = oracle_mish((double)v); break;
+    default: m = (double)v; break;
+  }
+  if (m_out) *m_out = m;
+  double q = rint(m); /* default rounding mode: nearest, ties to even */
+  if (q > 127.0) q = 127.0;
+  if (q < -127.0) q = -127.0;
+  return (int)q;
+}
+
+static int i8_point(const geom_t *g, const int8_t *x, const int8_t *wt,
+                    const int32_t *b, const float *s, int act, int out_i32,
+                    int64_t nn, int64_t ho, int64_t wo, int64_t co,
+                    int32_t *y32, int8_t *y8, double *m, int64_t o) {
+  int64_t acc = conv_point_i8(g, x, wt, nn, ho, wo, co);
+  if (b) acc += b[co];
+  if (acc > 2147483647LL || acc < -2147483648LL) return ORC_E_RANGE;
+  int32_t r32 = (int32_t)acc;
+  if (out_i32) {
+    if (act == ACT_RELU && r32 < 0) r32 = 0;
+    y32[o] = r32;
+  } else {
+    double mm;
+    y8[o] = (int8_t)oracle_requant(r32, s[co], act, &mm);
+    if (m) m[o] = mm;
+  }
+  return ORC_OK;
+}
+
+/* Full int8 convolution. out_i32 != 0: y32 gets R32 (act NONE or RELU).
+ * Otherwise y8 gets the requantised code and m (optional) the pre-rounding
+ * value. b may be NULL (zero bias); s is required for int8 output. */
+int oracle_conv_i8(const int8_t *x, const int8_t *wt, const int32_t *b,
+                   const float *s, int64_t n, int64_t h, int64_t w,
+                   int64_t cin, int64_t cout, int64_t kh, int64_t kw,
+                   int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                   int64_t groups, int act, int out_i32, int32_t *y32,
+                   int8_t *y8, double *m, int nthreads) {
+  geom_t g;
+  int st = make_geom(&g, n, h, w, cin, cout, kh, kw, sh, sw, ph, pw, groups);
+  if (st) return st;
+  if (out_i32 && act != ACT_NONE && act != ACT_RELU) return ORC_E_SHAPE;
+  if (!out_i32 && !s) return ORC_E_SHAPE;
+  set_threads(nthreads);
+  int64_t rows = g.n * g.ho;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t row = 0; row < rows; ++row) {
+    int64_t nn = row / g.ho, ho = row % g.ho;
+    for (int64_t wo = 0; wo < g.wo; ++wo)
+      for (int64_t co = 0; co < g.cout; ++co) {
+        int64_t o = ((nn * g.ho + ho) * g.wo + wo) * g.cout + co;
+        if (i8_point(&g, x, wt, b, s, act, out_i32, nn, ho, wo, co, y32, y8, m, o))
+          bad |= 1;
+      }
+  }
+  return bad ? ORC_E_RANGE : ORC_OK;
+}
+
+/* Sampled int8 convolution at flat output indices; outputs are indexed by
+ * sample position i, not by the flat index. */
+int oracle_conv_i8_at(const int8_t *x, const int8_t *wt, const int32_t *b,
+                      const float *s, int64_t n, int64_t h, int64_t w,
+                      int64_t cin, int64_t cout, int64_t kh, int64_t kw,
+                      int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                      int64_t groups, int act, int out_i32,
+                      const int64_t *idx, int64_t cnt, int32_t *y32,
+                      int8_t *y8, double *m, int nthreads) {
+  geom_t g;
+  int st = make_geom(&g, n, h, w, cin, cout, kh, kw, sh, sw, ph, pw, groups);
+  if (st) return st;
+  if (out_i32 && act != ACT_NONE && act != ACT_RELU) return ORC_E_SHAPE;
+  if (!out_i32 && !s) return ORC_E_SHAPE;
+  int64_t total = g.n * g.ho * g.wo * g.cout;
+  for (int64_t i = 0; i < cnt; ++i)
+    if (idx[i] < 0 || idx[i] >= total) return ORC_E_SHAPE;
+  set_threads(nthreads);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 64) reduction(| : bad)
+  for (int64_t i = 0; i < cnt; ++i) {
+    int64_t o = idx[i];
+    int64_t co = o % g.cout, t = o / g.cout;
+    int64_t wo = t % g.wo;
+    t /= g.wo;
+    int64_t ho = t % g.ho, nn = t / g.ho;
+    if (i8_point(&g, x, wt, b, s, act, out_i32, nn, ho, wo, co, y32, y8, m, i))
+      bad |= 1;
+  }
+  return bad ? ORC_E_RANGE : ORC_OK;
+}
+
+/* ------------------------------------------------------------- mosaic -- */
+
+/* IEEE binary32 -> bfloat16 bits, round to nearest, ties to even; NaN stays
+ * a quiet NaN. This is the textbook definition of RNE truncation of the low
+ * 16 mantissa bits. */
+uint16_t oracle_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
+    return (uint16_t)((u >> 16) | 0x0040u);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+/* tiles: [4*m][th][tw][c] float; canvas: [m][2th][2tw][c_pad].
+ * Tile 4i+0 goes top-left, 4i+1 top-right, 4i+2 bottom-left, 4i+3
+ * bottom-right of canvas i; channels c..c_pad-1 are zero.
+ * out_bf16 != 0: canvas holds bf16 bits (uint16); else float. */
+int oracle_mosaic(const float *tiles, int64_t m, int64_t th, int64_t tw,
+                  int64_t c, int64_t c_pad, int out_bf16, void *canvas) {
+  if (m <= 0 || th <= 0 || tw <= 0 || c <= 0 || c_pad < c) return ORC_E_SHAPE;
+  for (int64_t i = 0; i < m; ++i)
+    for (int64_t y = 0; y < 2 * th; ++y)
+      for (int64_t x = 0; x < 2 * tw; ++x) {
+        int64_t quad = 2 * (y >= th) + (x >= tw);
+        const float *src =
+            tiles + (((4 * i + quad) * th + (y % th)) * tw + (x % tw)) * c;
+        int64_t o = ((i * 2 * th + y) * 2 * tw + x) * c_pad;
+        for (int64_t ch = 0; ch < c_pad; ++ch) {
+          float v = ch < c ? src[ch] : 0.0f;
+          if (out_bf16)
+            ((uint16_t *)canvas)[o + ch] = oracle_f32_to_bf16(v);
+          else
+            ((float *)canvas)[o + ch] = v;
+        }
+      }
+  return ORC_OK;
+}
+
+int oracle_num_threads(int nthreads) { return set_threads(nthreads); }

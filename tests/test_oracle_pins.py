@@ -1,0 +1,380 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test ties the oracle to a library routine that computes the same
+textbook definition (torch float64 conv2d on the CPU, numpy matmul), to a
+closed form, to an invariant, or to a fact the pages state (see
+tests/golden/page_facts.json). Each is chosen so that a plausible slip in
+the oracle (flipped kernel, swapped pads, a wrong stride or group index, a
+dropped bias, the wrong activation, round-half-away, clamp to 128) fails.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from hypothesis import given, settings, strategies as st, HealthCheck
+
+from oracle import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
+
+
+def torch_conv_nhwc(x, w, b, stride, pad, groups):
+    """torch.nn.functional.conv2d in float64 on NHWC/OHWI arrays."""
+    xt = torch.from_numpy(np.asarray(x, np.float64)).permute(0, 3, 1, 2)
+    wt = torch.from_numpy(np.asarray(w, np.float64)).permute(0, 3, 1, 2)
+    bt = None if b is None else torch.from_numpy(np.asarray(b, np.float64))
+    y = F.conv2d(xt, wt, bt, stride=stride, padding=pad, groups=groups)
+    return y.permute(0, 2, 3, 1).contiguous().numpy()
+
+
+def torch_act(y, act):
+    t = torch.from_numpy(y)
+    if act == "relu":
+        return F.relu(t).numpy()
+    if act == "relu6":
+        return F.relu6(t).numpy()
+    if act == "mish":
+        return F.mish(t).numpy()
+    return y
+
+
+@st.composite
+def conv_case(draw):
+    groups_dw = draw(st.booleans())
+    c = draw(st.integers(1, 5))
+    if groups_dw:
+        cin = cout = c
+        groups = c
+    else:
+        cin = c
+        cout = draw(st.integers(1, 5))
+        groups = 1
+    kh = draw(st.integers(1, 5))
+    kw = draw(st.integers(1, 5))
+    sh = draw(st.integers(1, 3))
+    sw = draw(st.integers(1, 3))
+    ph = draw(st.integers(0, 5))
+    pw = draw(st.integers(0, 5))
+    h = draw(st.integers(max(1, kh - 2 * ph), 9))
+    w = draw(st.integers(max(1, kw - 2 * pw), 9))
+    n = draw(st.integers(1, 2))
+    seed = draw(st.integers(0, 2 ** 31 - 1))
+    act = draw(st.sampled_from(["none", "relu", "relu6", "mish"]))
+    return dict(n=n, h=h, w=w, cin=cin, cout=cout, kh=kh, kw=kw, sh=sh, sw=sw,
+                ph=ph, pw=pw, groups=groups, seed=seed, act=act)
+
+
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(conv_case())
+def test_float_matches_torch_float64(case):
+    rng = np.random.default_rng(case["seed"])
+    x = rng.uniform(-2, 2, (case["n"], case["h"], case["w"], case["cin"])).astype(np.float32)
+    w = rng.uniform(-1, 1, (case["cout"], case["kh"], case["kw"], case["cin"] // case["groups"])).astype(np.float32)
+    b = rng.uniform(-0.5, 0.5, case["cout"]).astype(np.float32)
+    stride, pad = (case["sh"], case["sw"]), (case["ph"], case["pw"])
+    r, a = oracle.conv_float(x, w, b, stride, pad, case["groups"], case["act"])
+    ref = torch_act(torch_conv_nhwc(x, w, b, stride, pad, case["groups"]), case["act"])
+    assert r.shape == ref.shape
+    # double sums in another order: agree to rounding of the abs sum.
+    assert np.all(np.abs(r - ref) <= 1e-12 * (a + 1.0))
+
+
+@settings(max_examples=100, deadline=None)
+@given(conv_case())
+def test_int8_matches_torch_float64_exactly(case):
+    rng = np.random.default_rng(case["seed"])
+    x = rng.integers(-127, 128, (case["n"], case["h"], case["w"], case["cin"])).astype(np.int8)
+    w = rng.integers(-127, 128, (case["cout"], case["kh"], case["kw"], case["cin"] // case["groups"])).astype(np.int8)
+    b = rng.integers(-16129, 16130, case["cout"]).astype(np.int32)
+    stride, pad = (case["sh"], case["sw"]), (case["ph"], case["pw"])
+    y = oracle.conv_i8(x, w, b, None, stride, pad, case["groups"], "none", out="i32")
+    ref = torch_conv_nhwc(x, w, b, stride, pad, case["groups"])
+    # every partial sum is an integer below 2^53: float64 is exact here.
+    assert np.array_equal(y.astype(np.float64), ref)
+    yr = oracle.conv_i8(x, w, b, None, stride, pad, case["groups"], "relu", out="i32")
+    assert np.array_equal(yr, np.maximum(y, 0))
+
+
+def test_1x1_is_gemm_float_and_int():
+    """nanoinfer README: a 1x1 stride-1 unpadded conv is a GEMM on the input."""
+    rng = np.random.default_rng(1)
+    n, h, w, cin, cout = 2, 5, 7, 13, 11
+    x = rng.uniform(-1, 1, (n, h, w, cin)).astype(np.float32)
+    wt = rng.uniform(-1, 1, (cout, 1, 1, cin)).astype(np.float32)
+    r, _ = oracle.conv_float(x, wt, None)
+    gemm = x.reshape(-1, cin).astype(np.float64) @ wt.reshape(cout, cin).T.astype(np.float64)
+    assert np.allclose(r.reshape(-1, cout), gemm, rtol=0, atol=1e-12)
+    xi = rng.integers(-127, 128, (n, h, w, cin)).astype(np.int8)
+    wi = rng.integers(-127, 128, (cout, 1, 1, cin)).astype(np.int8)
+    y = oracle.conv_i8(xi, wi, None, None, out="i32")
+    gi = xi.reshape(-1, cin).astype(np.int64) @ wi.reshape(cout, cin).T.astype(np.int64)
+    assert np.array_equal(y.reshape(-1, cout).astype(np.int64), gi)
+
+
+@pytest.mark.parametrize("stride,pad,k,tap", [((1, 1), (1, 1), (3, 3), (0, 2)),
+                                               ((2, 3), (2, 1), (5, 4), (4, 1)),
+                                               ((2, 2), (5, 1), (10, 4), (7, 3))])
+def test_delta_kernel_is_a_shift(stride, pad, k, tap):
+    """w = delta at (co=ci, kh0, kw0) gives y[n,h,w,c] = x[n, h*sh-ph+kh0,
+    w*sw-pw+kw0, c] and 0 outside: pins direction (no flip), per-axis pads,
+    strides and NHWC/OHWI indexing."""
+    rng = np.random.default_rng(2)
+    n, h, w, c = 2, 49, 10, 3
+    x = rng.integers(-127, 128, (n, h, w, c)).astype(np.int8)
+    wt = np.zeros((c, k[0], k[1], c), np.int8)
+    for ch in range(c):
+        wt[ch, tap[0], tap[1], ch] = 1
+    y = oracle.conv_i8(x, wt, None, None, stride, pad, 1, "none", out="i32")
+    ho, wo = y.shape[1:3]
+    exp = np.zeros_like(y)
+    for i in range(ho):
+        for j in range(wo):
+            hi = i * stride[0] - pad[0] + tap[0]
+            wi = j * stride[1] - pad[1] + tap[1]
+            if 0 <= hi < h and 0 <= wi < w:
+                exp[:, i, j, :] = x[:, hi, wi, :]
+    assert np.array_equal(y, exp)
+    # the float path agrees on the same integers
+    r, _ = oracle.conv_float(x.astype(np.float32), wt.astype(np.float32), None, stride, pad)
+    assert np.array_equal(r, exp.astype(np.float64))
+
+
+def test_kws_stem_shape_and_per_axis_padding():
+    """nanoinfer README: the 10x4 stem with pad (5, 1); the two pads must not
+    collapse into one. Constant-ones closed form: y = Cin * #valid rows *
+    #valid cols."""
+    facts = json.load(open(GOLDEN))["kws_stem"]
+    h, w = facts["input_hw"]
+    kh, kw = facts["kernel"]
+    ph, pw = facts["pad"]
+    sh, sw = facts["stride"]
+    x = np.ones((1, h, w, 1), np.int8)
+    wt = np.ones((1, kh, kw, 1), np.int8)
+    y = oracle.conv_i8(x, wt, None, None, (sh, sw), (ph, pw), 1, "none", out="i32")
+    assert y.shape == (1, 25, 5, 1)
+    exp = np.zeros((25, 5), np.int64)
+    for i in range(25):
+        rows = sum(1 for t in range(kh) if 0 <= i * sh - ph + t < h)
+        for j in range(5):
+            cols = sum(1 for t in range(kw) if 0 <= j * sw - pw + t < w)
+            exp[i, j] = rows * cols
+    assert np.array_equal(y[0, :, :, 0], exp)
+    # top-left output covers rows -5..4 (5 valid) and cols -1..2 (3 valid)
+    assert y[0, 0, 0, 0] == 15
+    # swapping the pads changes the answer: the axes are really separate
+    ys = oracle.conv_i8(x, wt, None, None, (sh, sw), (pw, ph), 1, "none", out="i32")
+    assert ys.shape != y.shape or not np.array_equal(ys, y)
+
+
+@pytest.mark.parametrize("groups", [1, 4])
+def test_constant_ones_closed_form(groups):
+    n, h, w, c = 1, 6, 5, 4
+    k, s, p = 3, 2, 1
+    x = np.ones((n, h, w, c), np.float32)
+    wt = np.ones((c, k, k, c // groups), np.float32)
+    b = np.zeros(c, np.float32)
+    r, a = oracle.conv_float(x, wt, b, (s, s), (p, p), groups)
+    ho, wo = r.shape[1:3]
+    for i in range(ho):
+        rows = sum(1 for t in range(k) if 0 <= i * s - p + t < h)
+        for j in range(wo):
+            cols = sum(1 for t in range(k) if 0 <= j * s - p + t < w)
+            assert np.all(r[0, i, j, :] == (c // groups) * rows * cols)
+    assert np.array_equal(a, r)
+
+
+def test_linearity_int():
+    rng = np.random.default_rng(3)
+    x1 = rng.integers(-40, 41, (1, 7, 6, 3)).astype(np.int8)
+    x2 = rng.integers(-40, 41, (1, 7, 6, 3)).astype(np.int8)
+    wt = rng.integers(-127, 128, (5, 3, 3, 3)).astype(np.int8)
+    y1 = oracle.conv_i8(x1, wt, None, None, (1, 2), (1, 0), 1, out="i32").astype(np.int64)
+    y2 = oracle.conv_i8(x2, wt, None, None, (1, 2), (1, 0), 1, out="i32").astype(np.int64)
+    y12 = oracle.conv_i8((2 * x1.astype(np.int16) + x2).astype(np.int8), wt, None, None,
+                         (1, 2), (1, 0), 1, out="i32").astype(np.int64)
+    assert np.array_equal(y12, 2 * y1 + y2)
+
+
+def test_bias_is_added_once_per_output():
+    x = np.zeros((1, 3, 3, 2), np.float32)
+    wt = np.ones((4, 3, 3, 2), np.float32)
+    b = np.array([0.25, -0.5, 1.0, 0.0], np.float32)
+    r, a = oracle.conv_float(x, wt, b, (1, 1), (1, 1))
+    assert np.all(r == b.astype(np.float64)[None, None, None, :])
+    assert np.all(a == np.abs(b.astype(np.float64))[None, None, None, :])
+
+
+def test_int32_range_is_checked():
+    cin = 133145  # 133145 * 127^2 > 2^31 - 1
+    x = np.full((1, 1, 1, cin), 127, np.int8)
+    wt = np.full((1, 1, 1, cin), 127, np.int8)
+    with pytest.raises(ValueError):
+        oracle.conv_i8(x, wt, None, None, out="i32")
+
+
+# ------------------------------------------------------------- activations
+
+def test_mish_closed_forms():
+    facts = json.load(open(GOLDEN))["mish_definition"]
+    ln2, ln3 = math.log(2.0), math.log(3.0)
+    assert oracle.mish(0.0) == 0.0
+    assert oracle.mish(ln2) == pytest.approx(0.8 * ln2, rel=1e-15)
+    assert oracle.mish(ln3) == pytest.approx(15.0 / 17.0 * ln3, rel=1e-15)
+    assert oracle.mish(-ln2) == pytest.approx(-5.0 / 13.0 * ln2, rel=1e-15)
+    # slope at zero is tanh(ln 2) = 3/5
+    e = 1e-7
+    assert (oracle.mish(e) - oracle.mish(-e)) / (2 * e) == pytest.approx(float(facts["slope_at_zero"]), rel=1e-8)
+
+
+def test_mish_against_mpmath_and_torch():
+    import mpmath
+    mpmath.mp.dps = 50
+    xs = [-30.0, -20.0, -5.0, -1.1924312145154952, -1.0, -0.3, 0.5, 1.0, 2.0, 7.5, 20.0, 40.0, 100.0]
+    for v in xs:
+        ref = float(mpmath.mpf(v) * mpmath.tanh(mpmath.log(1 + mpmath.exp(mpmath.mpf(v)))))
+        assert oracle.mish(v) == pytest.approx(ref, rel=1e-14, abs=1e-300)
+    t = F.mish(torch.tensor(xs, dtype=torch.float64)).numpy()
+    assert np.allclose([oracle.mish(v) for v in xs], t, rtol=1e-13, atol=0)
+    # minimum of Mish is about -0.30884 near x = -1.19243
+    assert oracle.mish(-1.1924312145154952) == pytest.approx(-0.30884341301725040663, rel=1e-13)
+
+
+def test_mish_equals_page_algebraic_form():
+    """K1's form x - 2x/((1+e^x)^2+1) is the same function (checked where it
+    does not cancel)."""
+    for v in np.linspace(-8, 8, 161):
+        alt = v - 2 * v / ((1 + math.exp(v)) ** 2 + 1)
+        assert oracle.mish(v) == pytest.approx(alt, rel=1e-12, abs=1e-15)
+
+
+def test_hardmish_is_not_mish():
+    facts = json.load(open(GOLDEN))["hardmish_definition"]
+    hard = lambda v: v * min(max(v + 2, 0.0), 2.0) / 2.0
+    assert hard(-2.0) == float(facts["value_at_minus_2"])
+    assert abs(oracle.mish(-2.0) - hard(-2.0)) > 0.25
+
+
+def test_relu_relu6():
+    for v, r, r6 in [(-3.0, 0.0, 0.0), (0.0, 0.0, 0.0), (2.5, 2.5, 2.5), (6.0, 6.0, 6.0), (9.0, 9.0, 6.0)]:
+        assert oracle.act(v, "relu") == r
+        assert oracle.act(v, "relu6") == r6
+        assert oracle.act(v, "none") == v
+
+
+# --------------------------------------------------------------- requant
+
+@pytest.mark.parametrize("r32,s,act,q", [
+    (5, 0.5, "none", 2),        # 2.5 -> 2 (ties to even)
+    (7, 0.5, "none", 4),        # 3.5 -> 4
+    (-5, 0.5, "none", -2),      # -2.5 -> -2
+    (6, 0.25, "none", 2),       # 1.5 -> 2
+    (3, 0.5, "none", 2),        # 1.5 -> 2
+    (1000, 1.0, "none", 127),   # saturate high
+    (-1000, 1.0, "none", -127), # saturate low at -127, not -128
+    (-128, 1.0, "none", -127),
+    (-40, 0.1, "relu", 0),      # ReLU before rounding
+    (90, 0.1, "relu6", 6),      # 9.0 clamps to 6
+    (55, 0.1, "relu6", 6),      # 5.5 -> 6 (tie to even)
+    (45, 0.1, "relu6", 4),      # fl32(45*0.1f) = 4.5000000... -> check below
+    (0, 0.37, "mish", 0),
+    (100, 0.05, "mish", 5),     # Mish(5.0) = 4.99954... -> 5
+    (-100, 0.05, "mish", 0),    # Mish(-5) = -0.0336 -> 0
+])
+def test_requant_hand_values(r32, s, act, q):
+    got, m = oracle.requant(r32, s, act)
+    if (r32, s) == (45, 0.1):
+        # 0.1f is slightly above 0.1, so 45*0.1f rounds to a float just above
+        # 4.5 or exactly 4.5; either way the answer follows from m.
+        q = 5 if m > 4.5 else 4
+    assert got == q
+
+
+def test_requant_uses_float32_multiply():
+    # 16777217 is not representable in float32: it converts to 16777216.
+    q, m = oracle.requant(16777217, 1.0 / 2 ** 20, "none")
+    assert m == 16.0 and q == 16
+    # product rounded to float32 once: 3 * 0.1f
+    q, m = oracle.requant(3, 0.1, "none")
+    assert m == float(np.float32(np.float32(3.0) * np.float32(0.1)))
+
+
+# ------------------------------------------------------------ bf16 / mosaic
+
+def test_bf16_rne_matches_torch_and_ties():
+    rng = np.random.default_rng(4)
+    v = np.concatenate([rng.normal(0, 3, 20000), rng.uniform(-1e30, 1e30, 1000),
+                        [0.0, -0.0, 1e-40, -1e-40, 65504.0, 3.0e38]]).astype(np.float32)
+    got = np.array([oracle.f32_to_bf16_bits(float(t)) for t in v], np.uint16)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+    # exact ties: 1 + 2^-8 sits halfway between 1 and 1 + 2^-7 -> even (1.0)
+    assert oracle.f32_to_bf16_bits(1.0 + 2 ** -8) == 0x3F80
+    # 1 + 3*2^-8 is halfway between 1+2^-7 and 1+2^-6 -> even (1 + 2^-6)
+    assert oracle.f32_to_bf16_bits(1.0 + 3 * 2 ** -8) == 0x3F82
+    assert oracle.f32_to_bf16_bits(float("inf")) == 0x7F80
+
+
+def test_mosaic_matches_numpy_slicing():
+    facts = json.load(open(GOLDEN))["mosaic_placement"]
+    th, tw = 7, 5
+    rng = np.random.default_rng(5)
+    tiles = rng.random((8, th, tw, 3)).astype(np.float32)
+    can = oracle.mosaic(tiles, c_pad=3, out="f32")
+    assert can.shape == (2, 2 * th, 2 * tw, 3)
+    for i in range(2):
+        A, B, C, D = tiles[4 * i: 4 * i + 4]
+        assert np.array_equal(can[i, :th, :tw], A)   # top-left
+        assert np.array_equal(can[i, :th, tw:], B)   # top-right
+        assert np.array_equal(can[i, th:, :tw], C)   # bottom-left
+        assert np.array_equal(can[i, th:, tw:], D)   # bottom-right
+    assert facts["order"][0].startswith("A:top-left")
+    bits = oracle.mosaic(tiles, c_pad=4, out="bf16")
+    ref = torch.from_numpy(np.ascontiguousarray(can)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits[..., :3], ref)
+    assert np.all(bits[..., 3] == 0)
+
+
+def test_depthwise_flop_convention_matches_page():
+    from convolution_conv2d_nhwc_amd.data import Layer
+    f = json.load(open(GOLDEN))["depthwise_flop_count"]
+    L = f["layer"]
+    layer = Layer("dw", L["n"], L["h"], L["w"], L["c"], L["c"], L["k"], L["k"], L["stride"], L["stride"],
+                  L["pad"], L["pad"], L["c"], "f32", "f32", "none", 28, 28)
+    assert round(layer.flops() / 1e6, 1) == f["mflop_rounded"]
+
+
+def test_sampled_equals_full():
+    rng = np.random.default_rng(6)
+    x = rng.uniform(-1, 1, (2, 9, 8, 6)).astype(np.float32)
+    w = rng.uniform(-1, 1, (5, 3, 2, 6)).astype(np.float32)
+    b = rng.uniform(-1, 1, 5).astype(np.float32)
+    r, a = oracle.conv_float(x, w, b, (2, 1), (1, 0), 1, "mish")
+    idx = rng.choice(r.size, 50, replace=False)
+    rs, as_ = oracle.conv_float_at(x, w, b, idx, (2, 1), (1, 0), 1, "mish")
+    assert np.array_equal(rs, r.reshape(-1)[idx]) and np.array_equal(as_, a.reshape(-1)[idx])
+    xi = rng.integers(-127, 128, (2, 9, 8, 6)).astype(np.int8)
+    wi = rng.integers(-127, 128, (5, 3, 2, 6)).astype(np.int8)
+    bi = rng.integers(-16129, 16130, 5).astype(np.int32)
+    si = rng.uniform(0.001, 0.01, 5).astype(np.float32)
+    q, m = oracle.conv_i8(xi, wi, bi, si, (2, 1), (1, 0), 1, "mish")
+    qs, ms = oracle.conv_i8_at(xi, wi, bi, si, idx, (2, 1), (1, 0), 1, "mish")
+    assert np.array_equal(qs, q.reshape(-1)[idx]) and np.array_equal(ms, m.reshape(-1)[idx])
+
+
+def test_requant_elementwise_matches_conv_path():
+    """conv_i8 (int8 out) equals requant applied to its own int32 output."""
+    rng = np.random.default_rng(7)
+    x = rng.integers(-127, 128, (1, 6, 6, 4)).astype(np.int8)
+    w = rng.integers(-127, 128, (3, 3, 3, 4)).astype(np.int8)
+    b = rng.integers(-16129, 16130, 3).astype(np.int32)
+    s = rng.uniform(0.001, 0.01, 3).astype(np.float32)
+    r32 = oracle.conv_i8(x, w, b, None, (1, 1), (1, 1), out="i32")
+    for act in ("none", "relu", "relu6", "mish"):
+        q, _ = oracle.conv_i8(x, w, b, s, (1, 1), (1, 1), 1, act)
+        exp = np.array([oracle.requant(int(v), float(s[i % 3]), act)[0]
+                        for i, v in enumerate(r32.reshape(-1))]).reshape(q.shape)
+        assert np.array_equal(q, exp)
