@@ -1,0 +1,211 @@
+"""ctypes binding of ``libconv_nhwc.so`` (declared in include/conv_nhwc.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library. torch supplies device memory and the current stream. If the library
+has not been built, the first call raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBPATH = os.path.join(_HERE, "libconv_nhwc.so")
+
+DTYPES = {"f32": 0, "bf16": 1, "i8": 2, "i32": 3}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "i32": torch.int32}
+ACTS = {"none": 0, "relu": 1, "relu6": 2, "mish": 3}
+STATUS = {0: "CONV_OK", -1: "CONV_E_NULL", -2: "CONV_E_SHAPE", -3: "CONV_E_UNSUPPORTED",
+          -4: "CONV_E_ALIGN", -5: "CONV_E_ALIAS", -6: "CONV_E_NOMEM", -7: "CONV_E_HIP"}
+
+
+class ConvError(RuntimeError):
+    """A negative conv_status from the library; ``.code`` and ``.name``."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+        self.name = STATUS.get(code, "unknown")
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("h", ctypes.c_int64), ("w", ctypes.c_int64),
+                ("c_in", ctypes.c_int64), ("c_out", ctypes.c_int64),
+                ("kh", ctypes.c_int32), ("kw", ctypes.c_int32),
+                ("stride_h", ctypes.c_int32), ("stride_w", ctypes.c_int32),
+                ("pad_h", ctypes.c_int32), ("pad_w", ctypes.c_int32),
+                ("groups", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("algo", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIBPATH
+
+
+def lib():
+    """Load the HIP library (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIBPATH):
+        raise RuntimeError("libconv_nhwc.so is not built: run `python -m convolution_conv2d_nhwc_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(_LIBPATH)
+    P = ctypes.c_void_p
+    L.conv_prepare.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(P)]
+    L.conv_prepare.restype = ctypes.c_int
+    L.conv_run.argtypes = [P, P, P, P, P, P]
+    L.conv_run.restype = ctypes.c_int
+    L.conv_destroy.argtypes = [P]
+    L.conv_destroy.restype = ctypes.c_int
+    L.conv_out_shape.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+    L.conv_out_shape.restype = ctypes.c_int
+    L.conv_describe.argtypes = [P, ctypes.c_char_p, ctypes.c_int32]
+    L.conv_describe.restype = ctypes.c_int
+    L.conv_algo_count.argtypes = []
+    L.conv_algo_count.restype = ctypes.c_int32
+    L.conv_mosaic_pack.argtypes = [P, ctypes.c_int32, P, ctypes.c_int32] + [ctypes.c_int32] * 5 + [P]
+    L.conv_mosaic_pack.restype = ctypes.c_int
+    L.conv_status_str.argtypes = [ctypes.c_int32]
+    L.conv_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise ConvError(st, "%s: %s" % (what, lib().conv_status_str(st).decode()))
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def conv_out_shape(h, w, kh, kw, stride=(1, 1), pad=(0, 0)):
+    """Output (ho, wo) of a layer, as the library computes it (prepares a
+    throw-away plan)."""
+    c = Conv2d(1, h, w, 1, 1, kh, kw, stride, pad, dtype="bf16")
+    try:
+        return c.out_shape[1], c.out_shape[2]
+    finally:
+        c.close()
+
+
+def pack_bias_scale(bias: torch.Tensor, scale: Optional[torch.Tensor]) -> torch.Tensor:
+    """One int32 block [bias[c_out], scale bits[c_out]] as the int8 layers
+    read it (scale may be None for the int32 checkpoint output)."""
+    b = bias.to(torch.int32).contiguous()
+    if scale is None:
+        return b
+    s = scale.to(torch.float32).contiguous().view(torch.int32)
+    return torch.cat([b, s.to(b.device)])
+
+
+class Conv2d:
+    """A prepared layer (one conv_plan). ``run`` enqueues it on the current
+    torch stream (or ``stream``)."""
+
+    def __init__(self, n: int, h: int, w: int, c_in: int, c_out: int, kh: int, kw: int,
+                 stride: Sequence[int] = (1, 1), pad: Sequence[int] = (0, 0), groups: int = 1,
+                 dtype: str = "bf16", out_dtype: Optional[str] = None, act: str = "none",
+                 algo: int = 0):
+        out_dtype = out_dtype or dtype
+        self.dtype, self.out_dtype, self.act = dtype, out_dtype, act
+        self.groups = groups
+        d = _Desc(n, h, w, c_in, c_out, kh, kw, stride[0], stride[1], pad[0], pad[1], groups,
+                  DTYPES[dtype], DTYPES[out_dtype], ACTS[act], algo)
+        self._plan = ctypes.c_void_p()
+        _check(lib().conv_prepare(ctypes.byref(d), ctypes.byref(self._plan)), "conv_prepare")
+        shp = (ctypes.c_int64 * 4)()
+        _check(lib().conv_out_shape(self._plan, shp), "conv_out_shape")
+        self.out_shape = tuple(int(v) for v in shp)
+        self.in_shape = (n, h, w, c_in)
+        self.w_shape = (c_out, kh, kw, c_in // groups)
+
+    @classmethod
+    def from_layer(cls, layer, algo: int = 0) -> "Conv2d":
+        return cls(layer.n, layer.h, layer.w, layer.cin, layer.cout, layer.kh, layer.kw,
+                   (layer.sh, layer.sw), (layer.ph, layer.pw), layer.groups, layer.dtype,
+                   layer.out, layer.act, algo)
+
+    def describe(self) -> str:
+        buf = ctypes.create_string_buffer(256)
+        _check(lib().conv_describe(self._plan, buf, 256), "conv_describe")
+        return buf.value.decode()
+
+    def empty_output(self, device="cuda") -> torch.Tensor:
+        return torch.empty(self.out_shape, dtype=TORCH_DT[self.out_dtype], device=device)
+
+    def _chk(self, t: torch.Tensor, name: str, dt, shape):
+        if not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+        if t.dtype != dt:
+            raise ValueError("%s dtype %s, expected %s" % (name, t.dtype, dt))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError("%s shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+    def run(self, x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor] = None,
+            y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """x NHWC, w OHWI, b as the header describes (float32[c_out] or the
+        packed int32 block for int8), y NHWC (allocated when None)."""
+        self._chk(x, "x", TORCH_DT[self.dtype], self.in_shape)
+        self._chk(w, "w", TORCH_DT[self.dtype], self.w_shape)
+        if b is not None:
+            want = torch.int32 if self.dtype == "i8" else torch.float32
+            self._chk(b, "b", want, None)
+        if y is None:
+            y = self.empty_output(x.device)
+        self._chk(y, "y", TORCH_DT[self.out_dtype], self.out_shape)
+        st = lib().conv_run(self._plan, x.data_ptr(), w.data_ptr(),
+                            None if b is None else b.data_ptr(), y.data_ptr(), _stream_handle(stream))
+        _check(st, "conv_run")
+        return y
+
+    def run_ptrs(self, x: int, w: int, b: Optional[int], y: int, stream=None) -> int:
+        """Raw call with integer device addresses; returns the conv_status."""
+        return lib().conv_run(self._plan, x, w, b, y, _stream_handle(stream) if stream is not False else None)
+
+    def close(self):
+        if self._plan is not None and self._plan.value:
+            lib().conv_destroy(self._plan)
+        self._plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def mosaic_pack(tiles: torch.Tensor, canvas: Optional[torch.Tensor] = None, c_pad: Optional[int] = None,
+                out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """Pack tiles [4m, th, tw, c] into canvases [m, 2th, 2tw, c_pad]."""
+    if tiles.dim() != 4 or tiles.shape[0] % 4:
+        raise ValueError("tiles must be [4m, th, tw, c]")
+    q, th, tw, c = tiles.shape
+    m = q // 4
+    c_pad = c if c_pad is None else c_pad
+    rev = {torch.float32: 0, torch.bfloat16: 1}
+    if tiles.dtype not in rev or out_dtype not in rev:
+        raise ValueError("mosaic supports float32 and bfloat16")
+    if not tiles.is_cuda or not tiles.is_contiguous():
+        raise ValueError("tiles must be a contiguous device tensor")
+    if canvas is None:
+        canvas = torch.empty((m, 2 * th, 2 * tw, c_pad), dtype=out_dtype, device=tiles.device)
+    if tuple(canvas.shape) != (m, 2 * th, 2 * tw, c_pad) or canvas.dtype != out_dtype or not canvas.is_contiguous():
+        raise ValueError("canvas must be a contiguous [m, 2th, 2tw, c_pad] tensor of out_dtype")
+    st = lib().conv_mosaic_pack(tiles.data_ptr(), rev[tiles.dtype], canvas.data_ptr(), rev[out_dtype],
+                                m, th, tw, c, c_pad, _stream_handle(stream))
+    _check(st, "conv_mosaic_pack")
+    return canvas

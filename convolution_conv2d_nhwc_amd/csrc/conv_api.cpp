@@ -1,0 +1,289 @@
+// conv_api.cpp -- the C ABI of the library (declared in include/conv_nhwc.h).
+//
+// conv_prepare validates a layer description and picks the kernel path and
+// launch shape on the host alone; every unsupported case is a named error at
+// preparation time rather than a wrong answer later (the nanoinfer README's
+// load-time op/dtype validation after an int8-through-float* bug; the SiMa
+// box-decode page's plan step that rejects unsupported profiles before any
+// buffer is bound). conv_run checks pointers, alignment and aliasing, then
+// only enqueues one kernel on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "device_common.h"
+#include "plan.h"
+
+using namespace convnhwc;
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+constexpr int64_t kMaxBytes = (int64_t)1 << 31;  // per tensor, see header
+constexpr int32_t kMaxSmall = 1 << 16;           // kernel, stride, pad limit
+
+int esz_of(int dt) {
+  switch (dt) {
+    case CONV_F32: return 4;
+    case CONV_BF16: return 2;
+    case CONV_I8: return 1;
+    case CONV_I32: return 4;
+    default: return 0;
+  }
+}
+
+// Concurrent workgroups one CU holds for a tile, limited by its LDS (double
+// buffered A and B tiles of 144-byte rows; 160 KiB of LDS per CU) and by the
+// 8 waves of 4-wave groups the register budget of these kernels allows.
+int wg_per_cu(const TileCfg& t) {
+  const int lds = 2 * (t.tco + t.tpx) * 144;
+  return std::max(1, std::min(2, (160 * 1024) / lds));
+}
+
+// Relative MFMA issue efficiency of a tile, from its operand reuse: a wave
+// tile of a x b 16x16 fragments reads (a + b) fragments from LDS per a*b
+// MFMAs. Used only to rank tiles, not to predict time.
+double tile_eff(const TileCfg& t) {
+  const double fa = t.tco / t.wco / 16.0, fb = t.tpx / t.wpx / 16.0;
+  const double reuse = fa * fb / (fa + fb);  // MFMAs per fragment read
+  return reuse / (reuse + 1.0);
+}
+
+// Analytic tile choice: estimated time = (workgroup rounds over 256 CUs) x
+// (padded tile work / tile efficiency). It charges the padding a tile wastes
+// on ragged Cout and pixel counts, and the idle CUs of the last round (wave
+// quantisation), which is what decides small-M layers.
+int choose_tile(const Geometry& g, int esz) {
+  const int kbytes = g.k * esz;
+  const double kpad = (double)((kbytes + 127) / 128) * 128;
+  double best = 1e300;
+  int best_i = 0;
+  for (int i = 0; i < kNumTiles; ++i) {
+    const TileCfg& t = kTiles[i];
+    const long nco = (g.cout + t.tco - 1) / t.tco;
+    const long npx = (g.m + t.tpx - 1) / t.tpx;
+    const long nwg = nco * npx;
+    const long slots = 256L * wg_per_cu(t);
+    const long rounds = (nwg + slots - 1) / slots;
+    const double per_wg = (double)t.tco * t.tpx * kpad / tile_eff(t) / wg_per_cu(t);
+    const double est = rounds * per_wg;
+    if (est < best * 0.999) {
+      best = est;
+      best_i = i;
+    }
+  }
+  return best_i;
+}
+
+bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+}  // namespace
+
+extern "C" {
+
+conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
+  if (!d || !out) return CONV_E_NULL;
+  *out = nullptr;
+  if (d->n <= 0 || d->h <= 0 || d->w <= 0 || d->c_in <= 0 || d->c_out <= 0 || d->kh <= 0 ||
+      d->kw <= 0 || d->stride_h <= 0 || d->stride_w <= 0 || d->pad_h < 0 || d->pad_w < 0 ||
+      d->groups <= 0)
+    return CONV_E_SHAPE;
+  if (d->c_in % d->groups || d->c_out % d->groups) return CONV_E_SHAPE;
+  if (d->kh > kMaxSmall || d->kw > kMaxSmall || d->stride_h > kMaxSmall || d->stride_w > kMaxSmall ||
+      d->pad_h > kMaxSmall || d->pad_w > kMaxSmall)
+    return CONV_E_UNSUPPORTED;
+  if (d->h > kMaxBytes || d->w > kMaxBytes || d->c_in > kMaxBytes || d->c_out > kMaxBytes ||
+      d->n > kMaxBytes)
+    return CONV_E_UNSUPPORTED;
+  const int64_t hp = d->h + 2 * (int64_t)d->pad_h - d->kh;
+  const int64_t wp = d->w + 2 * (int64_t)d->pad_w - d->kw;
+  if (hp < 0 || wp < 0) return CONV_E_SHAPE;
+  const int64_t ho = hp / d->stride_h + 1, wo = wp / d->stride_w + 1;
+
+  // dtype / output / activation combinations
+  const int dt = d->dtype, ot = d->out_dtype;
+  if (!(dt == CONV_F32 && ot == CONV_F32) && !(dt == CONV_BF16 && ot == CONV_BF16) &&
+      !(dt == CONV_I8 && (ot == CONV_I8 || ot == CONV_I32)))
+    return CONV_E_UNSUPPORTED;
+  if (d->act < CONV_ACT_NONE || d->act > CONV_ACT_MISH) return CONV_E_UNSUPPORTED;
+  if (ot == CONV_I32 && d->act != CONV_ACT_NONE && d->act != CONV_ACT_RELU) return CONV_E_UNSUPPORTED;
+
+  const int in_esz = esz_of(dt), out_esz = esz_of(ot);
+  const int64_t cg = d->c_in / d->groups;
+  const int64_t x_bytes = d->n * d->h * d->w * d->c_in * in_esz;
+  const int64_t w_bytes = d->c_out * (int64_t)d->kh * d->kw * cg * in_esz;
+  const int64_t y_bytes = d->n * ho * wo * d->c_out * out_esz;
+  if (x_bytes >= kMaxBytes || w_bytes >= kMaxBytes || y_bytes >= kMaxBytes) return CONV_E_UNSUPPORTED;
+
+  int path;
+  int loader = LOAD_GENERIC;
+  if (d->groups == 1) {
+    path = dt == CONV_F32 ? PATH_F32 : PATH_IGEMM;
+    if (path == PATH_IGEMM) {
+      const bool vec = (d->c_in * in_esz) % 16 == 0;
+      if (vec && d->kh == 1 && d->kw == 1 && d->stride_h == 1 && d->stride_w == 1 && d->pad_h == 0 &&
+          d->pad_w == 0)
+        loader = LOAD_1X1;
+      else if (vec)
+        loader = LOAD_VEC;
+    }
+  } else {
+    if (!(d->groups == d->c_in && d->c_in == d->c_out)) return CONV_E_UNSUPPORTED;
+    if (d->kh != 3 || d->kw != 3) return CONV_E_UNSUPPORTED;
+    path = PATH_DW;
+    loader = (d->c_in * in_esz) % 16 == 0 ? LOAD_VEC : LOAD_GENERIC;
+  }
+  if (d->algo != 0 && (path != PATH_IGEMM || d->algo < 1 || d->algo > kNumTiles)) return CONV_E_UNSUPPORTED;
+
+  conv_plan* p = new (std::nothrow) conv_plan;
+  if (!p) return CONV_E_NOMEM;
+  std::memset(p, 0, sizeof(*p));
+  p->d = *d;
+  Geometry& g = p->g;
+  g.n = (int)d->n;
+  g.h = (int)d->h;
+  g.w = (int)d->w;
+  g.c = (int)d->c_in;
+  g.ho = (int)ho;
+  g.wo = (int)wo;
+  g.cout = (int)d->c_out;
+  g.kh = d->kh;
+  g.kw = d->kw;
+  g.sh = d->stride_h;
+  g.sw = d->stride_w;
+  g.ph = d->pad_h;
+  g.pw = d->pad_w;
+  g.m = (int)(d->n * ho * wo);
+  g.k = (int)(d->kh * d->kw * cg);
+  p->path = path;
+  p->loader = loader;
+  p->in_esz = in_esz;
+  p->out_esz = out_esz;
+  p->out_kind = ot == CONV_F32 ? OUT_F32 : ot == CONV_BF16 ? OUT_BF16 : ot == CONV_I8 ? OUT_I8 : OUT_I32;
+  p->tile = path == PATH_IGEMM ? (d->algo ? d->algo - 1 : choose_tile(g, in_esz)) : 0;
+  p->x_bytes = x_bytes;
+  p->w_bytes = w_bytes;
+  p->y_bytes = y_bytes;
+  p->b_bytes = dt == CONV_I8 ? (ot == CONV_I8 ? 8 * d->c_out : 4 * d->c_out) : 4 * d->c_out;
+  *out = p;
+  return CONV_OK;
+}
+
+conv_status conv_run(const conv_plan* p, const void* x, const void* w, const void* b, void* y,
+                     void* stream) {
+  if (!p || !x || !w || !y) return CONV_E_NULL;
+  const bool i8out = p->d.dtype == CONV_I8 && p->d.out_dtype == CONV_I8;
+  if (i8out && !b) return CONV_E_NULL;
+  if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) & 15) return CONV_E_ALIGN;
+  if ((uintptr_t)b & 3) return CONV_E_ALIGN;
+  if (ranges_overlap(y, p->y_bytes, x, p->x_bytes) || ranges_overlap(y, p->y_bytes, w, p->w_bytes) ||
+      ranges_overlap(y, p->y_bytes, b, p->b_bytes))
+    return CONV_E_ALIAS;
+
+  Epi e;
+  e.act = p->d.act;
+  e.bias = nullptr;
+  e.ibias = nullptr;
+  e.scale = nullptr;
+  if (p->d.dtype == CONV_I8) {
+    e.ibias = static_cast<const int32_t*>(b);
+    e.scale = b ? reinterpret_cast<const float*>(static_cast<const int32_t*>(b) + p->d.c_out) : nullptr;
+    if (!i8out) e.scale = nullptr;
+  } else {
+    e.bias = static_cast<const float*>(b);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  switch (p->path) {
+    case PATH_IGEMM: err = launch_igemm(p, x, w, e, y, s); break;
+    case PATH_DW: err = launch_dw(p, x, w, e, y, s); break;
+    default: err = launch_f32(p, x, w, e, y, s); break;
+  }
+  if (err != hipSuccess) {
+    std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(err));
+    return CONV_E_HIP;
+  }
+  return CONV_OK;
+}
+
+conv_status conv_destroy(conv_plan* p) {
+  delete p;
+  return CONV_OK;
+}
+
+conv_status conv_out_shape(const conv_plan* p, int64_t nhwc[4]) {
+  if (!p || !nhwc) return CONV_E_NULL;
+  nhwc[0] = p->g.n;
+  nhwc[1] = p->g.ho;
+  nhwc[2] = p->g.wo;
+  nhwc[3] = p->g.cout;
+  return CONV_OK;
+}
+
+conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
+  if (!p || !buf || len <= 0) return CONV_E_NULL;
+  static const char* kLoader[] = {"generic", "vec16", "1x1"};
+  static const char* kDt[] = {"f32", "bf16", "i8", "i32"};
+  if (p->path == PATH_IGEMM) {
+    const TileCfg& t = kTiles[p->tile];
+    const long nwg = (long)((p->g.cout + t.tco - 1) / t.tco) * ((p->g.m + t.tpx - 1) / t.tpx);
+    std::snprintf(buf, len, "igemm dtype=%s out=%s loader=%s tile=%d co%dxpx%d waves=%dx%d wgs=%ld m=%d k=%d",
+                  kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], p->tile + 1, t.tco, t.tpx, t.wco,
+                  t.wpx, nwg, p->g.m, p->g.k);
+  } else if (p->path == PATH_DW) {
+    std::snprintf(buf, len, "dw3x3 dtype=%s out=%s loader=%s stride=%dx%d", kDt[p->d.dtype], kDt[p->d.out_dtype],
+                  kLoader[p->loader], p->g.sh, p->g.sw);
+  } else {
+    std::snprintf(buf, len, "direct_f32 m=%d k=%d", p->g.m, p->g.k);
+  }
+  return CONV_OK;
+}
+
+int32_t conv_algo_count(void) { return kNumTiles; }
+
+conv_status conv_mosaic_pack(const void* tiles, int32_t in_dtype, void* canvas, int32_t out_dtype, int32_t m,
+                             int32_t th, int32_t tw, int32_t c, int32_t c_pad, void* stream) {
+  if (!tiles || !canvas) return CONV_E_NULL;
+  if (m <= 0 || th <= 0 || tw <= 0 || c <= 0 || c_pad < c) return CONV_E_SHAPE;
+  if ((in_dtype != CONV_F32 && in_dtype != CONV_BF16) || (out_dtype != CONV_F32 && out_dtype != CONV_BF16))
+    return CONV_E_UNSUPPORTED;
+  const int64_t in_bytes = 4LL * m * th * tw * c * esz_of(in_dtype);
+  const int64_t out_bytes = 4LL * m * th * tw * c_pad * esz_of(out_dtype);
+  if (in_bytes >= kMaxBytes || out_bytes >= kMaxBytes) return CONV_E_UNSUPPORTED;
+  if (((uintptr_t)tiles | (uintptr_t)canvas) & 15) return CONV_E_ALIGN;
+  if (ranges_overlap(tiles, in_bytes, canvas, out_bytes)) return CONV_E_ALIAS;
+  hipError_t err = launch_mosaic(tiles, in_dtype == CONV_F32, canvas, out_dtype == CONV_F32, m, th, tw, c, c_pad,
+                                 static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(err));
+    return CONV_E_HIP;
+  }
+  return CONV_OK;
+}
+
+const char* conv_status_str(int32_t status) {
+  static thread_local char buf[320];
+  switch (status) {
+    case CONV_OK: return "CONV_OK";
+    case CONV_E_NULL: return "CONV_E_NULL: a required pointer is NULL";
+    case CONV_E_SHAPE: return "CONV_E_SHAPE: invalid sizes or empty output";
+    case CONV_E_UNSUPPORTED: return "CONV_E_UNSUPPORTED: layer kind, dtype, activation, algo or size not supported";
+    case CONV_E_ALIGN: return "CONV_E_ALIGN: x, w, y need 16-byte and b 4-byte alignment";
+    case CONV_E_ALIAS: return "CONV_E_ALIAS: output overlaps an input";
+    case CONV_E_NOMEM: return "CONV_E_NOMEM: plan allocation failed";
+    case CONV_E_HIP:
+      std::snprintf(buf, sizeof(buf), "CONV_E_HIP: %s", g_last_hip_error);
+      return buf;
+    default: return "unknown conv_status";
+  }
+}
+
+}  // extern "C"

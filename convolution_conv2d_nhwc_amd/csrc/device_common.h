@@ -1,0 +1,78 @@
+// device_common.h -- types and the fused epilogue shared by the gfx950 kernels.
+//
+// The epilogue is the per-output-element tail of every conv kernel: bias add,
+// activation, and the conversion to the output type, done in registers so the
+// output tensor is written exactly once (nanoinfer README, GPU section: the
+// fused bias/ReLU epilogue removes two extra passes over the output).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convnhwc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+enum Act { ACT_NONE = 0, ACT_RELU = 1, ACT_RELU6 = 2, ACT_MISH = 3 };
+
+// Output kinds of a kernel instance.
+enum OutKind {
+  OUT_F32 = 0,   // float out (fp32 layers)
+  OUT_BF16 = 1,  // bf16 out, one RNE rounding
+  OUT_I8 = 2,    // int8 out through the per-channel requantisation
+  OUT_I32 = 3    // int32 checkpoint (acc + bias, optional ReLU)
+};
+
+// Mish(v) = v * tanh(ln(1 + e^v)) (YOLOv4 on Tenstorrent Wormhole, section 7
+// function table). With t = e^v, tanh(ln(1+t)) = ((1+t)^2 - 1)/((1+t)^2 + 1)
+// = n/(n + 2) where n = t*(t + 2). This form has no cancellation for v << 0
+// (the K1 form v - 2v/((1+t)^2+1) of section 9 subtracts two nearly equal
+// numbers there). For v > 20, n/(n+2) rounds to 1 in fp32, so Mish(v) = v.
+__device__ __forceinline__ float mish_f32(float v) {
+  if (v > 20.0f) return v;
+  const float t = __expf(v);
+  const float n = t * (t + 2.0f);
+  return v * (n / (n + 2.0f));
+}
+
+__device__ __forceinline__ float apply_act(float v, int act) {
+  switch (act) {
+    case ACT_RELU: return fmaxf(v, 0.0f);
+    case ACT_RELU6: return fminf(fmaxf(v, 0.0f), 6.0f);
+    case ACT_MISH: return mish_f32(v);
+    default: return v;
+  }
+}
+
+// int8 requantisation of one int32 value r = acc + bias: an RNE int->float
+// conversion, one RNE float multiply (never fused), the activation, then
+// round-half-to-even and saturation to [-127, 127].
+__device__ __forceinline__ int requant_i8(int r, float s, int act) {
+  const float v = __fmul_rn((float)r, s);
+  const float m = apply_act(v, act);
+  const float q = fminf(fmaxf(__builtin_rintf(m), -127.0f), 127.0f);
+  return (int)q;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  __bf16 h = (__bf16)v;  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// Per-layer epilogue constants. For fp32/bf16 layers `bias` is float[c_out]
+// (or null); for int8 layers `ibias` is int32[c_out] (or null) and `scale`
+// float[c_out] (null only for the int32 checkpoint output).
+struct Epi {
+  const float* bias;
+  const int32_t* ibias;
+  const float* scale;
+  int act;
+};
+
+}  // namespace convnhwc

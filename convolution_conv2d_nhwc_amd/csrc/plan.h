@@ -1,0 +1,67 @@
+// plan.h -- host-side plan and the launchers each kernel file exports to the
+// C-ABI layer (conv_api.cpp). Internal: not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/conv_nhwc.h"
+
+namespace convnhwc {
+
+enum Path {
+  PATH_IGEMM = 1,  // MFMA implicit GEMM (bf16 / int8), dense KxK and 1x1
+  PATH_DW = 2,     // depthwise 3x3, VALU stencil
+  PATH_F32 = 3     // true-fp32 direct convolution, VALU
+};
+
+// How the implicit-GEMM kernel gathers its activation operand.
+enum Loader {
+  LOAD_GENERIC = 0,  // element-wise gather: any channel count
+  LOAD_VEC = 1,      // 16-byte channel vectors: c_in * elem_size % 16 == 0
+  LOAD_1X1 = 2       // 1x1, stride 1, pad 0: the input is the GEMM operand
+};
+
+// One tile configuration of the implicit-GEMM kernel: a workgroup of four
+// wave64s computes tco output channels x tpx output pixels; the waves are
+// arranged wco x wpx.
+struct TileCfg {
+  int tco, tpx, wco, wpx;
+};
+
+constexpr int kNumTiles = 8;
+extern const TileCfg kTiles[kNumTiles];  // index = algo - 1
+
+struct Geometry {
+  int n, h, w, c;        // input
+  int ho, wo, cout;      // output
+  int kh, kw, sh, sw, ph, pw;
+  int m;                 // n * ho * wo (GEMM pixels)
+  int k;                 // kh * kw * c (GEMM reduction length)
+};
+
+}  // namespace convnhwc
+
+struct conv_plan {
+  conv_desc d;
+  convnhwc::Geometry g;
+  int path;
+  int loader;   // PATH_IGEMM
+  int tile;     // PATH_IGEMM: index into kTiles
+  int out_kind; // convnhwc::OutKind
+  int in_esz, out_esz;
+  int64_t x_bytes, w_bytes, y_bytes, b_bytes;
+};
+
+namespace convnhwc {
+
+hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
+                        hipStream_t s);
+hipError_t launch_dw(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
+                     hipStream_t s);
+hipError_t launch_f32(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
+                      hipStream_t s);
+hipError_t launch_mosaic(const void* tiles, int in_f32, void* canvas, int out_f32, int m, int th,
+                         int tw, int c, int c_pad, hipStream_t s);
+
+}  // namespace convnhwc

@@ -9,6 +9,8 @@ tests share.
 Draw recipe (every workload, seed 0 unless a caller asks for another):
   * stream i of a workload is ``default_rng(SeedSequence([seed, i]))``;
     stream 0 draws the network input, stream i >= 1 draws layer i;
+  * stream 1000 + i draws a fresh input for layer i when one layer of a
+    chained workload is tested on its own;
   * a layer stream draws, in order: (its own input ``x`` when the workload
     gives each layer a fresh input), ``w``, ``b``, then ``s`` for int8;
   * float laws are drawn in float64 and cast to float32; bf16 tensors are
@@ -237,6 +239,12 @@ def network_input(wl: Workload, seed: int = 0) -> torch.Tensor:
         m, th, tw, c = wl.mosaic
         return torch.from_numpy(rng.random((4 * m, th, tw, c)).astype(np.float32))
     return _x(wl.layers[0], wl.law, rng)
+
+
+def fresh_input(wl: Workload, i: int, seed: int = 0) -> torch.Tensor:
+    """A fresh seeded input of layer i's shape under the workload's value law
+    (stream 1000 + i), for testing one layer of a chained stack on its own."""
+    return _x(wl.layers[i], wl.law, rng_for(seed, 1000 + i))
 
 
 def random_layer_tensors(layer: Layer, law: str, seed: int, stream: int = 1) -> dict:

@@ -1,0 +1,162 @@
+/*
+ * conv_nhwc.h -- C ABI of the MI355X (gfx950) fused NHWC conv2d library.
+ *
+ * One layer of edge / YOLO-style CNN inference:
+ *
+ *   y = act( conv(x, w) + b )            (fp32, bf16)
+ *   y = requant( conv(x, w) + b, s, act) (int8)
+ *
+ * where conv is the 2-D cross-correlation (no kernel flip) with zero
+ * padding, as used by PyTorch and by the nanoinfer engine (nanoinfer README,
+ * naive reference convolution and its PyTorch parity table). Supported
+ * layer kinds (nanoinfer README, "what is still slow" and GPU section): dense
+ * KxK, 1x1 pointwise, and 3x3 depthwise (groups == Cin == Cout).
+ *
+ * Layouts (all tensors plain, dense, row-major):
+ *   x  NHWC  [n][h][w][c_in]                      dtype
+ *   w  OHWI  [c_out][kh][kw][c_in/groups]          dtype  (K-contiguous)
+ *   y  NHWC  [n][ho][wo][c_out]                    out_dtype
+ *   ho = (h + 2*pad_h - kh) / stride_h + 1, wo likewise (floor division).
+ *   pad_h applies to the top and the bottom edge, pad_w to the left and the
+ *   right edge (the per-axis padding of the keyword-spotting stem, 10x4
+ *   kernel with pad (5,1), nanoinfer README, "Asymmetric padding collapsed
+ *   to one axis").
+ *
+ * Precisions:
+ *   F32  in, F32 out  : true fp32 multiply-add, fp32 accumulate (no
+ *                       reduced-precision matrix mode; nanoinfer README,
+ *                       cuDNN default-math paragraph).
+ *   BF16 in, BF16 out : fp32 accumulate (YOLOv4 on Tenstorrent Wormhole,
+ *                       section 7: 16-bit accumulation lost accuracy, fp32
+ *                       fixed it); one round-to-nearest-even bf16 store.
+ *   I8   in, I8 out   : int32 accumulate; R = acc + bias (int32);
+ *                       v = fl32(fl32(R) * scale[co]); m = act(v);
+ *                       y = clamp(round_half_even(m), -127, 127)
+ *                       (symmetric per-output-channel scales, nanoinfer
+ *                       README, quantization section).
+ *   I8   in, I32 out  : the int32 checkpoint R (act NONE or RELU only).
+ *
+ * Activations (YOLOv4 on Tenstorrent Wormhole, section 7 table):
+ *   NONE, RELU = max(v,0), RELU6 = min(max(v,0),6),
+ *   MISH = v * tanh(ln(1 + e^v))   (the real function, not HardMish).
+ *
+ * Ownership: every device buffer (x, w, b, y, mosaic tiles and canvas) is
+ * owned by the caller. A plan owns only host metadata; it is immutable after
+ * conv_prepare and may be used from any thread and on any stream. conv_run
+ * only enqueues work on the given stream: it allocates nothing, never
+ * synchronises, copies nothing between host and device and caches nothing
+ * between calls (x, w, b are read afresh every call), so it can be captured
+ * into a HIP graph.
+ *
+ * Errors: every entry point returns a conv_status; a negative value names
+ * the failure and nothing was enqueued. Faults inside an enqueued kernel
+ * surface at the caller's next synchronisation, as for any HIP call.
+ *
+ * Size limit: each of x, w and y must be smaller than 2^31 bytes.
+ */
+#ifndef CONV_NHWC_H
+#define CONV_NHWC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum conv_dtype {
+  CONV_F32 = 0,
+  CONV_BF16 = 1,
+  CONV_I8 = 2,
+  CONV_I32 = 3 /* output only: the int32 checkpoint of an int8 layer */
+} conv_dtype;
+
+typedef enum conv_act {
+  CONV_ACT_NONE = 0,
+  CONV_ACT_RELU = 1,
+  CONV_ACT_RELU6 = 2,
+  CONV_ACT_MISH = 3
+} conv_act;
+
+typedef enum conv_status {
+  CONV_OK = 0,
+  CONV_E_NULL = -1,        /* a required pointer is NULL */
+  CONV_E_SHAPE = -2,       /* non-positive size, empty output, c_in or c_out not divisible by groups */
+  CONV_E_UNSUPPORTED = -3, /* groups not in {1, c_in==c_out}, depthwise not 3x3, dtype/out/act combination, size limit, bad algo */
+  CONV_E_ALIGN = -4,       /* x, w or y not 16-byte aligned, or b not 4-byte aligned */
+  CONV_E_ALIAS = -5,       /* y overlaps x, w or b */
+  CONV_E_NOMEM = -6,       /* host allocation of the plan failed */
+  CONV_E_HIP = -7          /* the HIP launch reported an error */
+} conv_status;
+
+/* Description of one layer. All sizes in elements. */
+typedef struct conv_desc {
+  int64_t n, h, w, c_in, c_out;
+  int32_t kh, kw;
+  int32_t stride_h, stride_w;
+  int32_t pad_h, pad_w;   /* each applied to both edges of its axis */
+  int32_t groups;         /* 1, or c_in (== c_out) for depthwise */
+  int32_t dtype;          /* conv_dtype of x and w: F32, BF16 or I8 */
+  int32_t out_dtype;      /* F32 for F32; BF16 for BF16; I8 or I32 for I8 */
+  int32_t act;            /* conv_act */
+  int32_t algo;           /* 0 = the library chooses the kernel and tile;
+                             k > 0 forces tile configuration k of the
+                             implicit-GEMM kernel (see conv_algo_count) */
+} conv_desc;
+
+typedef struct conv_plan conv_plan;
+
+/* Validate d and choose the kernel and its launch shape. Host only: touches
+ * no device. On success *out holds a new plan (free with conv_destroy). */
+conv_status conv_prepare(const conv_desc* d, conv_plan** out);
+
+/* Enqueue the layer on `stream` (a hipStream_t; NULL = the default stream).
+ *   x : device pointer, NHWC of dtype, 16-byte aligned.
+ *   w : device pointer, OHWI of dtype, 16-byte aligned.
+ *   b : F32/BF16 layers: device float[c_out] bias, or NULL for zero bias.
+ *       I8 layers: device block of int32 bias[c_out] immediately followed by
+ *       float scale[c_out] (one allocation, 4-byte aligned). The scales are
+ *       required for I8 output; I32 output reads only the bias and accepts
+ *       NULL (zero bias).
+ *   y : device pointer, NHWC of out_dtype, 16-byte aligned; must not overlap
+ *       x, w or b (a layer reads its input while it writes its output, the
+ *       planner-aliasing bug of the nanoinfer README).
+ * Calls on different streams may run concurrently with one plan. */
+conv_status conv_run(const conv_plan* p, const void* x, const void* w,
+                     const void* b, void* y, void* stream);
+
+/* Free a plan. NULL is a no-op. */
+conv_status conv_destroy(conv_plan* p);
+
+/* Output shape {n, ho, wo, c_out} of a plan. */
+conv_status conv_out_shape(const conv_plan* p, int64_t nhwc[4]);
+
+/* Human-readable description of the chosen kernel path and tile, written
+ * into buf (NUL-terminated, truncated to len). */
+conv_status conv_describe(const conv_plan* p, char* buf, int32_t len);
+
+/* Number of forceable tile configurations (valid algo values are
+ * 1..conv_algo_count()). */
+int32_t conv_algo_count(void);
+
+/* Mosaic packing (YOLOv4 on Tenstorrent Wormhole, section 4, the m640 2x2
+ * layout): four th x tw x c tiles per canvas, tile 4i+0 top-left, 4i+1
+ * top-right, 4i+2 bottom-left, 4i+3 bottom-right of canvas i.
+ *   tiles  : device [4*m][th][tw][c] of in_dtype (F32 or BF16)
+ *   canvas : device [m][2*th][2*tw][c_pad] of out_dtype (F32 or BF16);
+ *            channels c..c_pad-1 are written as zero. fp32 -> bf16 rounds to
+ *            nearest even.
+ * Both pointers 16-byte aligned, non-overlapping; c_pad >= c. */
+conv_status conv_mosaic_pack(const void* tiles, int32_t in_dtype, void* canvas,
+                             int32_t out_dtype, int32_t m, int32_t th,
+                             int32_t tw, int32_t c, int32_t c_pad,
+                             void* stream);
+
+/* Name of a status code ("CONV_OK", "CONV_E_SHAPE", ...). For CONV_E_HIP
+ * the text of the last HIP error seen by this thread is appended. */
+const char* conv_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV_NHWC_H */

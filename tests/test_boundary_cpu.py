@@ -1,0 +1,175 @@
+"""The C-ABI boundary, on the CPU: the library loads, exports every symbol the
+header declares, and rejects every malformed call with a named error before
+anything would be enqueued (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from convolution_conv2d_nhwc_amd import _lib
+from convolution_conv2d_nhwc_amd._lib import Conv2d, ConvError, _Desc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv_nhwc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.library_path()),
+                                reason="libconv_nhwc.so not built")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(conv_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_symbols_are_exported():
+    names = header_functions()
+    assert {"conv_prepare", "conv_run", "conv_destroy", "conv_out_shape", "conv_mosaic_pack",
+            "conv_status_str", "conv_describe", "conv_algo_count"} <= set(names)
+    L = ctypes.CDLL(_lib.library_path())
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (conv_[a-z_0-9]+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def desc(**kw):
+    base = dict(n=1, h=8, w=8, c_in=16, c_out=16, kh=3, kw=3, stride_h=1, stride_w=1, pad_h=1,
+                pad_w=1, groups=1, dtype=1, out_dtype=1, act=0, algo=0)
+    base.update(kw)
+    return _Desc(**base)
+
+
+def prepare(d):
+    p = ctypes.c_void_p()
+    st = _lib.lib().conv_prepare(ctypes.byref(d), ctypes.byref(p))
+    return st, p
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), -2), (dict(h=-1), -2), (dict(c_in=0), -2), (dict(kh=0), -2),
+    (dict(stride_w=0), -2), (dict(pad_h=-1), -2),
+    (dict(h=2, pad_h=0), -2),                      # kernel larger than padded input
+    (dict(groups=3), -2),                          # 16 % 3 != 0
+    (dict(groups=4), -3),                          # grouped, not depthwise
+    (dict(groups=16, kh=5, kw=5, pad_h=2, pad_w=2), -3),  # depthwise must be 3x3
+    (dict(groups=16, c_out=32), -3),               # depthwise needs c_out == c_in (32 % 16 == 0)
+    (dict(dtype=0, out_dtype=1), -3),              # f32 -> bf16 not offered
+    (dict(dtype=1, out_dtype=2), -3),
+    (dict(dtype=2, out_dtype=1), -3),
+    (dict(dtype=5, out_dtype=5), -3),
+    (dict(act=7), -3),
+    (dict(dtype=2, out_dtype=3, act=3), -3),       # int32 checkpoint: NONE/RELU only
+    (dict(dtype=2, out_dtype=3, act=2), -3),
+    (dict(algo=99), -3),
+    (dict(dtype=0, out_dtype=0, algo=1), -3),      # algo only for the MFMA path
+    (dict(n=1, h=1 << 15, w=1 << 15, c_in=8), -3),  # x over 2^31 bytes
+])
+def test_prepare_rejects(kw, code):
+    st, p = prepare(desc(**kw))
+    assert st == code
+    assert not p.value
+    assert _lib.lib().conv_status_str(st).decode().startswith(_lib.STATUS[code])
+
+
+def test_prepare_null():
+    p = ctypes.c_void_p()
+    assert _lib.lib().conv_prepare(None, ctypes.byref(p)) == -1
+    d = desc()
+    assert _lib.lib().conv_prepare(ctypes.byref(d), None) == -1
+
+
+@pytest.mark.parametrize("layer,expect", [
+    (dict(c_in=3, c_out=32, dtype="bf16"), "igemm dtype=bf16 out=bf16 loader=generic"),
+    (dict(c_in=32, c_out=64, dtype="bf16"), "loader=vec16"),
+    (dict(c_in=64, c_out=64, kh=1, kw=1, pad=(0, 0), dtype="bf16"), "loader=1x1"),
+    (dict(c_in=64, c_out=64, kh=1, kw=1, pad=(0, 0), stride=(2, 2), dtype="bf16"), "loader=vec16"),
+    (dict(c_in=8, c_out=8, dtype="i8", out_dtype="i8"), "loader=generic"),  # 8 bytes per pixel
+    (dict(c_in=16, c_out=16, dtype="i8", out_dtype="i32"), "out=i32 loader=vec16"),
+    (dict(c_in=64, c_out=64, groups=64, dtype="i8"), "dw3x3 dtype=i8"),
+    (dict(c_in=1, c_out=8, dtype="f32"), "direct_f32"),
+    (dict(c_in=4, c_out=4, groups=4, dtype="f32"), "dw3x3 dtype=f32 out=f32 loader=vec16"),
+])
+def test_path_selection(layer, expect):
+    args = dict(n=1, h=16, w=16, kh=3, kw=3, stride=(1, 1), pad=(1, 1), groups=1, act="relu")
+    args.update(layer)
+    c = Conv2d(args["n"], args["h"], args["w"], args["c_in"], args["c_out"], args["kh"], args["kw"],
+               args["stride"], args["pad"], args["groups"], args["dtype"], args.get("out_dtype"), args["act"])
+    assert expect in c.describe()
+    c.close()
+
+
+def test_out_shape_floor_rule_and_per_axis_pads():
+    # the keyword-spotting stem: 49x10, 10x4 kernel, stride 2, pad (5, 1)
+    c = Conv2d(1, 49, 10, 1, 64, 10, 4, (2, 2), (5, 1), dtype="i8")
+    assert c.out_shape == (1, 25, 5, 64)
+    c.close()
+    c = Conv2d(1, 49, 10, 1, 64, 10, 4, (2, 2), (1, 5), dtype="i8")
+    assert c.out_shape == (1, 21, 9, 64)
+    c.close()
+
+
+def test_forced_algo_and_count():
+    n = _lib.lib().conv_algo_count()
+    assert n >= 1
+    for a in range(1, n + 1):
+        c = Conv2d(1, 20, 20, 64, 64, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=a)
+        assert "tile=%d " % a in c.describe()
+        c.close()
+
+
+def fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_run_pointer_checks_before_launch():
+    """NULL, misaligned and overlapping pointers are refused on the host;
+    the fake addresses are never dereferenced or handed to a kernel."""
+    c = Conv2d(1, 8, 8, 16, 16, 3, 3, (1, 1), (1, 1), dtype="bf16")
+    L = _lib.lib()
+    P = c._plan
+    X, W, B, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+    assert L.conv_run(None, X, W, B, Y, None) == -1
+    assert L.conv_run(P, None, W, B, Y, None) == -1
+    assert L.conv_run(P, X, None, B, Y, None) == -1
+    assert L.conv_run(P, X, W, B, None, None) == -1
+    assert L.conv_run(P, X + 8, W, B, Y, None) == -4
+    assert L.conv_run(P, X, W + 2, B, Y, None) == -4
+    assert L.conv_run(P, X, W, B, Y + 4, None) == -4
+    assert L.conv_run(P, X, W, B + 2, Y, None) == -4
+    xbytes = 8 * 8 * 16 * 2
+    assert L.conv_run(P, X, W, B, X + xbytes - 16 * 4, None) == -5  # y starts inside x
+    assert L.conv_run(P, Y + 2048 - 1024, W, B, Y, None) == -5      # x starts inside y
+    assert L.conv_run(P, X, W, Y + 64, Y, None) == -5               # b inside y
+    c.close()
+    ci = Conv2d(1, 8, 8, 16, 16, 3, 3, (1, 1), (1, 1), dtype="i8", out_dtype="i8")
+    assert L.conv_run(ci._plan, X, W, None, Y, None) == -1  # int8 output needs the scale block
+    ci.close()
+
+
+def test_mosaic_argument_checks():
+    L = _lib.lib()
+    T, C = 0x10000000, 0x50000000
+    assert L.conv_mosaic_pack(None, 0, C, 1, 1, 4, 4, 3, 3, None) == -1
+    assert L.conv_mosaic_pack(T, 0, C, 1, 0, 4, 4, 3, 3, None) == -2
+    assert L.conv_mosaic_pack(T, 0, C, 1, 1, 4, 4, 3, 2, None) == -2   # c_pad < c
+    assert L.conv_mosaic_pack(T, 2, C, 1, 1, 4, 4, 3, 3, None) == -3   # int8 tiles
+    assert L.conv_mosaic_pack(T + 4, 0, C, 1, 1, 4, 4, 3, 3, None) == -4
+    assert L.conv_mosaic_pack(T, 0, T + 64, 1, 1, 4, 4, 3, 3, None) == -5
+
+
+def test_destroy_null_is_noop():
+    assert _lib.lib().conv_destroy(None) == 0
+
+
+def test_python_binding_validates_tensors():
+    import torch
+    c = Conv2d(1, 8, 8, 16, 16, 3, 3, (1, 1), (1, 1), dtype="bf16")
+    x = torch.zeros(1, 8, 8, 16, dtype=torch.bfloat16)
+    w = torch.zeros(16, 3, 3, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        c.run(x, w)   # host tensors are refused before any library call
+    c.close()

@@ -1,0 +1,192 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element
+by element on the same seeded inputs (small shapes that span several tiles
+with ragged tails, every tile configuration of the MFMA kernel forced in
+turn), plus the hygiene checks: canary-filled outputs, guard bands,
+determinism, a non-default stream and HIP-graph replay."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from convolution_conv2d_nhwc_amd import _lib
+from convolution_conv2d_nhwc_amd.data import Layer, random_layer_tensors
+from oracle import oracle
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+NTILES = 8
+
+
+def L(name, n, h, w, cin, cout, kh, kw, s=(1, 1), p=(0, 0), groups=1, dtype="bf16", out=None, act="mish"):
+    ho, wo = oracle.out_hw(h, w, kh, kw, s[0], s[1], p[0], p[1])
+    out = out or dtype
+    return Layer(name, n, h, w, cin, cout, kh, kw, s[0], s[1], p[0], p[1], groups, dtype, out, act, ho, wo)
+
+
+LAW = {"f32": "mnist", "bf16": "bf16", "i8": "int8"}
+
+# Dense layers for the MFMA kernel: every loader (vec16, 1x1, generic), ragged
+# pixel counts and channel counts, strides, per-axis padding.
+DENSE = [
+    L("bf16_3x3_vec", 2, 19, 23, 32, 80, 3, 3, (1, 1), (1, 1)),
+    L("bf16_3x3s2_vec", 1, 37, 29, 64, 72, 3, 3, (2, 2), (1, 1), act="relu6"),
+    L("bf16_1x1", 2, 17, 13, 64, 136, 1, 1, act="none"),
+    L("bf16_1x1_s2", 1, 18, 18, 48, 40, 1, 1, (2, 2), act="relu"),
+    L("bf16_stem_c3", 1, 41, 45, 3, 32, 3, 3, (1, 1), (1, 1)),
+    L("bf16_c61_cout61", 1, 21, 19, 61, 61, 3, 3, (1, 1), (1, 1)),
+    L("bf16_5x3_pad21", 1, 23, 17, 16, 24, 5, 3, (2, 1), (2, 1), act="relu"),
+    L("bf16_deepK", 1, 9, 9, 512, 96, 3, 3, (1, 1), (1, 1)),
+    L("i8_3x3_vec_i8", 2, 19, 23, 32, 80, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="relu"),
+    L("i8_3x3_vec_i32", 1, 21, 17, 64, 72, 3, 3, (2, 2), (1, 1), dtype="i8", out="i32", act="none"),
+    L("i8_1x1_i8_mish", 2, 15, 13, 128, 96, 1, 1, dtype="i8", out="i8", act="mish"),
+    L("i8_1x1_i32_relu", 1, 16, 16, 64, 64, 1, 1, dtype="i8", out="i32", act="relu"),
+    L("i8_stem10x4", 1, 49, 10, 1, 64, 10, 4, (2, 2), (5, 1), dtype="i8", out="i8", act="relu"),
+    L("i8_c24_generic", 1, 20, 20, 24, 40, 3, 3, (1, 1), (1, 1), dtype="i8", out="i32", act="none"),
+    L("i8_cout61", 1, 19, 21, 32, 61, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="relu6"),
+    L("i8_deepK", 1, 8, 8, 512, 64, 3, 3, (1, 1), (1, 1), dtype="i8", out="i32", act="none"),
+]
+
+
+@pytest.mark.parametrize("layer", DENSE, ids=[l.name for l in DENSE])
+def test_dense_all_tiles(layer):
+    t = random_layer_tensors(layer, LAW[layer.dtype], seed=11)
+    ref = H.oracle_full(layer, t["x"], t)
+    xg = t["x"].cuda()
+    for algo in [0] + list(range(1, NTILES + 1)):
+        y, conv = H.gpu_run(layer, xg, t, algo=algo)
+        what = "%s algo=%d [%s]" % (layer.name, algo, conv.describe())
+        yc = y.cpu()
+        if layer.dtype == "i8":
+            H.check_int(yc.numpy(), ref, layer, what)
+        else:
+            H.check_float(yc.float().numpy(), ref[0], ref[1], layer.dtype, what)
+        conv.close()
+
+
+DW = [
+    L("dw_bf16_s1", 2, 17, 19, 64, 64, 3, 3, (1, 1), (1, 1), groups=64, act="relu6"),
+    L("dw_bf16_s2", 1, 24, 23, 32, 32, 3, 3, (2, 2), (1, 1), groups=32, act="mish"),
+    L("dw_bf16_c12_generic", 1, 13, 11, 12, 12, 3, 3, (1, 1), (1, 1), groups=12, act="none"),
+    L("dw_i8_s1", 1, 25, 5, 64, 64, 3, 3, (1, 1), (1, 1), groups=64, dtype="i8", out="i8", act="relu"),
+    L("dw_i8_s2_i32", 2, 15, 16, 32, 32, 3, 3, (2, 2), (1, 1), groups=32, dtype="i8", out="i32", act="none"),
+    L("dw_i8_c8_generic", 1, 12, 9, 8, 8, 3, 3, (1, 1), (1, 1), groups=8, dtype="i8", out="i8", act="mish"),
+    L("dw_f32_c4", 1, 14, 13, 4, 4, 3, 3, (1, 1), (1, 1), groups=4, dtype="f32", act="relu"),
+    L("dw_f32_c6_s2", 1, 15, 15, 6, 6, 3, 3, (2, 2), (1, 1), groups=6, dtype="f32", act="mish"),
+    L("dw_bf16_pad0", 1, 10, 11, 16, 16, 3, 3, (1, 1), (0, 0), groups=16, act="relu"),
+]
+
+
+@pytest.mark.parametrize("layer", DW, ids=[l.name for l in DW])
+def test_depthwise(layer):
+    t = random_layer_tensors(layer, LAW[layer.dtype], seed=12)
+    y, conv = H.gpu_run(layer, t["x"], t)
+    assert "dw3x3" in conv.describe()
+    H.check_layer_full(layer, t["x"], t, y, "%s [%s]" % (layer.name, conv.describe()))
+
+
+F32 = [
+    L("f32_mnist_like", 1, 28, 28, 1, 8, 3, 3, (1, 1), (1, 1), dtype="f32", act="relu"),
+    L("f32_ragged", 2, 11, 9, 5, 7, 3, 2, (2, 1), (1, 0), dtype="f32", act="mish"),
+    L("f32_1x1", 1, 7, 7, 16, 10, 1, 1, dtype="f32", act="relu6"),
+]
+
+
+@pytest.mark.parametrize("layer", F32, ids=[l.name for l in F32])
+def test_fp32_direct(layer):
+    t = random_layer_tensors(layer, "mnist", seed=13)
+    y, conv = H.gpu_run(layer, t["x"], t)
+    assert "direct_f32" in conv.describe()
+    H.check_layer_full(layer, t["x"], t, y, layer.name)
+
+
+def test_zero_bias_pointer():
+    layer = L("nobias", 1, 9, 9, 16, 16, 3, 3, (1, 1), (1, 1), act="none")
+    t = random_layer_tensors(layer, "bf16", seed=14)
+    conv = _lib.Conv2d.from_layer(layer)
+    y = conv.run(t["x"].cuda(), t["w"].cuda(), None)
+    r, a = oracle.conv_float(H.to_np_f32(t["x"]), H.to_np_f32(t["w"]), None, (1, 1), (1, 1))
+    H.check_float(y.cpu().float().numpy(), r, a, "bf16", "null bias")
+
+
+# ------------------------------------------------------------------ mosaic
+
+@pytest.mark.parametrize("th,tw,c,c_pad,in_dt,out_dt", [
+    (320, 320, 3, 3, torch.float32, torch.bfloat16),   # the 640x640 workload (vector path)
+    (320, 320, 3, 4, torch.float32, torch.bfloat16),   # channel padding (pixel path)
+    (7, 5, 3, 3, torch.float32, torch.float32),        # odd sizes
+    (16, 8, 4, 8, torch.bfloat16, torch.bfloat16),
+])
+def test_mosaic_bit_exact(th, tw, c, c_pad, in_dt, out_dt):
+    g = np.random.default_rng(15)
+    tiles32 = g.random((8, th, tw, c)).astype(np.float32) * 3 - 1
+    tiles = torch.from_numpy(tiles32).to(in_dt)
+    can = _lib.mosaic_pack(tiles.cuda(), c_pad=c_pad, out_dtype=out_dt).cpu()
+    ref = oracle.mosaic(tiles.float().numpy(), c_pad=c_pad, out="bf16" if out_dt == torch.bfloat16 else "f32")
+    got = can.view(torch.int16).numpy().view(np.uint16) if out_dt == torch.bfloat16 else can.numpy()
+    assert np.array_equal(got, ref)
+
+
+# ----------------------------------------------------------------- hygiene
+
+def _guarded_run(layer, t, algo=0):
+    """Output placed in the middle of a larger buffer whose margins hold a
+    pattern that must survive the run."""
+    conv = _lib.Conv2d.from_layer(layer, algo=algo)
+    dt = _lib.TORCH_DT[layer.out]
+    numel = int(np.prod(conv.out_shape))
+    esz = torch.tensor([], dtype=dt).element_size()
+    guard = 4096 // esz
+    buf = torch.empty(numel + 2 * guard, dtype=dt, device="cuda")
+    if dt.is_floating_point:
+        buf.fill_(-4096.0)
+    else:
+        buf.fill_(-99)
+    y = buf[guard:guard + numel].view(conv.out_shape)
+    conv.run(t["x"].cuda(), t["w"].cuda(), H.bias_arg(layer, t), y)
+    torch.cuda.synchronize()
+    head, tail = buf[:guard], buf[guard + numel:]
+    fill = -4096.0 if dt.is_floating_point else -99
+    assert torch.all(head == fill) and torch.all(tail == fill), "write outside y"
+    return y
+
+
+@pytest.mark.parametrize("layer", [DENSE[0], DENSE[5], DENSE[8], DENSE[14], DW[0], DW[3], F32[1]],
+                         ids=lambda l: l.name)
+def test_guard_bands_and_determinism(layer):
+    t = random_layer_tensors(layer, LAW[layer.dtype], seed=16)
+    algos = [0] + (list(range(1, NTILES + 1)) if layer.groups == 1 and layer.dtype != "f32" else [])
+    for algo in algos:
+        y1 = _guarded_run(layer, t, algo).clone()
+        y2 = _guarded_run(layer, t, algo)
+        assert torch.equal(y1.cpu().view(torch.uint8), y2.cpu().view(torch.uint8)), "run-to-run difference"
+        if algo == 0:
+            H.check_layer_full(layer, t["x"], t, y2, "%s guarded" % layer.name)
+
+
+def test_side_stream_and_graph_replay():
+    layer = DENSE[0]
+    t = random_layer_tensors(layer, "bf16", seed=17)
+    ref = H.oracle_full(layer, t["x"], t)
+    conv = _lib.Conv2d.from_layer(layer)
+    x, w, b = t["x"].cuda(), t["w"].cuda(), H.bias_arg(layer, t)
+    y = conv.empty_output()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y.fill_(float("nan"))
+        conv.run(x, w, b, y)
+    s.synchronize()
+    H.check_float(y.cpu().float().numpy(), ref[0], ref[1], "bf16", "side stream")
+    # capture into a graph, replay several times with eager work between
+    g = torch.cuda.CUDAGraph()
+    yg = conv.empty_output()
+    with torch.cuda.graph(g):
+        conv.run(x, w, b, yg)
+    for i in range(4):
+        yg.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        H.check_float(yg.cpu().float().numpy(), ref[0], ref[1], "bf16", "graph replay %d" % i)
+        _ = (x.float() * 2).sum().item()  # unrelated eager work between replays
