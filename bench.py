@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused NHWC conv2d hot path on one MI355X.
+
+A step is one pass of the 640x640 YOLO layer stack (four 320x320x3 fp32
+tiles mosaic-packed into a 640x640x3 bf16 canvas, then nine bf16 convs with
+fused bias + Mish, N=1), captured once into a HIP graph and replayed. All
+inputs, weights and intermediate buffers are resident in device memory
+before the timed region starts.
+
+Prints ONE JSON line:
+  value         TFLOP/s of the stack (26.5 GFLOP per step, every tap counted)
+  ms_per_step   ms per 640x640 layer stack
+  roofline      the dominant kernel (largest share of the step), timed with
+                HIP events on the stream it runs on, against MI355X peaks
+  cpu_baseline  the CPU oracle on the same stack (all host threads)
+  layers        per-layer time and roofline fraction
+
+Options: --gpus N (only 1 is supported), --steps K, --warmup W,
+--workload NAME (another stack, for information), --no-cpu-baseline,
+--calib-copy MIB (run only a plain device copy of known size, for the
+counter calibration of the traffic figure).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "conv TFLOP/s (bf16) / TOPS (int8) + % MFMA or HBM peak; ms per 640² layer stack"
+PEAK = {"bf16": 2500.0, "i8": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s (TOPS for int8)
+HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="yolo640_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources, to tell whether stored counter figures still
+    describe the current kernels."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "convolution_conv2d_nhwc_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(PROFILES, "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("source_digest") != kernel_source_digest():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the multi-GPU sharding is a design note, not built)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.calib_copy:
+        n = args.calib_copy * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4, "launches": 5}))
+        return
+
+    from convolution_conv2d_nhwc_amd import _lib
+    from convolution_conv2d_nhwc_amd.data import layer_params, network_input, workload
+
+    wl = workload(args.workload)
+    if not wl.chained:
+        print("bench.py: the step is a chained stack; %s is not one" % wl.name, file=sys.stderr)
+        sys.exit(2)
+
+    # ---- resident inputs, weights and buffers --------------------------------
+    convs, params, bufs = [], [], []
+    for i, layer in enumerate(wl.layers):
+        p = layer_params(wl, i)
+        conv = _lib.Conv2d.from_layer(layer)
+        dev = {"w": p["w"].cuda()}
+        if layer.dtype == "i8":
+            dev["b"] = _lib.pack_bias_scale(p["b"], p.get("s") if layer.out == "i8" else None).cuda()
+        else:
+            dev["b"] = p["b"].cuda()
+        convs.append(conv)
+        params.append(dev)
+        bufs.append(conv.empty_output())
+    x0 = network_input(wl).cuda()
+    canvas = None
+    if wl.mosaic is not None:
+        m, th, tw, c = wl.mosaic
+        canvas = torch.empty((m, 2 * th, 2 * tw, c), dtype=torch.bfloat16, device="cuda")
+
+    def launch(i, x):
+        convs[i].run(x, params[i]["w"], params[i]["b"], bufs[i])
+        return bufs[i]
+
+    def step():
+        x = x0
+        if canvas is not None:
+            _lib.mosaic_pack(x0, canvas, out_dtype=torch.bfloat16)
+            x = canvas
+        for i in range(len(convs)):
+            x = launch(i, x)
+
+    # warm up on a side stream, then capture one step into a graph
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K graph replays ------------------------------------------
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # ---- per-kernel durations -------------------------------------------------
+    # Each layer (and the mosaic) is captured R times back to back into a graph
+    # of its own, on the stream its kernel runs on; HIP events around replays of
+    # that graph give the kernel's average launch duration without host launch
+    # gaps, which is what the profiler's per-dispatch durations measure.
+    R = 10
+    reps = max(5, min(args.steps // 10, 50))
+
+    def time_graph(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(R):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1000.0 / (reps * R)
+
+    ins = [canvas if canvas is not None else x0] + bufs[:-1]
+    dur_us = []
+    if canvas is not None:
+        dur_us.append(time_graph(lambda: _lib.mosaic_pack(x0, canvas, out_dtype=torch.bfloat16)))
+    for i in range(len(convs)):
+        dur_us.append(time_graph(lambda i=i: launch(i, ins[i])))
+
+    layers = []
+    j = 0
+    if canvas is not None:
+        m, th, tw, c = wl.mosaic
+        mb = 4 * m * th * tw * c * 4 + m * 4 * th * tw * c * 2
+        layers.append({"name": "mosaic_pack", "kernel": "mosaic_vec8_kernel", "us": dur_us[0],
+                       "gflop": 0.0, "mbytes": mb / 1e6, "bound": "hbm",
+                       "frac": (mb / (HBM_GBS * 1e9)) / (dur_us[0] * 1e-6)})
+        j = 1
+    for i, layer in enumerate(wl.layers):
+        us = dur_us[j + i]
+        fl, by = layer.flops(), layer.bytes()
+        t_mfma = fl / (PEAK[layer.dtype] * 1e12)
+        t_hbm = by / (HBM_GBS * 1e9)
+        bound = "mfma" if t_mfma >= t_hbm else "hbm"
+        desc = convs[i].describe()
+        layers.append({"name": layer.name, "kernel": desc.split(" kernel=")[-1] if " kernel=" in desc else desc,
+                       "desc": desc, "us": us, "gflop": fl / 1e9, "mbytes": by / 1e6,
+                       "tflops": fl / (us * 1e-6) / 1e12, "gbs": by / (us * 1e-6) / 1e9, "bound": bound,
+                       "frac": max(t_mfma, t_hbm) / (us * 1e-6)})
+
+    # dominant kernel = the kernel symbol with the largest time per step
+    by_kernel = {}
+    for L in layers:
+        by_kernel.setdefault(L["kernel"], []).append(L)
+    dom, dl = max(by_kernel.items(), key=lambda kv: sum(L["us"] for L in kv[1]))
+    n_launch = len(dl)
+    avg_us = sum(L["us"] for L in dl) / n_launch
+    fl = sum(L["gflop"] for L in dl) * 1e9 / n_launch
+    by = sum(L["mbytes"] for L in dl) * 1e6 / n_launch
+    t_m = fl / (PEAK[wl.layers[0].dtype] * 1e12) if fl else 0.0
+    t_h = by / (HBM_GBS * 1e9)
+    if t_m >= t_h and fl:
+        roof = {"bound": "mfma", "achieved": fl / (avg_us * 1e-6) / 1e12, "peak": PEAK[wl.layers[0].dtype],
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": by / (avg_us * 1e-6) / 1e9, "peak": HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = stored_traffic(dom)
+    roof["kernel"] = dom
+    roof["launches_per_step"] = n_launch
+    roof["avg_launch_us"] = avg_us
+    roof["algorithmic_per_launch"] = {"flop": fl, "bytes": by}
+
+    total_flop = wl.flops()
+    value = total_flop / (ms_per_step * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl)
+
+    dt = wl.layers[0].dtype
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s" if dt != "i8" else "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": "%s: %s" % (wl.name, wl.description), "global_batch": wl.layers[0].n,
+                   "input": "640x640x3 from 4x320x320x3" if wl.mosaic else "%dx%dx%d" % (
+                       wl.layers[0].h, wl.layers[0].w, wl.layers[0].cin),
+                   "gflop_per_step": total_flop / 1e9, "timing": "hipGraph replay, HIP events",
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "layers": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in L.items() if k != "desc"}
+                   for L in layers],
+        "wall_s_timed": round(wall, 4),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl):
+    """The oracle, untuned, on the same stack: mosaic + every layer, all host
+    threads, one pass (the whole 640x640 stack is ~13 GMAC)."""
+    import numpy as np
+    import torch
+
+    from convolution_conv2d_nhwc_amd.data import layer_params, network_input
+    from oracle import oracle
+
+    threads = oracle.num_threads(0)
+    x0 = network_input(wl)
+    t = time.perf_counter()
+    if wl.mosaic is not None:
+        bits = oracle.mosaic(x0.numpy(), out="bf16")
+        x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    else:
+        x = x0.float().numpy()
+    for i, layer in enumerate(wl.layers):
+        p = layer_params(wl, i)
+        r, _ = oracle.conv_float(x, p["w"].float().numpy(), p["b"].numpy(), (layer.sh, layer.sw),
+                                 (layer.ph, layer.pw), layer.groups, layer.act, want_abs=False, threads=threads)
+        x = torch.from_numpy(r.astype(np.float32)).to(torch.bfloat16).float().numpy() if layer.out == "bf16" \
+            else r.astype(np.float32)
+    sec = time.perf_counter() - t
+    return {"value": round(wl.flops() / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole %s stack, one pass (%.2f GFLOP), %.2f s" % (wl.name, wl.flops() / 1e9, sec),
+            "ms_per_step": round(sec * 1e3, 1),
+            "cpu": _cpu_name()}
+
+
+def _cpu_name():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -235,14 +235,21 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
   if (p->path == PATH_IGEMM) {
     const TileCfg& t = kTiles[p->tile];
     const long nwg = (long)((p->g.cout + t.tco - 1) / t.tco) * ((p->g.m + t.tpx - 1) / t.tpx);
-    std::snprintf(buf, len, "igemm dtype=%s out=%s loader=%s tile=%d co%dxpx%d waves=%dx%d wgs=%ld m=%d k=%d",
+    std::snprintf(buf, len,
+                  "igemm dtype=%s out=%s loader=%s tile=%d co%dxpx%d waves=%dx%d wgs=%ld m=%d k=%d "
+                  "kernel=igemm_kernel<%d, %d, %d, %d, %d, %d>",
                   kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], p->tile + 1, t.tco, t.tpx, t.wco,
-                  t.wpx, nwg, p->g.m, p->g.k);
+                  t.wpx, nwg, p->g.m, p->g.k, p->in_esz, t.tco, t.tpx, t.wco, t.wpx, p->loader);
   } else if (p->path == PATH_DW) {
-    std::snprintf(buf, len, "dw3x3 dtype=%s out=%s loader=%s stride=%dx%d", kDt[p->d.dtype], kDt[p->d.out_dtype],
-                  kLoader[p->loader], p->g.sh, p->g.sw);
+    static const char* kT[] = {"", "signed char", "unsigned short", "", "float"};
+    const bool vec = p->loader == LOAD_VEC;
+    const int ve = vec ? 16 / p->in_esz : 1;
+    const int pw = (p->in_esz == 1 && vec) ? 2 : 4;
+    std::snprintf(buf, len, "dw3x3 dtype=%s out=%s loader=%s stride=%dx%d kernel=dw3x3_kernel<%s, %d, %d>",
+                  kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], p->g.sh, p->g.sw, kT[p->in_esz], ve,
+                  pw);
   } else {
-    std::snprintf(buf, len, "direct_f32 m=%d k=%d", p->g.m, p->g.k);
+    std::snprintf(buf, len, "direct_f32 m=%d k=%d kernel=conv_f32_kernel", p->g.m, p->g.k);
   }
   return CONV_OK;
 }
