@@ -9,7 +9,6 @@
 // only enqueues one kernel on the caller's stream.
 #include <hip/hip_runtime.h>
 
-#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -36,47 +35,20 @@ int esz_of(int dt) {
   }
 }
 
-// Concurrent workgroups one CU holds for a tile, limited by its LDS (double
-// buffered A and B tiles of 144-byte rows; 160 KiB of LDS per CU) and by the
-// 8 waves of 4-wave groups the register budget of these kernels allows.
-int wg_per_cu(const TileCfg& t) {
-  const int lds = 2 * (t.tco + t.tpx) * 144;
-  return std::max(1, std::min(2, (160 * 1024) / lds));
-}
-
-// Relative MFMA issue efficiency of a tile, from its operand reuse: a wave
-// tile of a x b 16x16 fragments reads (a + b) fragments from LDS per a*b
-// MFMAs. Used only to rank tiles, not to predict time.
-double tile_eff(const TileCfg& t) {
-  const double fa = t.tco / t.wco / 16.0, fb = t.tpx / t.wpx / 16.0;
-  const double reuse = fa * fb / (fa + fb);  // MFMAs per fragment read
-  return reuse / (reuse + 1.0);
-}
-
-// Analytic tile choice: estimated time = (workgroup rounds over 256 CUs) x
-// (padded tile work / tile efficiency). It charges the padding a tile wastes
-// on ragged Cout and pixel counts, and the idle CUs of the last round (wave
-// quantisation), which is what decides small-M layers.
+// Tile choice, fitted to a sweep of every tile on every layer of the YOLO
+// workloads on MI355X (64x64 workgroup tiles keep 4-5 workgroups per CU and
+// win on short reductions and small layers; 128-channel tiles win once the
+// reduction is long and there are enough of them to fill 256 CUs twice).
 int choose_tile(const Geometry& g, int esz) {
-  const int kbytes = g.k * esz;
-  const double kpad = (double)((kbytes + 127) / 128) * 128;
-  double best = 1e300;
-  int best_i = 0;
-  for (int i = 0; i < kNumTiles; ++i) {
-    const TileCfg& t = kTiles[i];
-    const long nco = (g.cout + t.tco - 1) / t.tco;
-    const long npx = (g.m + t.tpx - 1) / t.tpx;
-    const long nwg = nco * npx;
-    const long slots = 256L * wg_per_cu(t);
-    const long rounds = (nwg + slots - 1) / slots;
-    const double per_wg = (double)t.tco * t.tpx * kpad / tile_eff(t) / wg_per_cu(t);
-    const double est = rounds * per_wg;
-    if (est < best * 0.999) {
-      best = est;
-      best_i = i;
-    }
-  }
-  return best_i;
+  const long kbytes = (long)g.k * esz;
+  auto nwg = [&](int ti) {
+    const TileCfg& t = kTiles[ti];
+    return (long)((g.cout + t.tco - 1) / t.tco) * ((g.m + t.tpx - 1) / t.tpx);
+  };
+  const int t128x128 = 3, t128x64 = 4, t64x64 = 5;
+  if (kbytes >= 2048 && g.cout >= 128 && nwg(t128x128) >= 384)
+    return nwg(t128x64) >= 2000 ? t128x64 : t128x128;
+  return t64x64;
 }
 
 bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
@@ -129,9 +101,13 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
     path = dt == CONV_F32 ? PATH_F32 : PATH_IGEMM;
     if (path == PATH_IGEMM) {
       const bool vec = (d->c_in * in_esz) % 16 == 0;
+      const bool tap = (d->c_in * in_esz) % 128 == 0 && (int64_t)d->kh * d->kw <= 32 &&
+                       (x_bytes + ((int64_t)d->pad_h * d->w + d->pad_w) * d->c_in * in_esz) < kMaxBytes;
       if (vec && d->kh == 1 && d->kw == 1 && d->stride_h == 1 && d->stride_w == 1 && d->pad_h == 0 &&
           d->pad_w == 0)
         loader = LOAD_1X1;
+      else if (tap)
+        loader = LOAD_TAP;
       else if (vec)
         loader = LOAD_VEC;
     }
@@ -142,6 +118,11 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
     loader = (d->c_in * in_esz) % 16 == 0 ? LOAD_VEC : LOAD_GENERIC;
   }
   if (d->algo != 0 && (path != PATH_IGEMM || d->algo < 1 || d->algo > kNumTiles)) return CONV_E_UNSUPPORTED;
+  // A short reduction over an odd channel count (the 3-channel and 1-channel
+  // stems) goes to the LDS-free small-K kernel unless a tile is forced.
+  if (path == PATH_IGEMM && loader == LOAD_GENERIC && d->algo == 0 &&
+      (int64_t)d->kh * d->kw * cg * in_esz <= 128)
+    path = PATH_SMALLK;
 
   conv_plan* p = new (std::nothrow) conv_plan;
   if (!p) return CONV_E_NOMEM;
@@ -205,6 +186,7 @@ conv_status conv_run(const conv_plan* p, const void* x, const void* w, const voi
   switch (p->path) {
     case PATH_IGEMM: err = launch_igemm(p, x, w, e, y, s); break;
     case PATH_DW: err = launch_dw(p, x, w, e, y, s); break;
+    case PATH_SMALLK: err = launch_smallk(p, x, w, e, y, s); break;
     default: err = launch_f32(p, x, w, e, y, s); break;
   }
   if (err != hipSuccess) {
@@ -230,7 +212,7 @@ conv_status conv_out_shape(const conv_plan* p, int64_t nhwc[4]) {
 
 conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
   if (!p || !buf || len <= 0) return CONV_E_NULL;
-  static const char* kLoader[] = {"generic", "vec16", "1x1"};
+  static const char* kLoader[] = {"generic", "vec16", "1x1", "tap"};
   static const char* kDt[] = {"f32", "bf16", "i8", "i32"};
   if (p->path == PATH_IGEMM) {
     const TileCfg& t = kTiles[p->tile];
@@ -240,6 +222,11 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
                   "kernel=igemm_kernel<%d, %d, %d, %d, %d, %d>",
                   kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], p->tile + 1, t.tco, t.tpx, t.wco,
                   t.wpx, nwg, p->g.m, p->g.k, p->in_esz, t.tco, t.tpx, t.wco, t.wpx, p->loader);
+  } else if (p->path == PATH_SMALLK) {
+    int fco, ks;
+    smallk_shape(p->g, p->in_esz, &fco, &ks);
+    std::snprintf(buf, len, "smallk dtype=%s out=%s m=%d k=%d kernel=smallk_kernel<%d, %d, %d>", kDt[p->d.dtype],
+                  kDt[p->d.out_dtype], p->g.m, p->g.k, p->in_esz, fco, ks);
   } else if (p->path == PATH_DW) {
     static const char* kT[] = {"", "signed char", "unsigned short", "", "float"};
     const bool vec = p->loader == LOAD_VEC;

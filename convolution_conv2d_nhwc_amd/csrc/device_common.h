@@ -29,12 +29,13 @@ enum OutKind {
 // function table). With t = e^v, tanh(ln(1+t)) = ((1+t)^2 - 1)/((1+t)^2 + 1)
 // = n/(n + 2) where n = t*(t + 2). This form has no cancellation for v << 0
 // (the K1 form v - 2v/((1+t)^2+1) of section 9 subtracts two nearly equal
-// numbers there). For v > 20, n/(n+2) rounds to 1 in fp32, so Mish(v) = v.
+// numbers there). The exponent is clamped at 20: beyond it n/(n+2) rounds to
+// 1 in fp32, so Mish(v) = v, and e^v cannot overflow. The quotient uses the
+// hardware reciprocal (1 ulp) instead of an IEEE division.
 __device__ __forceinline__ float mish_f32(float v) {
-  if (v > 20.0f) return v;
-  const float t = __expf(v);
+  const float t = __expf(fminf(v, 20.0f));
   const float n = t * (t + 2.0f);
-  return v * (n / (n + 2.0f));
+  return v * (n * __builtin_amdgcn_rcpf(n + 2.0f));
 }
 
 __device__ __forceinline__ float apply_act(float v, int act) {

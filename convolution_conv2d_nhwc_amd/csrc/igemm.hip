@@ -15,10 +15,17 @@
 // and keeps its fp32/int32 accumulators in registers for the whole K loop
 // (output-stationary, one of the schedules the TSO paper compares). K is
 // walked in tiles of 128 bytes per row (64 bf16 or 128 int8); each tile is
-// one 16-byte chunk per (row, 1/8 of the tile). The next tile's chunks are
-// fetched into registers while the MFMAs consume the current LDS buffer
-// (double-buffered LDS, one barrier per tile). LDS rows are padded to 144
-// bytes so the 16 rows one ds_read_b128 touches fall on distinct banks.
+// 8 chunks of 16 bytes per row.
+//
+// Memory pipeline. All global reads are buffer loads: an out-of-range offset
+// returns zero, so image borders, the K tail and ragged tiles need no
+// branches (a lane that must read zero gets the offset 0x80000000). Each
+// thread keeps D K-tiles of chunks in flight in registers; at every K-tile it
+// writes the oldest one into one of two LDS buffers, passes one barrier,
+// re-issues the freed registers for the tile D ahead, and runs the MFMAs of
+// the tile just written. LDS rows are 128 bytes with chunk c of row r stored
+// at position c ^ (r & 7), so both the 16-byte stores and the ds_read_b128 of
+// 16 consecutive rows hit distinct banks.
 //
 // MFMA operand mapping (v_mfma_f32_16x16x32_bf16 / v_mfma_i32_16x16x64_i8):
 // the weights are the "A" operand (rows = output channels) and the gathered
@@ -27,6 +34,7 @@
 // 4*(l/16) .. 4*(l/16)+3 of column l % 16, i.e. four consecutive output
 // channels of one pixel, which the epilogue stores as one NHWC vector.
 #include "device_common.h"
+#include "mfma_epilogue.h"
 #include "plan.h"
 
 namespace convnhwc {
@@ -44,8 +52,8 @@ const TileCfg kTiles[kNumTiles] = {
 
 namespace {
 
-constexpr int kBKB = 128;     // bytes of K per tile row
-constexpr int kLdsRow = 144;  // padded LDS row stride (bytes)
+constexpr int kBKB = 128;         // bytes of K per tile row
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past any tensor: reads 0
 
 struct IgArgs {
   const char* x;
@@ -55,6 +63,11 @@ struct IgArgs {
   Geometry g;
   int out_kind;
   int nco_tiles;
+  int x_bytes;
+  int w_bytes;
+  float rcp_c;   // 1.0f / Cin
+  float rcp_kw;  // 1.0f / KW
+  int x_shift;   // LOAD_TAP: bytes the x descriptor starts before x
 };
 
 template <int ESZ>
@@ -77,31 +90,49 @@ struct Mfma<1> {
   }
 };
 
-__device__ __forceinline__ i32x4 zero4() { return i32x4{0, 0, 0, 0}; }
-
-__device__ __forceinline__ i32x4 ld16(const char* p) {
-  return *reinterpret_cast<const i32x4*>(p);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
-// Read one element of ESZ bytes as an unsigned integer.
+__device__ __forceinline__ i32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// Same with a wave-uniform byte offset added by the buffer unit (soffset).
+__device__ __forceinline__ i32x4 bload16s(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, soff, 0);
+}
+
 template <int ESZ>
-__device__ __forceinline__ uint32_t ld_elem(const char* p) {
+__device__ __forceinline__ uint32_t bload_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (ESZ == 2)
-    return *reinterpret_cast<const uint16_t*>(p);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
   else
-    return *reinterpret_cast<const uint8_t*>(p);
+    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
 }
 
-// Put element e (of 16/ESZ) into a 16-byte chunk held as four dwords.
-template <int ESZ>
-__device__ __forceinline__ void put_elem(uint32_t (&wds)[4], int e, uint32_t v) {
-  constexpr int PER = 4 / ESZ;
-  wds[e / PER] |= v << (8 * ESZ * (e % PER));
+// q = n / d and r = n % d for 0 <= n < 2^24 and 1 <= d < 2^24 through an fp32
+// reciprocal (rcp_d = 1.0f / d): the float quotient is off by at most one,
+// and one correction step each way makes it exact.
+__device__ __forceinline__ void divmod_small(int n, int d, float rcp_d, int& q, int& r) {
+  q = (int)((float)n * rcp_d);
+  r = n - q * d;
+  if (r < 0) {
+    --q;
+    r += d;
+  }
+  if (r >= d) {
+    ++q;
+    r -= d;
+  }
 }
+
+// LDS byte offset of chunk c of row r (128-byte rows, XOR-swizzled chunks).
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kBKB + ((c ^ (r & 7)) << 4); }
 
 // ---------------------------------------------------------------- kernel
 
-template <int ESZ, int TCO, int TPX, int WCO, int WPX, int LOADER>
+template <int ESZ, int TCO, int TPX, int WCO, int WPX, int LOADER, int D>
 __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
   constexpr int VE = 16 / ESZ;      // elements per 16-byte chunk
   constexpr int BKE = kBKB / ESZ;   // elements per K-tile row
@@ -110,11 +141,12 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
   constexpr int ACH = TCO / 32;     // 16-byte A chunks per thread per tile
   constexpr int BCH = TPX / 32;     // 16-byte B chunks per thread per tile
   static_assert(FCO >= 1 && FPX >= 1 && WCO * WPX == 4, "bad tile");
+  static_assert(LOADER != LOAD_GENERIC || D == 1, "generic loader is single-stage");
   typedef typename Mfma<ESZ>::acc_t acc_t;
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * (TCO + TPX) * kLdsRow];
+  __shared__ __attribute__((aligned(16))) char smem[2 * (TCO + TPX) * kBKB];
   char* const As = smem;
-  char* const Bs = smem + 2 * TCO * kLdsRow;
+  char* const Bs = smem + 2 * TCO * kBKB;
 
   const Geometry g = a.g;
   const int tid = threadIdx.x;
@@ -122,6 +154,8 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
   const int wave = tid >> 6;
   const int wco = wave / WPX;
   const int wpx = wave % WPX;
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t rw = rsrc(a.w, a.w_bytes);
 
   // Tiles are handed to the 8 XCDs round-robin by workgroup id; remap so each
   // XCD (own L2) gets a contiguous run of tiles that share activation rows.
@@ -136,50 +170,75 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
   // VEC / 1X1: chunk j of this thread is (row tid/8 + 32 j, column tid%8).
   // GENERIC:   chunk j of this thread is (row tid%T, column (tid/T)*CH + j).
   int b_base[BCH], b_hi0[BCH], b_wi0[BCH];
-  int kh_s = 0, kw_s = 0, ci_s = 0;  // VEC: decomposition of this thread's k
-  {
-    for (int j = 0; j < BCH; ++j) {
-      int row;
-      if constexpr (LOADER == LOAD_GENERIC)
-        row = tid % TPX;
-      else
-        row = (tid >> 3) + 32 * j;
-      const int p = px0 + row;
-      if (p < g.m) {
-        const int n = p / hw_o;
-        const int r = p - n * hw_o;
-        const int ho = r / g.wo;
-        const int wo = r - ho * g.wo;
-        if constexpr (LOADER == LOAD_1X1) {
-          b_base[j] = p * g.c;
-          b_hi0[j] = 0;
-          b_wi0[j] = 0;
-        } else {
-          const int hi0 = ho * g.sh - g.ph;
-          const int wi0 = wo * g.sw - g.pw;
-          b_hi0[j] = hi0;
-          b_wi0[j] = wi0;
-          b_base[j] = ((n * g.h + hi0) * g.w + wi0) * g.c;
-        }
-      } else {
-        b_base[j] = 0;
-        b_hi0[j] = -0x40000000;  // every bounds test fails
+  for (int j = 0; j < BCH; ++j) {
+    int row;
+    if constexpr (LOADER == LOAD_GENERIC)
+      row = tid % TPX;
+    else
+      row = (tid >> 3) + 32 * j;
+    const int p = px0 + row;
+    if (p < g.m) {
+      const int n = p / hw_o;
+      const int r = p - n * hw_o;
+      const int ho = r / g.wo;
+      const int wo = r - ho * g.wo;
+      if constexpr (LOADER == LOAD_1X1) {
+        b_base[j] = p * g.c;
+        b_hi0[j] = 0;
         b_wi0[j] = 0;
+      } else {
+        const int hi0 = ho * g.sh - g.ph;
+        const int wi0 = wo * g.sw - g.pw;
+        b_hi0[j] = hi0;
+        b_wi0[j] = wi0;
+        b_base[j] = ((n * g.h + hi0) * g.w + wi0) * g.c;
       }
-    }
-    if constexpr (LOADER == LOAD_VEC) {
-      const int k0 = (tid & 7) * VE;
-      const int tap = k0 / g.c;
-      ci_s = k0 - tap * g.c;
-      kh_s = tap / g.kw;
-      kw_s = tap - kh_s * g.kw;
+    } else {
+      b_base[j] = 0;
+      b_hi0[j] = -0x40000000;  // every bounds test fails
+      b_wi0[j] = 0;
     }
   }
 
-  i32x4 ra[ACH], rb[BCH];
+  // LOAD_TAP / LOAD_1X1: per-thread byte offsets that stay fixed for the
+  // whole K loop; the K position enters every load as a wave-uniform soffset.
+  // The x descriptor of LOAD_TAP starts x_shift = (ph*W + pw)*Cin*ESZ bytes
+  // before x, so that the offset of a pixel's top-left tap is never negative.
+  // tmask[j] bit t says whether tap t of row j lies inside the image.
+  uint32_t voff_a[ACH], voff_b[BCH], tmask[BCH];
+  __amdgpu_buffer_rsrc_t rxt = rx;
+  const int cbytes = g.c * ESZ;
+  const int nkt_all = (g.k * ESZ + kBKB - 1) / kBKB;
+  int t_kh = 0, t_kw = 0, t_cb = 0;  // uniform tap state of the next fetch
+  if constexpr (LOADER == LOAD_TAP || LOADER == LOAD_1X1) {
+    const int c16 = (tid & 7) * 16;
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) {
+      const int co = co0 + (tid >> 3) + 32 * j;
+      voff_a[j] = co < g.cout ? (uint32_t)(co * g.k * ESZ + c16) : kOOB;
+    }
+    if constexpr (LOADER == LOAD_TAP) {
+      rxt = rsrc(a.x - a.x_shift, a.x_bytes + a.x_shift);
+#pragma unroll
+      for (int j = 0; j < BCH; ++j) {
+        voff_b[j] = (uint32_t)(b_base[j] * ESZ + a.x_shift + c16);
+        uint32_t m = 0;
+        for (int kh = 0, tap = 0; kh < g.kh; ++kh)
+          for (int kw = 0; kw < g.kw; ++kw, ++tap) {
+            const int hi = b_hi0[j] + kh, wi = b_wi0[j] + kw;
+            if ((unsigned)hi < (unsigned)g.h && (unsigned)wi < (unsigned)g.w) m |= 1u << tap;
+          }
+        tmask[j] = m;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < BCH; ++j) voff_b[j] = b_hi0[j] == 0 ? (uint32_t)(b_base[j] * ESZ + c16) : kOOB;
+    }
+  }
 
-  // Fetch K-tile kt into registers (tiles are fetched in increasing order).
-  auto fetch = [&](int kt) {
+  // Issue the global loads of K-tile kt into one register stage (tiles are
+  // fetched in increasing order).
+  auto fetch = [&](int kt, i32x4 (&ra)[ACH], i32x4 (&rb)[BCH]) {
     const int kb = kt * BKE;
     if constexpr (LOADER == LOAD_GENERIC) {
       // A: weights, element-wise (K * ESZ need not be 16-byte aligned).
@@ -189,17 +248,25 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
         const int row = tid % TCO, grp = tid / TCO;
         const int co = co0 + row;
         const int k_first = kb + grp * CH * VE;
-        for (int j = 0; j < CH; ++j) {
-          uint32_t wds[4] = {0, 0, 0, 0};
+        uint32_t v[CH][VE];
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+#pragma unroll
           for (int e = 0; e < VE; ++e) {
             const int k = k_first + j * VE + e;
-            if (co < g.cout && k < g.k)
-              put_elem<ESZ>(wds, e, ld_elem<ESZ>(a.w + ((size_t)co * g.k + k) * ESZ));
+            const uint32_t off = (co < g.cout && k < g.k) ? (uint32_t)(co * g.k + k) * ESZ : kOOB;
+            v[j][e] = bload_elem<ESZ>(rw, off);
           }
-          ra[j] = i32x4{(int)wds[0], (int)wds[1], (int)wds[2], (int)wds[3]};
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          uint32_t wd[4] = {0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < VE; ++e) wd[e * ESZ / 4] |= v[j][e] << (8 * ((e * ESZ) & 3));
+          ra[j] = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
         }
       }
-      // B: activations, element-wise gather with bounds tests.
+      // B: activations, element-wise gather; every load is issued before
+      // any is used.
       {
         constexpr int G = 256 / TPX;
         constexpr int CH = 8 / G;
@@ -209,14 +276,16 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
         int ci = k_first - tap * g.c;
         int kh = tap / g.kw;
         int kw = tap - kh * g.kw;
-        for (int j = 0; j < CH; ++j) {
-          uint32_t wds[4] = {0, 0, 0, 0};
+        uint32_t v[CH][VE];
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+#pragma unroll
           for (int e = 0; e < VE; ++e) {
             const int hi = b_hi0[0] + kh;
             const int wi = b_wi0[0] + kw;
-            if (kh < g.kh && (unsigned)hi < (unsigned)g.h && (unsigned)wi < (unsigned)g.w)
-              put_elem<ESZ>(wds, e,
-                            ld_elem<ESZ>(a.x + (size_t)(b_base[0] + (kh * g.w + kw) * g.c + ci) * ESZ));
+            const bool ok = kh < g.kh && (unsigned)hi < (unsigned)g.h && (unsigned)wi < (unsigned)g.w;
+            const uint32_t off = ok ? (uint32_t)(b_base[0] + (kh * g.w + kw) * g.c + ci) * ESZ : kOOB;
+            v[j][e] = bload_elem<ESZ>(rx, off);
             if (++ci == g.c) {
               ci = 0;
               if (++kw == g.kw) {
@@ -225,185 +294,208 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
               }
             }
           }
-          rb[j] = i32x4{(int)wds[0], (int)wds[1], (int)wds[2], (int)wds[3]};
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          uint32_t wd[4] = {0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < VE; ++e) wd[e * ESZ / 4] |= v[j][e] << (8 * ((e * ESZ) & 3));
+          rb[j] = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
         }
       }
+    } else if constexpr (LOADER == LOAD_TAP) {
+      // Cin*ESZ % 128 == 0: the whole K-tile is one tap, one 128-byte block of
+      // channels; the tap offset is the same for every lane.
+      const bool live = kt < nkt_all;
+      const int tap = t_kh * g.kw + t_kw;
+      const int soff_b = (t_kh * g.w + t_kw) * cbytes + t_cb;
+      const int soff_a = kt * kBKB;
+#pragma unroll
+      for (int j = 0; j < ACH; ++j) ra[j] = bload16s(rw, live ? voff_a[j] : kOOB, live ? soff_a : 0);
+#pragma unroll
+      for (int j = 0; j < BCH; ++j) {
+        const bool ok = live && ((tmask[j] >> (tap & 31)) & 1u);
+        rb[j] = bload16s(rxt, ok ? voff_b[j] : kOOB, live ? soff_b : 0);
+      }
+      t_cb += kBKB;
+      if (t_cb == cbytes) {
+        t_cb = 0;
+        if (++t_kw == g.kw) {
+          t_kw = 0;
+          ++t_kh;
+        }
+      }
+    } else if constexpr (LOADER == LOAD_1X1) {
+      // K = Cin: chunk c of tile kt is valid while kt*128 + 16c < Cin*ESZ.
+      const int soff = kt * kBKB;
+      const bool cin_ok = (tid & 7) * 16 < cbytes - soff;
+#pragma unroll
+      for (int j = 0; j < ACH; ++j) ra[j] = bload16s(rw, cin_ok ? voff_a[j] : kOOB, cin_ok ? soff : 0);
+#pragma unroll
+      for (int j = 0; j < BCH; ++j) rb[j] = bload16s(rx, cin_ok ? voff_b[j] : kOOB, cin_ok ? soff : 0);
     } else {
       const int kc = kb + (tid & 7) * VE;  // first element of this thread's chunk
-      // A: weights [cout][K], K-contiguous, 16-byte chunks.
+      const bool kin = kc < g.k;
+#pragma unroll
       for (int j = 0; j < ACH; ++j) {
         const int co = co0 + (tid >> 3) + 32 * j;
-        ra[j] = (co < g.cout && kc < g.k) ? ld16(a.w + ((size_t)co * g.k + kc) * ESZ) : zero4();
+        ra[j] = bload16(rw, (co < g.cout && kin) ? (uint32_t)(co * g.k + kc) * ESZ : kOOB);
       }
-      if constexpr (LOADER == LOAD_1X1) {
-        for (int j = 0; j < BCH; ++j)
-          rb[j] = (b_hi0[j] == 0 && kc < g.k) ? ld16(a.x + (size_t)(b_base[j] + kc) * ESZ) : zero4();
-      } else {
-        const int tap_off = (kh_s * g.w + kw_s) * g.c + ci_s;
-        const bool kin = kh_s < g.kh;
+      {
+        // this thread's chunk starts at element kc = (kh, kw, ci) of the
+        // pixel's receptive field; Cin * ESZ % 16 == 0 keeps it in one tap
+        int tap, ci, kh, kw;
+        divmod_small(kc, g.c, a.rcp_c, tap, ci);
+        divmod_small(tap, g.kw, a.rcp_kw, kh, kw);
+        const int tap_off = (kh * g.w + kw) * g.c + ci;
+        const bool khin = kh < g.kh;
+#pragma unroll
         for (int j = 0; j < BCH; ++j) {
-          const int hi = b_hi0[j] + kh_s;
-          const int wi = b_wi0[j] + kw_s;
-          rb[j] = (kin && (unsigned)hi < (unsigned)g.h && (unsigned)wi < (unsigned)g.w)
-                      ? ld16(a.x + (size_t)(b_base[j] + tap_off) * ESZ)
-                      : zero4();
-        }
-        // advance this thread's k by one tile
-        ci_s += BKE;
-        while (ci_s >= g.c) {
-          ci_s -= g.c;
-          if (++kw_s == g.kw) {
-            kw_s = 0;
-            ++kh_s;
-          }
+          const int hi = b_hi0[j] + kh;
+          const int wi = b_wi0[j] + kw;
+          const bool ok = khin && (unsigned)hi < (unsigned)g.h && (unsigned)wi < (unsigned)g.w;
+          rb[j] = bload16(rx, ok ? (uint32_t)(b_base[j] + tap_off) * ESZ : kOOB);
         }
       }
     }
   };
 
-  auto stash = [&](int buf) {
-    char* A = As + buf * TCO * kLdsRow;
-    char* B = Bs + buf * TPX * kLdsRow;
+  auto stash = [&](int buf, const i32x4 (&ra)[ACH], const i32x4 (&rb)[BCH]) {
+    char* A = As + buf * TCO * kBKB;
+    char* B = Bs + buf * TPX * kBKB;
     if constexpr (LOADER == LOAD_GENERIC) {
       {
         constexpr int G = 256 / TCO;
         constexpr int CH = 8 / G;
         const int row = tid % TCO, grp = tid / TCO;
-        for (int j = 0; j < CH; ++j)
-          *reinterpret_cast<i32x4*>(A + row * kLdsRow + (grp * CH + j) * 16) = ra[j];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) *reinterpret_cast<i32x4*>(A + lds_off(row, grp * CH + j)) = ra[j];
       }
       {
         constexpr int G = 256 / TPX;
         constexpr int CH = 8 / G;
         const int row = tid % TPX, grp = tid / TPX;
-        for (int j = 0; j < CH; ++j)
-          *reinterpret_cast<i32x4*>(B + row * kLdsRow + (grp * CH + j) * 16) = rb[j];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) *reinterpret_cast<i32x4*>(B + lds_off(row, grp * CH + j)) = rb[j];
       }
     } else {
-      const int col = (tid & 7) * 16;
-      for (int j = 0; j < ACH; ++j)
-        *reinterpret_cast<i32x4*>(A + ((tid >> 3) + 32 * j) * kLdsRow + col) = ra[j];
-      for (int j = 0; j < BCH; ++j)
-        *reinterpret_cast<i32x4*>(B + ((tid >> 3) + 32 * j) * kLdsRow + col) = rb[j];
+      const int col = tid & 7;
+#pragma unroll
+      for (int j = 0; j < ACH; ++j) *reinterpret_cast<i32x4*>(A + lds_off((tid >> 3) + 32 * j, col)) = ra[j];
+#pragma unroll
+      for (int j = 0; j < BCH; ++j) *reinterpret_cast<i32x4*>(B + lds_off((tid >> 3) + 32 * j, col)) = rb[j];
     }
   };
 
   acc_t acc[FCO][FPX];
+#pragma unroll
   for (int i = 0; i < FCO; ++i)
+#pragma unroll
     for (int j = 0; j < FPX; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
-  const int lrow = lane & 15;
-  const int lk = (lane >> 4) * 16;
-  const int a_row0 = wco * (TCO / WCO) + lrow;
-  const int b_row0 = wpx * (TPX / WPX) + lrow;
+  // MFMA operand addresses within a stage: row (lane & 15) of each 16-row
+  // fragment, chunk 4*s + (lane >> 4) of the tile.
+  const int a_row0 = wco * (TCO / WCO) + (lane & 15);
+  const int b_row0 = wpx * (TPX / WPX) + (lane & 15);
 
-  const int nkt = (g.k + BKE - 1) / BKE;
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) fetch(kt + 1);
-    const char* A = As + cur * TCO * kLdsRow;
-    const char* B = Bs + cur * TPX * kLdsRow;
+  // MFMAs of the tile in LDS buffer `buf`; when `more`, the next tile
+  // (registers ra_n/rb_n) is written into buffer `nbuf` between the first and
+  // the second K-step, so the LDS stores overlap the matrix work.
+  auto compute = [&](int buf, const i32x4 (&ra_n)[ACH], const i32x4 (&rb_n)[BCH], int nbuf, bool more) {
+    const char* A = As + buf * TCO * kBKB;
+    const char* B = Bs + buf * TPX * kBKB;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+      const int c = 4 * s + (lane >> 4);
       i32x4 af[FCO], bf[FPX];
 #pragma unroll
-      for (int i = 0; i < FCO; ++i) af[i] = ld16(A + (a_row0 + 16 * i) * kLdsRow + s * 64 + lk);
+      for (int i = 0; i < FCO; ++i)
+        af[i] = *reinterpret_cast<const i32x4*>(A + lds_off(a_row0 + 16 * i, c));
 #pragma unroll
-      for (int j = 0; j < FPX; ++j) bf[j] = ld16(B + (b_row0 + 16 * j) * kLdsRow + s * 64 + lk);
+      for (int j = 0; j < FPX; ++j)
+        bf[j] = *reinterpret_cast<const i32x4*>(B + lds_off(b_row0 + 16 * j, c));
+      if (s == 0 && more) stash(nbuf, ra_n, rb_n);
 #pragma unroll
       for (int i = 0; i < FCO; ++i)
 #pragma unroll
         for (int j = 0; j < FPX; ++j) acc[i][j] = Mfma<ESZ>::run(af[i], bf[j], acc[i][j]);
     }
-    if (more) stash(cur ^ 1);
-    __syncthreads();
+  };
+
+  const int nkt = (g.k + BKE - 1) / BKE;
+  // Pipeline. LDS buffer t%2 holds K-tile t while it is consumed; register
+  // set r holds a tile in flight from global memory. Step t: one barrier
+  // (tile t is visible, and buffer (t+1)%2 is no longer read by anyone),
+  // then the MFMAs of tile t run while tile t+1 is copied from its register
+  // set into the other buffer, then that register set is re-issued for tile
+  // t+1+D. Loads for tiles at or beyond nkt are all out of range (zero, no
+  // memory traffic), so fetches need no guard.
+  i32x4 ra[D][ACH], rb[D][BCH];
+  {
+    i32x4 a0[ACH], b0[BCH];
+    fetch(0, a0, b0);
+#pragma unroll
+    for (int d = 0; d < D; ++d) fetch(1 + d, ra[d], rb[d]);
+    stash(0, a0, b0);
+  }
+  int t = 0;
+  for (; t + D <= nkt; t += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      __syncthreads();
+      compute((t + d) & 1, ra[d], rb[d], (t + d + 1) & 1, t + d + 1 < nkt);
+      fetch(t + d + 1 + D, ra[d], rb[d]);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if (t + d < nkt) {
+      __syncthreads();
+      compute((t + d) & 1, ra[d], rb[d], (t + d + 1) & 1, t + d + 1 < nkt);
+    }
   }
 
   // ---- fused epilogue -------------------------------------------------
   const int co_w = co0 + wco * (TCO / WCO) + 4 * (lane >> 4);
   const int px_w = px0 + wpx * (TPX / WPX) + (lane & 15);
-  const bool vec4 = (g.cout & 3) == 0;
 #pragma unroll
   for (int i = 0; i < FCO; ++i) {
     const int co = co_w + 16 * i;
     if (co >= g.cout) continue;
-    // per-channel constants of the 4 channels this lane owns
-    float bsf[4] = {0.f, 0.f, 0.f, 0.f};
-    int bsi[4] = {0, 0, 0, 0};
-    float scl[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < 4; ++r) {
-      if (co + r < g.cout) {
-        if constexpr (ESZ == 2) {
-          if (a.e.bias) bsf[r] = a.e.bias[co + r];
-        } else {
-          if (a.e.ibias) bsi[r] = a.e.ibias[co + r];
-          if (a.e.scale) scl[r] = a.e.scale[co + r];
-        }
-      }
-    }
+    const QuadConsts q = load_quad_consts<ESZ>(a.e, co, g.cout);
 #pragma unroll
     for (int j = 0; j < FPX; ++j) {
       const int px = px_w + 16 * j;
-      if (px >= g.m) continue;
-      const size_t off = (size_t)px * g.cout + co;
-      if constexpr (ESZ == 2) {
-        uint32_t hbits[4];
-        for (int r = 0; r < 4; ++r)
-          hbits[r] = f32_to_bf16_bits(apply_act(acc[i][j][r] + bsf[r], a.e.act));
-        uint16_t* yp = reinterpret_cast<uint16_t*>(a.y) + off;
-        if (vec4) {
-          uint2 v;
-          v.x = hbits[0] | (hbits[1] << 16);
-          v.y = hbits[2] | (hbits[3] << 16);
-          *reinterpret_cast<uint2*>(yp) = v;
-        } else {
-          for (int r = 0; r < 4; ++r)
-            if (co + r < g.cout) yp[r] = (uint16_t)hbits[r];
-        }
-      } else if (a.out_kind == OUT_I32) {
-        int v[4];
-        for (int r = 0; r < 4; ++r) {
-          v[r] = acc[i][j][r] + bsi[r];
-          if (a.e.act == ACT_RELU) v[r] = v[r] > 0 ? v[r] : 0;
-        }
-        int32_t* yp = reinterpret_cast<int32_t*>(a.y) + off;
-        if (vec4) {
-          *reinterpret_cast<i32x4*>(yp) = i32x4{v[0], v[1], v[2], v[3]};
-        } else {
-          for (int r = 0; r < 4; ++r)
-            if (co + r < g.cout) yp[r] = v[r];
-        }
-      } else {
-        uint32_t q[4];
-        for (int r = 0; r < 4; ++r)
-          q[r] = (uint32_t)(requant_i8(acc[i][j][r] + bsi[r], scl[r], a.e.act) & 0xff);
-        int8_t* yp = reinterpret_cast<int8_t*>(a.y) + off;
-        if (vec4) {
-          *reinterpret_cast<uint32_t*>(yp) = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-        } else {
-          for (int r = 0; r < 4; ++r)
-            if (co + r < g.cout) yp[r] = (int8_t)q[r];
-        }
-      }
+      if (px < g.m) store_quad<ESZ>(acc[i][j], q, co, px, g.cout, a.out_kind, a.e.act, a.y);
     }
   }
 }
+
+// Register stages per loader: the element-wise gather issues up to 64 loads
+// per thread per tile and stays single-staged.
+#ifndef IGEMM_STAGES
+#define IGEMM_STAGES 2
+#endif
+template <int LOADER>
+constexpr int kStages = LOADER == LOAD_GENERIC ? 1 : IGEMM_STAGES;
 
 template <int ESZ, int TCO, int TPX, int WCO, int WPX>
 hipError_t launch_tile(int loader, const IgArgs& args, int nwg, hipStream_t s) {
   switch (loader) {
     case LOAD_GENERIC:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_GENERIC>), dim3(nwg), dim3(256), 0, s, args);
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_GENERIC, kStages<LOAD_GENERIC>>), dim3(nwg),
+                         dim3(256), 0, s, args);
       break;
     case LOAD_VEC:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_VEC>), dim3(nwg), dim3(256), 0, s, args);
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_VEC, kStages<LOAD_VEC>>), dim3(nwg), dim3(256),
+                         0, s, args);
+      break;
+    case LOAD_1X1:
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_1X1, kStages<LOAD_1X1>>), dim3(nwg), dim3(256),
+                         0, s, args);
       break;
     default:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_1X1>), dim3(nwg), dim3(256), 0, s, args);
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_TAP, kStages<LOAD_TAP>>), dim3(nwg), dim3(256),
+                         0, s, args);
       break;
   }
   return hipGetLastError();
@@ -434,6 +526,11 @@ hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const 
   args.e = e;
   args.g = p->g;
   args.out_kind = p->out_kind;
+  args.x_bytes = (int)p->x_bytes;
+  args.w_bytes = (int)p->w_bytes;
+  args.rcp_c = 1.0f / (float)p->g.c;
+  args.rcp_kw = 1.0f / (float)p->g.kw;
+  args.x_shift = (p->g.ph * p->g.w + p->g.pw) * p->g.c * p->in_esz;
   const TileCfg& t = kTiles[p->tile];
   args.nco_tiles = (p->g.cout + t.tco - 1) / t.tco;
   const int npx = (p->g.m + t.tpx - 1) / t.tpx;

@@ -12,14 +12,17 @@ namespace convnhwc {
 enum Path {
   PATH_IGEMM = 1,  // MFMA implicit GEMM (bf16 / int8), dense KxK and 1x1
   PATH_DW = 2,     // depthwise 3x3, VALU stencil
-  PATH_F32 = 3     // true-fp32 direct convolution, VALU
+  PATH_F32 = 3,    // true-fp32 direct convolution, VALU
+  PATH_SMALLK = 4  // MFMA, operands straight from global memory: short K, odd Cin
 };
 
 // How the implicit-GEMM kernel gathers its activation operand.
 enum Loader {
   LOAD_GENERIC = 0,  // element-wise gather: any channel count
   LOAD_VEC = 1,      // 16-byte channel vectors: c_in * elem_size % 16 == 0
-  LOAD_1X1 = 2       // 1x1, stride 1, pad 0: the input is the GEMM operand
+  LOAD_1X1 = 2,      // 1x1, stride 1, pad 0: the input is the GEMM operand
+  LOAD_TAP = 3       // Cin * elem_size % 128 == 0 and KH*KW <= 32: every K-tile
+                     // lies in one tap, so the tap offset is wave-uniform
 };
 
 // One tile configuration of the implicit-GEMM kernel: a workgroup of four
@@ -57,6 +60,9 @@ namespace convnhwc {
 
 hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                         hipStream_t s);
+hipError_t launch_smallk(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
+                         hipStream_t s);
+void smallk_shape(const Geometry& g, int esz, int* fco, int* ks);
 hipError_t launch_dw(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                      hipStream_t s);
 hipError_t launch_f32(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,

@@ -83,11 +83,17 @@ def test_prepare_null():
 
 
 @pytest.mark.parametrize("layer,expect", [
-    (dict(c_in=3, c_out=32, dtype="bf16"), "igemm dtype=bf16 out=bf16 loader=generic"),
+    (dict(c_in=3, c_out=32, dtype="bf16"), "smallk dtype=bf16 out=bf16"),
+    (dict(c_in=61, c_out=32, dtype="bf16"), "igemm dtype=bf16 out=bf16 loader=generic"),
     (dict(c_in=32, c_out=64, dtype="bf16"), "loader=vec16"),
     (dict(c_in=64, c_out=64, kh=1, kw=1, pad=(0, 0), dtype="bf16"), "loader=1x1"),
-    (dict(c_in=64, c_out=64, kh=1, kw=1, pad=(0, 0), stride=(2, 2), dtype="bf16"), "loader=vec16"),
-    (dict(c_in=8, c_out=8, dtype="i8", out_dtype="i8"), "loader=generic"),  # 8 bytes per pixel
+    (dict(c_in=64, c_out=64, kh=1, kw=1, pad=(0, 0), stride=(2, 2), dtype="bf16"), "loader=tap"),
+    (dict(c_in=64, c_out=64, dtype="bf16"), "loader=tap"),
+    (dict(c_in=128, c_out=64, kh=5, kw=5, pad=(2, 2), dtype="i8"), "loader=tap"),
+    (dict(c_in=128, c_out=64, kh=7, kw=5, pad=(3, 3), dtype="i8"), "loader=vec16"),  # 35 taps > 32
+    (dict(c_in=8, c_out=8, dtype="i8", out_dtype="i8"), "smallk dtype=i8"),  # 8 bytes per pixel, K=72
+    (dict(c_in=24, c_out=8, dtype="i8", out_dtype="i8"), "loader=generic"),  # K = 216 bytes
+    (dict(c_in=40, c_out=8, dtype="i8", out_dtype="i8"), "loader=generic"),  # K = 360 bytes
     (dict(c_in=16, c_out=16, dtype="i8", out_dtype="i32"), "out=i32 loader=vec16"),
     (dict(c_in=64, c_out=64, groups=64, dtype="i8"), "dw3x3 dtype=i8"),
     (dict(c_in=1, c_out=8, dtype="f32"), "direct_f32"),

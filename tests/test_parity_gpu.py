@@ -46,7 +46,33 @@ DENSE = [
     L("i8_c24_generic", 1, 20, 20, 24, 40, 3, 3, (1, 1), (1, 1), dtype="i8", out="i32", act="none"),
     L("i8_cout61", 1, 19, 21, 32, 61, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="relu6"),
     L("i8_deepK", 1, 8, 8, 512, 64, 3, 3, (1, 1), (1, 1), dtype="i8", out="i32", act="none"),
+    # tap loader (Cin * elem_size a multiple of 128 bytes)
+    L("bf16_tap_5x3_pad21", 1, 23, 17, 64, 40, 5, 3, (2, 1), (2, 1), act="relu"),
+    L("bf16_tap_1x1_s2", 1, 18, 18, 128, 40, 1, 1, (2, 2), act="relu6"),
+    L("bf16_tap_pad3", 2, 9, 9, 64, 16, 3, 3, (1, 1), (3, 3)),
+    L("i8_tap_3x3_s2_mish", 1, 19, 21, 128, 72, 3, 3, (2, 2), (1, 1), dtype="i8", out="i8", act="mish"),
+    L("i8_tap_5x5_i32", 1, 13, 11, 128, 24, 5, 5, (1, 1), (2, 2), dtype="i8", out="i32", act="none"),
+    L("i8_vec_7x7_i32", 1, 13, 11, 128, 24, 7, 7, (1, 1), (3, 3), dtype="i8", out="i32", act="none"),
 ]
+
+# Short-K layers with odd channel counts: the LDS-free small-K kernel (auto).
+SMALLK = [
+    L("sk_bf16_c3_s1", 1, 41, 45, 3, 32, 3, 3, (1, 1), (1, 1)),
+    L("sk_bf16_c3_s2_cout8", 2, 33, 30, 3, 8, 3, 3, (2, 2), (1, 1), act="relu6"),
+    L("sk_bf16_c1_5x5_cout70", 1, 20, 17, 1, 70, 5, 5, (1, 2), (2, 1), act="relu"),
+    L("sk_bf16_c7_k63", 1, 19, 23, 7, 40, 3, 3, (1, 1), (1, 1), act="none"),
+    L("sk_i8_stem10x4", 1, 49, 10, 1, 64, 10, 4, (2, 2), (5, 1), dtype="i8", out="i8", act="relu"),
+    L("sk_i8_c3_i32", 2, 15, 17, 3, 24, 3, 3, (1, 1), (1, 1), dtype="i8", out="i32", act="none"),
+    L("sk_i8_c8_mish", 1, 21, 19, 8, 130, 3, 3, (2, 1), (0, 1), dtype="i8", out="i8", act="mish"),
+]
+
+
+@pytest.mark.parametrize("layer", SMALLK, ids=[l.name for l in SMALLK])
+def test_smallk(layer):
+    t = random_layer_tensors(layer, LAW[layer.dtype], seed=18)
+    y, conv = H.gpu_run(layer, t["x"], t)
+    assert "smallk" in conv.describe(), conv.describe()
+    H.check_layer_full(layer, t["x"], t, y, "%s [%s]" % (layer.name, conv.describe()))
 
 
 @pytest.mark.parametrize("layer", DENSE, ids=[l.name for l in DENSE])
@@ -152,7 +178,8 @@ def _guarded_run(layer, t, algo=0):
     return y
 
 
-@pytest.mark.parametrize("layer", [DENSE[0], DENSE[5], DENSE[8], DENSE[14], DW[0], DW[3], F32[1]],
+@pytest.mark.parametrize("layer", [DENSE[0], DENSE[5], DENSE[8], DENSE[14], DW[0], DW[3], F32[1], SMALLK[2],
+                                   SMALLK[6]],
                          ids=lambda l: l.name)
 def test_guard_bands_and_determinism(layer):
     t = random_layer_tensors(layer, LAW[layer.dtype], seed=16)
