@@ -51,6 +51,40 @@ int choose_tile(const Geometry& g, int esz) {
   return t64x64;
 }
 
+// Split the reduction when the output tiles alone would fill fewer than half
+// of the 256 CUs and each split still has >= 8 K-tiles of 128 bytes: aim at
+// ~512 workgroups, at most 8 splits. The splits' raw partial sums go to a device
+// workspace owned by the plan; a second kernel adds them in split order and
+// applies the epilogue. If the workspace cannot be allocated (no device, out
+// of memory) the plan runs unsplit, which is slower but the same arithmetic
+// up to the order of the fp32 additions.
+void plan_split_k(conv_plan* p) {
+  const Geometry& g = p->g;
+  const TileCfg& t = kTiles[p->tile];
+  const long nwg = (long)((g.cout + t.tco - 1) / t.tco) * ((g.m + t.tpx - 1) / t.tpx);
+  const int nkt = p->kt_per;
+  if (nwg >= 128 || nkt < 16 || (g.cout & 3)) return;
+  int s = (int)((512 + nwg - 1) / nwg);
+  s = s < 8 ? s : 8;
+  s = s < nkt / 8 ? s : nkt / 8;
+  if (s < 2) return;
+  const int per = (nkt + s - 1) / s;
+  s = (nkt + per - 1) / per;
+  if (s < 2) return;
+  const int64_t bytes = (int64_t)s * g.m * g.cout * 4;
+  int dev = 0;
+  void* ws = nullptr;
+  if (hipGetDevice(&dev) != hipSuccess || hipMalloc(&ws, bytes) != hipSuccess) {
+    (void)hipGetLastError();  // clear the failure; run unsplit
+    return;
+  }
+  p->ksplit = s;
+  p->kt_per = per;
+  p->ws = ws;
+  p->ws_bytes = bytes;
+  p->ws_device = dev;
+}
+
 bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
   if (!a || !b || na <= 0 || nb <= 0) return false;
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -117,7 +151,7 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
     path = PATH_DW;
     loader = (d->c_in * in_esz) % 16 == 0 ? LOAD_VEC : LOAD_GENERIC;
   }
-  if (d->algo != 0 && (path != PATH_IGEMM || d->algo < 1 || d->algo > kNumTiles)) return CONV_E_UNSUPPORTED;
+  if (d->algo != 0 && (path != PATH_IGEMM || d->algo < 1 || d->algo > kAlgoPatch)) return CONV_E_UNSUPPORTED;
   // A short reduction over an odd channel count (the 3-channel and 1-channel
   // stems) goes to the LDS-free small-K kernel unless a tile is forced.
   if (path == PATH_IGEMM && loader == LOAD_GENERIC && d->algo == 0 &&
@@ -149,7 +183,21 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
   p->in_esz = in_esz;
   p->out_esz = out_esz;
   p->out_kind = ot == CONV_F32 ? OUT_F32 : ot == CONV_BF16 ? OUT_BF16 : ot == CONV_I8 ? OUT_I8 : OUT_I32;
+  // 3x3 layers with 64-byte channel blocks can be forced onto the halo-patch
+  // kernel (algo kAlgoPatch). It is not chosen automatically: on MI355X the
+  // implicit GEMM measured faster on every workload layer.
+  if (path == PATH_IGEMM && patch_eligible(g, in_esz, d->groups)) {
+    if (d->algo == kAlgoPatch) path = PATH_PATCH;
+  } else if (d->algo == kAlgoPatch) {
+    delete p;
+    *out = nullptr;
+    return CONV_E_UNSUPPORTED;
+  }
+  p->path = path;
   p->tile = path == PATH_IGEMM ? (d->algo ? d->algo - 1 : choose_tile(g, in_esz)) : 0;
+  p->ksplit = 1;
+  p->kt_per = (int)((g.k * (int64_t)in_esz + 127) / 128);
+  if (path == PATH_IGEMM) plan_split_k(p);
   p->x_bytes = x_bytes;
   p->w_bytes = w_bytes;
   p->y_bytes = y_bytes;
@@ -187,6 +235,7 @@ conv_status conv_run(const conv_plan* p, const void* x, const void* w, const voi
     case PATH_IGEMM: err = launch_igemm(p, x, w, e, y, s); break;
     case PATH_DW: err = launch_dw(p, x, w, e, y, s); break;
     case PATH_SMALLK: err = launch_smallk(p, x, w, e, y, s); break;
+    case PATH_PATCH: err = launch_patch(p, x, w, e, y, s); break;
     default: err = launch_f32(p, x, w, e, y, s); break;
   }
   if (err != hipSuccess) {
@@ -197,6 +246,13 @@ conv_status conv_run(const conv_plan* p, const void* x, const void* w, const voi
 }
 
 conv_status conv_destroy(conv_plan* p) {
+  if (p && p->ws) {
+    int cur = 0;
+    const bool have = hipGetDevice(&cur) == hipSuccess;
+    if (have && cur != p->ws_device) (void)hipSetDevice(p->ws_device);
+    (void)hipFree(p->ws);
+    if (have && cur != p->ws_device) (void)hipSetDevice(cur);
+  }
   delete p;
   return CONV_OK;
 }
@@ -219,9 +275,14 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
     const long nwg = (long)((p->g.cout + t.tco - 1) / t.tco) * ((p->g.m + t.tpx - 1) / t.tpx);
     std::snprintf(buf, len,
                   "igemm dtype=%s out=%s loader=%s tile=%d co%dxpx%d waves=%dx%d wgs=%ld m=%d k=%d "
-                  "kernel=igemm_kernel<%d, %d, %d, %d, %d, %d>",
+                  "ksplit=%d kernel=igemm_kernel<%d, %d, %d, %d, %d, %d>",
                   kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], p->tile + 1, t.tco, t.tpx, t.wco,
-                  t.wpx, nwg, p->g.m, p->g.k, p->in_esz, t.tco, t.tpx, t.wco, t.wpx, p->loader);
+                  t.wpx, nwg, p->g.m, p->g.k, p->ksplit, p->in_esz, t.tco, t.tpx, t.wco, t.wpx, p->loader);
+  } else if (p->path == PATH_PATCH) {
+    const int s = p->g.sh, bh = s == 1 ? 16 : 8, cb = patch_cb(p->g, p->in_esz);
+    std::snprintf(buf, len, "patch3x3 dtype=%s out=%s tile=%d stride=%d block=%dx16 cb=%d m=%d k=%d "
+                  "kernel=patch3x3_kernel<%d, %d, %d, %d>", kDt[p->d.dtype], kDt[p->d.out_dtype], kAlgoPatch, s, bh,
+                  cb, p->g.m, p->g.k, p->in_esz, s, bh, cb);
   } else if (p->path == PATH_SMALLK) {
     int fco, ks;
     smallk_shape(p->g, p->in_esz, &fco, &ks);
@@ -241,7 +302,7 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
   return CONV_OK;
 }
 
-int32_t conv_algo_count(void) { return kNumTiles; }
+int32_t conv_algo_count(void) { return kAlgoPatch; }
 
 conv_status conv_mosaic_pack(const void* tiles, int32_t in_dtype, void* canvas, int32_t out_dtype, int32_t m,
                              int32_t th, int32_t tw, int32_t c, int32_t c_pad, void* stream) {

@@ -33,6 +33,8 @@
 // (l % 16) and 16 bytes of K at byte offset 16*(l / 16); it receives D rows
 // 4*(l/16) .. 4*(l/16)+3 of column l % 16, i.e. four consecutive output
 // channels of one pixel, which the epilogue stores as one NHWC vector.
+#include <algorithm>
+
 #include "device_common.h"
 #include "mfma_epilogue.h"
 #include "plan.h"
@@ -68,6 +70,10 @@ struct IgArgs {
   float rcp_c;   // 1.0f / Cin
   float rcp_kw;  // 1.0f / KW
   int x_shift;   // LOAD_TAP: bytes the x descriptor starts before x
+  int px_fastest;  // tile order: pixel tiles vary fastest (weights > activations)
+  int ksplit;    // K-splits (gridDim.y); > 1 writes raw partial sums to ws
+  int kt_per;    // K-tiles per split
+  void* ws;      // [ksplit][m][cout] fp32 / int32 partial sums
 };
 
 template <int ESZ>
@@ -158,12 +164,16 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
   const __amdgpu_buffer_rsrc_t rw = rsrc(a.w, a.w_bytes);
 
   // Tiles are handed to the 8 XCDs round-robin by workgroup id; remap so each
-  // XCD (own L2) gets a contiguous run of tiles that share activation rows.
+  // XCD (own L2) gets a contiguous run of tiles. With the channel tile varying
+  // fastest an XCD's run shares activation rows (layers whose activations
+  // outweigh their weights); with the pixel tile fastest it shares weight
+  // rows (deep layers whose weights are the larger operand).
   int lin = blockIdx.x;
   const int nwg = gridDim.x;
   if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
-  const int co0 = (lin % a.nco_tiles) * TCO;
-  const int px0 = (lin / a.nco_tiles) * TPX;
+  const int npx_tiles = nwg / a.nco_tiles;
+  const int co0 = (a.px_fastest ? lin / npx_tiles : lin % a.nco_tiles) * TCO;
+  const int px0 = (a.px_fastest ? lin % npx_tiles : lin / a.nco_tiles) * TPX;
   const int hw_o = g.ho * g.wo;
 
   // ---- per-thread loader state -------------------------------------
@@ -209,7 +219,17 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
   __amdgpu_buffer_rsrc_t rxt = rx;
   const int cbytes = g.c * ESZ;
   const int nkt_all = (g.k * ESZ + kBKB - 1) / kBKB;
+  // K-tiles [kt0, kt0 + nkt) belong to this workgroup's split
+  const int kt0 = blockIdx.y * a.kt_per;
+  const int nkt = min(a.kt_per, nkt_all - kt0);
   int t_kh = 0, t_kw = 0, t_cb = 0;  // uniform tap state of the next fetch
+  if constexpr (LOADER == LOAD_TAP) {
+    const int kb0 = kt0 * kBKB;
+    const int tap0 = kb0 / cbytes;
+    t_cb = kb0 - tap0 * cbytes;
+    t_kh = tap0 / g.kw;
+    t_kw = tap0 - t_kh * g.kw;
+  }
   if constexpr (LOADER == LOAD_TAP || LOADER == LOAD_1X1) {
     const int c16 = (tid & 7) * 16;
 #pragma unroll
@@ -421,7 +441,6 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
     }
   };
 
-  const int nkt = (g.k + BKE - 1) / BKE;
   // Pipeline. LDS buffer t%2 holds K-tile t while it is consumed; register
   // set r holds a tile in flight from global memory. Step t: one barrier
   // (tile t is visible, and buffer (t+1)%2 is no longer read by anyone),
@@ -432,9 +451,9 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
   i32x4 ra[D][ACH], rb[D][BCH];
   {
     i32x4 a0[ACH], b0[BCH];
-    fetch(0, a0, b0);
+    fetch(kt0, a0, b0);
 #pragma unroll
-    for (int d = 0; d < D; ++d) fetch(1 + d, ra[d], rb[d]);
+    for (int d = 0; d < D; ++d) fetch(kt0 + 1 + d, ra[d], rb[d]);
     stash(0, a0, b0);
   }
   int t = 0;
@@ -443,7 +462,7 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
     for (int d = 0; d < D; ++d) {
       __syncthreads();
       compute((t + d) & 1, ra[d], rb[d], (t + d + 1) & 1, t + d + 1 < nkt);
-      fetch(t + d + 1 + D, ra[d], rb[d]);
+      fetch(kt0 + t + d + 1 + D, ra[d], rb[d]);
     }
   }
 #pragma unroll
@@ -457,6 +476,21 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
   // ---- fused epilogue -------------------------------------------------
   const int co_w = co0 + wco * (TCO / WCO) + 4 * (lane >> 4);
   const int px_w = px0 + wpx * (TPX / WPX) + (lane & 15);
+  if (a.ksplit > 1) {
+    // raw partial sums of this split; Cout % 4 == 0 on this path
+    acc_t* ws = reinterpret_cast<acc_t*>(a.ws) + (size_t)blockIdx.y * g.m * (g.cout / 4);
+#pragma unroll
+    for (int i = 0; i < FCO; ++i) {
+      const int co = co_w + 16 * i;
+      if (co >= g.cout) continue;
+#pragma unroll
+      for (int j = 0; j < FPX; ++j) {
+        const int px = px_w + 16 * j;
+        if (px < g.m) ws[(size_t)px * (g.cout / 4) + co / 4] = acc[i][j];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FCO; ++i) {
     const int co = co_w + 16 * i;
@@ -470,6 +504,24 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
   }
 }
 
+// Sum of the K-split partials in split order (the same order on every run),
+// then the fused epilogue. One lane per output quad (4 channels).
+template <int ESZ>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const void* ws, int ksplit, int m, int cout, Epi e,
+                                                            int out_kind, void* y) {
+  typedef typename Mfma<ESZ>::acc_t acc_t;
+  const int nq = cout / 4;
+  const long total = (long)m * nq;
+  const acc_t* w = reinterpret_cast<const acc_t*>(ws);
+  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (long)gridDim.x * blockDim.x) {
+    acc_t acc = w[q];
+    for (int s = 1; s < ksplit; ++s) acc += w[(size_t)s * total + q];
+    const int px = (int)(q / nq);
+    const int co = (int)(q - (long)px * nq) * 4;
+    store_quad<ESZ>(acc, load_quad_consts<ESZ>(e, co, cout), co, px, cout, out_kind, e.act, y);
+  }
+}
+
 // Register stages per loader: the element-wise gather issues up to 64 loads
 // per thread per tile and stays single-staged.
 #ifndef IGEMM_STAGES
@@ -479,7 +531,7 @@ template <int LOADER>
 constexpr int kStages = LOADER == LOAD_GENERIC ? 1 : IGEMM_STAGES;
 
 template <int ESZ, int TCO, int TPX, int WCO, int WPX>
-hipError_t launch_tile(int loader, const IgArgs& args, int nwg, hipStream_t s) {
+hipError_t launch_tile(int loader, const IgArgs& args, dim3 nwg, hipStream_t s) {
   switch (loader) {
     case LOAD_GENERIC:
       hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_GENERIC, kStages<LOAD_GENERIC>>), dim3(nwg),
@@ -502,7 +554,7 @@ hipError_t launch_tile(int loader, const IgArgs& args, int nwg, hipStream_t s) {
 }
 
 template <int ESZ>
-hipError_t launch_esz(int tile, int loader, const IgArgs& args, int nwg, hipStream_t s) {
+hipError_t launch_esz(int tile, int loader, const IgArgs& args, dim3 nwg, hipStream_t s) {
   switch (tile) {
     case 0: return launch_tile<ESZ, 32, 256, 1, 4>(loader, args, nwg, s);
     case 1: return launch_tile<ESZ, 64, 128, 2, 2>(loader, args, nwg, s);
@@ -534,9 +586,23 @@ hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const 
   const TileCfg& t = kTiles[p->tile];
   args.nco_tiles = (p->g.cout + t.tco - 1) / t.tco;
   const int npx = (p->g.m + t.tpx - 1) / t.tpx;
-  const int nwg = npx * args.nco_tiles;
-  if (p->in_esz == 2) return launch_esz<2>(p->tile, p->loader, args, nwg, s);
-  return launch_esz<1>(p->tile, p->loader, args, nwg, s);
+  args.px_fastest = p->w_bytes > p->x_bytes;
+  args.ksplit = p->ksplit;
+  args.kt_per = p->kt_per;
+  args.ws = p->ws;
+  const dim3 grid(npx * args.nco_tiles, p->ksplit);
+  hipError_t err = p->in_esz == 2 ? launch_esz<2>(p->tile, p->loader, args, grid, s)
+                                  : launch_esz<1>(p->tile, p->loader, args, grid, s);
+  if (err != hipSuccess || p->ksplit == 1) return err;
+  const long quads = (long)p->g.m * (p->g.cout / 4);
+  const int blocks = (int)std::min<long>((quads + 255) / 256, 256L * 8);
+  if (p->in_esz == 2)
+    hipLaunchKernelGGL(splitk_reduce_kernel<2>, dim3(blocks), dim3(256), 0, s, p->ws, p->ksplit, p->g.m,
+                       p->g.cout, e, p->out_kind, y);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<1>, dim3(blocks), dim3(256), 0, s, p->ws, p->ksplit, p->g.m,
+                       p->g.cout, e, p->out_kind, y);
+  return hipGetLastError();
 }
 
 }  // namespace convnhwc

@@ -13,7 +13,8 @@ enum Path {
   PATH_IGEMM = 1,  // MFMA implicit GEMM (bf16 / int8), dense KxK and 1x1
   PATH_DW = 2,     // depthwise 3x3, VALU stencil
   PATH_F32 = 3,    // true-fp32 direct convolution, VALU
-  PATH_SMALLK = 4  // MFMA, operands straight from global memory: short K, odd Cin
+  PATH_SMALLK = 4, // MFMA, operands straight from global memory: short K, odd Cin
+  PATH_PATCH = 5   // MFMA 3x3 with the input halo patch staged in LDS
 };
 
 // How the implicit-GEMM kernel gathers its activation operand.
@@ -33,6 +34,7 @@ struct TileCfg {
 };
 
 constexpr int kNumTiles = 8;
+constexpr int kAlgoPatch = kNumTiles + 1;  // desc.algo value forcing PATH_PATCH
 extern const TileCfg kTiles[kNumTiles];  // index = algo - 1
 
 struct Geometry {
@@ -54,6 +56,11 @@ struct conv_plan {
   int out_kind; // convnhwc::OutKind
   int in_esz, out_esz;
   int64_t x_bytes, w_bytes, y_bytes, b_bytes;
+  int ksplit;       // PATH_IGEMM: K-splits (1 = none)
+  int kt_per;       // K-tiles per split
+  void* ws;         // split-K partial sums [ksplit][m][cout] (fp32/int32), device
+  int64_t ws_bytes;
+  int ws_device;    // device the workspace lives on
 };
 
 namespace convnhwc {
@@ -63,6 +70,10 @@ hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const 
 hipError_t launch_smallk(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                          hipStream_t s);
 void smallk_shape(const Geometry& g, int esz, int* fco, int* ks);
+hipError_t launch_patch(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
+                        hipStream_t s);
+bool patch_eligible(const Geometry& g, int esz, int groups);
+int patch_cb(const Geometry& g, int esz);
 hipError_t launch_dw(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                      hipStream_t s);
 hipError_t launch_f32(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,

@@ -136,6 +136,80 @@ def test_zero_bias_pointer():
     H.check_float(y.cpu().float().numpy(), r, a, "bf16", "null bias")
 
 
+# 3x3 layers through the halo-patch kernel (forced with algo 9): strides 1 and
+# 2, 64- and 128-byte channel blocks, several blocks, ragged edges and Cout.
+PATCH = [
+    L("patch_bf16_s1_c64", 2, 35, 37, 64, 72, 3, 3, (1, 1), (1, 1)),
+    L("patch_bf16_s1_c32", 1, 33, 18, 32, 64, 3, 3, (1, 1), (1, 1), act="relu"),
+    L("patch_bf16_s1_c256", 1, 20, 21, 256, 130, 3, 3, (1, 1), (1, 1), act="relu6"),
+    L("patch_bf16_s2_c32", 1, 41, 39, 32, 64, 3, 3, (2, 2), (1, 1)),
+    L("patch_bf16_s2_c128", 2, 17, 35, 128, 64, 3, 3, (2, 2), (1, 1), act="none"),
+    L("patch_bf16_s1_pad0", 1, 19, 20, 64, 16, 3, 3, (1, 1), (0, 0)),
+    L("patch_i8_s1_c128", 1, 34, 33, 128, 64, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="mish"),
+    L("patch_i8_s1_c64_i32", 2, 17, 19, 64, 72, 3, 3, (1, 1), (1, 1), dtype="i8", out="i32", act="none"),
+    L("patch_i8_s2_c256", 1, 23, 40, 256, 64, 3, 3, (2, 2), (1, 1), dtype="i8", out="i8", act="relu"),
+]
+
+
+@pytest.mark.parametrize("layer", PATCH, ids=[l.name for l in PATCH])
+def test_patch3x3(layer):
+    t = random_layer_tensors(layer, LAW[layer.dtype], seed=20)
+    ref = H.oracle_full(layer, t["x"], t)
+    y, conv = H.gpu_run(layer, t["x"], t, algo=9)
+    desc = conv.describe()
+    assert desc.startswith("patch3x3"), desc
+    what = "%s [%s]" % (layer.name, desc)
+    if layer.dtype == "i8":
+        H.check_int(y.cpu().numpy(), ref, layer, what)
+    else:
+        H.check_float(y.cpu().float().numpy(), ref[0], ref[1], layer.dtype, what)
+
+
+# Few output tiles, long reduction: the plan splits K over workgroups and a
+# second kernel sums the partials in split order.
+SPLITK = [
+    L("splitk_bf16_mish", 1, 20, 20, 512, 1024, 3, 3, (2, 2), (1, 1)),
+    L("splitk_bf16_1x1", 1, 12, 12, 2048, 96, 1, 1, act="relu"),
+    L("splitk_i8_i8", 2, 10, 10, 256, 72, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="relu6"),
+    L("splitk_i8_i32", 1, 9, 9, 512, 64, 3, 3, (1, 1), (1, 1), dtype="i8", out="i32", act="relu"),
+    L("splitk_i8_mish_vec", 1, 11, 13, 96, 40, 5, 5, (1, 1), (2, 2), dtype="i8", out="i8", act="mish"),
+]
+
+
+@pytest.mark.parametrize("layer", SPLITK, ids=[l.name for l in SPLITK])
+def test_split_k(layer):
+    t = random_layer_tensors(layer, LAW[layer.dtype], seed=19)
+    ref = H.oracle_full(layer, t["x"], t)
+    conv = _lib.Conv2d.from_layer(layer)
+    desc = conv.describe()
+    assert "ksplit=1 " not in desc, desc
+    x, w, b = t["x"].cuda(), t["w"].cuda(), H.bias_arg(layer, t)
+    ys = []
+    for _ in range(2):
+        y = conv.empty_output()
+        y.fill_(float("nan") if y.dtype.is_floating_point else -77)
+        conv.run(x, w, b, y)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0].view(torch.uint8), ys[1].view(torch.uint8)), "split-K run-to-run difference"
+    what = "%s [%s]" % (layer.name, desc)
+    if layer.dtype == "i8":
+        H.check_int(ys[0].cpu().numpy(), ref, layer, what)
+    else:
+        H.check_float(ys[0].cpu().float().numpy(), ref[0], ref[1], layer.dtype, what)
+    # graph replays reuse the plan's workspace
+    g = torch.cuda.CUDAGraph()
+    yg = conv.empty_output()
+    with torch.cuda.graph(g):
+        conv.run(x, w, b, yg)
+    for _ in range(3):
+        yg.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg.view(torch.uint8), ys[0].view(torch.uint8)), "graph replay differs"
+
+
 # ------------------------------------------------------------------ mosaic
 
 @pytest.mark.parametrize("th,tw,c,c_pad,in_dt,out_dt", [
@@ -179,11 +253,13 @@ def _guarded_run(layer, t, algo=0):
 
 
 @pytest.mark.parametrize("layer", [DENSE[0], DENSE[5], DENSE[8], DENSE[14], DW[0], DW[3], F32[1], SMALLK[2],
-                                   SMALLK[6]],
+                                   SMALLK[6], PATCH[0], PATCH[3]],
                          ids=lambda l: l.name)
 def test_guard_bands_and_determinism(layer):
     t = random_layer_tensors(layer, LAW[layer.dtype], seed=16)
     algos = [0] + (list(range(1, NTILES + 1)) if layer.groups == 1 and layer.dtype != "f32" else [])
+    if layer.name.startswith("patch_"):
+        algos = [9]
     for algo in algos:
         y1 = _guarded_run(layer, t, algo).clone()
         y2 = _guarded_run(layer, t, algo)
