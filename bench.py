@@ -15,8 +15,13 @@ Prints ONE JSON line:
   cpu_baseline  the CPU oracle on the same stack (all host threads)
   layers        per-layer time and roofline fraction
 
+  secondary     per-layer rates of the depthwise probe (vs the HBM peak) and
+                of the N=16 YOLO sweep (vs the MFMA peak), measured after the
+                step, each launch on its own buffer set (Infinity-Cache cold)
+
 Options: --gpus N (only 1 is supported), --steps K, --warmup W,
 --workload NAME (another stack, for information), --no-cpu-baseline,
+--no-secondary,
 --calib-copy MIB (run only a plain device copy of known size, for the
 counter calibration of the traffic figure).
 """
@@ -46,6 +51,8 @@ def parse():
     ap.add_argument("--workload", default="yolo640_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the depthwise-probe and N=16-sweep measurements")
     return ap.parse_args()
 
 
@@ -248,6 +255,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl)
 
+    secondary = None if args.no_secondary else secondary_measurements()
+
     dt = wl.layers[0].dtype
     out = {
         "metric": METRIC,
@@ -271,10 +280,87 @@ def main():
         "cpu_baseline": cpu,
         "layers": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in L.items() if k != "desc"}
                    for L in layers],
+        "secondary": secondary,
         "wall_s_timed": round(wall, 4),
         "gpu": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)
+
+
+def secondary_measurements():
+    """Per-layer rates of the depthwise probe (against the HBM peak) and of the
+    N=16 YOLO sweep (against the MFMA peak), outside the step's timed region.
+    Inputs are seeded device tensors of each layer's shape and value law;
+    every launch reads a different buffer set, with the sets together larger
+    than 768 MB, so repeated launches cannot be served from the 256 MB
+    Infinity Cache."""
+    import torch
+
+    from convolution_conv2d_nhwc_amd import _lib
+    from convolution_conv2d_nhwc_amd.data import workload
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+
+    def draw(layer, shape, what):
+        if layer.dtype == "i8":
+            if what == "b":
+                return torch.randint(-16129, 16130, shape, generator=gen, device="cuda", dtype=torch.int32)
+            return torch.randint(-127, 128, shape, generator=gen, device="cuda", dtype=torch.int8)
+        if what == "b":
+            return (torch.rand(shape, generator=gen, device="cuda") * 0.2 - 0.1).float()
+        fan_in = (layer.cin // layer.groups) * layer.kh * layer.kw
+        sd = 0.5 if what == "x" else (2.0 / fan_in) ** 0.5
+        return (torch.randn(shape, generator=gen, device="cuda") * sd).to(torch.bfloat16)
+
+    out = {}
+    for name in ("dw_probe_bf16", "dw_probe_int8", "yolo_sweep_bf16", "yolo_sweep_int8"):
+        rows = []
+        tot_flop = tot_us = 0.0
+        for layer in workload(name).layers:
+            conv = _lib.Conv2d.from_layer(layer)
+            w = draw(layer, (layer.cout, layer.kh, layer.kw, layer.cin // layer.groups), "w")
+            b = draw(layer, (layer.cout,), "b")
+            if layer.dtype == "i8":
+                s_ = torch.rand(layer.cout, generator=gen, device="cuda") * 0.009 + 0.001
+                b = _lib.pack_bias_scale(b, s_)
+            xy_bytes = layer.bytes()
+            nsets = max(2, min(32, -(-768 * 2 ** 20 // xy_bytes)))
+            xs = [draw(layer, (layer.n, layer.h, layer.w, layer.cin), "x") for _ in range(nsets)]
+            ys = [conv.empty_output() for _ in range(nsets)]
+            for i in range(nsets):
+                conv.run(xs[i], w, b, ys[i])
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(nsets):
+                    conv.run(xs[i], w, b, ys[i])
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 5
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0 / (reps * nsets)
+            fl, by = layer.flops(), layer.bytes()
+            peak = PEAK[layer.dtype]
+            t_roof = max(fl / (peak * 1e12), by / (HBM_GBS * 1e9))
+            rows.append({"layer": layer.name, "kernel": conv.describe().split("kernel=")[-1], "us": round(us, 2),
+                         "tflops": round(fl / (us * 1e-6) / 1e12, 2), "gbs": round(by / (us * 1e-6) / 1e9, 1),
+                         "bound": "mfma" if fl / (peak * 1e12) >= by / (HBM_GBS * 1e9) else "hbm",
+                         "roof_frac": round(t_roof / (us * 1e-6), 4),
+                         "frac_mfma_peak": round(fl / (us * 1e-6) / 1e12 / peak, 4),
+                         "frac_hbm_peak": round(by / (us * 1e-6) / 1e9 / HBM_GBS, 4), "buffer_sets": nsets})
+            tot_flop += fl
+            tot_us += us
+            del xs, ys, g
+            torch.cuda.empty_cache()
+        out[name] = {"layers": rows, "total_us": round(tot_us, 2),
+                     "tflops": round(tot_flop / (tot_us * 1e-6) / 1e12, 2)}
+    return out
 
 
 def cpu_baseline(wl):

@@ -290,12 +290,15 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
                   kDt[p->d.out_dtype], p->g.m, p->g.k, p->in_esz, fco, ks);
   } else if (p->path == PATH_DW) {
     static const char* kT[] = {"", "signed char", "unsigned short", "", "float"};
-    const bool vec = p->loader == LOAD_VEC;
-    const int ve = vec ? 16 / p->in_esz : 1;
-    const int pw = (p->in_esz == 1 && vec) ? 2 : 4;
-    std::snprintf(buf, len, "dw3x3 dtype=%s out=%s loader=%s stride=%dx%d kernel=dw3x3_kernel<%s, %d, %d>",
-                  kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], p->g.sh, p->g.sw, kT[p->in_esz], ve,
-                  pw);
+    int ve, pw, th = 0;
+    dw_shape(p, &ve, &pw, &th);
+    if (th)
+      std::snprintf(buf, len, "dw3x3 dtype=%s out=%s stride=%dx%d rows kernel=dw3x3_rows_kernel<%s, %d, %d, %d>",
+                    kDt[p->d.dtype], kDt[p->d.out_dtype], p->g.sh, p->g.sw, kT[p->in_esz], ve, pw, th);
+    else
+      std::snprintf(buf, len, "dw3x3 dtype=%s out=%s loader=%s stride=%dx%d kernel=dw3x3_kernel<%s, %d, %d>",
+                    kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], p->g.sh, p->g.sw, kT[p->in_esz], ve,
+                    pw);
   } else {
     std::snprintf(buf, len, "direct_f32 m=%d k=%d kernel=conv_f32_kernel", p->g.m, p->g.k);
   }

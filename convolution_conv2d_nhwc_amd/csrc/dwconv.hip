@@ -34,6 +34,7 @@ struct DwArgs {
   int cv;      // channel vectors per pixel
   int wgrp;    // pixel groups per output row
   long total;  // threads doing work
+  int x_bytes;
 };
 
 // Element loads/stores for the three input types, widened to the
@@ -230,6 +231,220 @@ __global__ __launch_bounds__(256) void dw3x3_kernel(DwArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Stride-1 kernel with a sliding row window. A lane owns VE channels of PW
+// adjacent output columns and walks TH output rows down the image: the three
+// input rows it needs sit in registers already widened to the accumulator
+// type, each new input row is loaded (PW+2 vectors) and widened once, and the
+// next row's loads are in flight during the current row's multiply-adds, so
+// memory latency overlaps arithmetic. The lane shapes
+// (channels, columns, rows) were chosen by timing the depthwise probe on
+// MI355X: bf16 4x2x8, int8 4x4x4, fp32 4x2x8. Loads are buffer loads: rows and
+// columns outside the image read zero (the zero padding). Weights are widened
+// once per lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dw_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
+constexpr uint32_t kDwOOB = 0x80000000u;
+
+// raw vector of VE elements of T
+template <typename T, int VE>
+struct RawVec {
+  static constexpr int kBytes = VE * (int)sizeof(T);
+  static constexpr int kWords = kBytes / 4;
+  uint32_t w[kWords];
+};
+
+template <typename T, int VE>
+__device__ __forceinline__ RawVec<T, VE> load_raw(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  RawVec<T, VE> v;
+  if constexpr (RawVec<T, VE>::kBytes == 16) {
+    const i32x4 q = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    v.w[0] = q[0];
+    v.w[1] = q[1];
+    v.w[2] = q[2];
+    v.w[3] = q[3];
+  } else if constexpr (RawVec<T, VE>::kBytes == 4) {
+    v.w[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+  } else {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    const i32x2 q = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    v.w[0] = q[0];
+    v.w[1] = q[1];
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ typename Elt<T>::acc_t widen_word(uint32_t wd, int e) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(float, wd);
+  } else if constexpr (sizeof(T) == 2) {
+    return bf16_bits_to_f32((e & 1) ? (wd >> 16) : (wd & 0xffffu));
+  } else {
+    return (int)(int8_t)(wd >> (8 * (e & 3)));
+  }
+}
+
+template <typename T, int VE, int PW, int TH>
+__global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
+  typedef typename Elt<T>::acc_t acc_t;
+  constexpr int ESZ = sizeof(T);
+  constexpr int PER = 4 / ESZ;  // elements per 32-bit word
+  constexpr int NC = PW + 2;    // input columns per row
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.total) return;
+  const Geometry& g = a.g;
+  const int cvi = (int)(t % a.cv);
+  long r = t / a.cv;
+  const int wgi = (int)(r % a.wgrp);
+  r /= a.wgrp;
+  const int nhb = (g.ho + TH - 1) / TH;
+  const int hb = (int)(r % nhb);
+  const int n = (int)(r / nhb);
+  const int c0 = cvi * VE;
+  const int wo0 = wgi * PW;
+  const int ho0 = hb * TH;
+  const __amdgpu_buffer_rsrc_t rx = dw_rsrc(a.x, a.x_bytes);
+
+  acc_t wr[VE][9];
+#pragma unroll
+  for (int e = 0; e < VE; ++e)
+#pragma unroll
+    for (int q = 0; q < 9; ++q) wr[e][q] = Elt<T>::get1(a.w + ((size_t)(c0 + e) * 9 + q) * ESZ);
+
+  // byte offsets of this lane's input columns within one input row
+  const int rowbytes = g.w * g.c * ESZ;
+  uint32_t coff[NC];
+  bool cok[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int wi = wo0 - g.pw + j;
+    cok[j] = (unsigned)wi < (unsigned)g.w;
+    coff[j] = (uint32_t)((wi * g.c + c0) * ESZ);
+  }
+  auto fetch_row = [&](int hi, RawVec<T, VE> (&raw)[NC]) {
+    const bool rok = (unsigned)hi < (unsigned)g.h;
+    const uint32_t rbase = (uint32_t)((n * g.h + hi) * rowbytes);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) raw[j] = load_raw<T, VE>(rx, (rok && cok[j]) ? rbase + coff[j] : kDwOOB);
+  };
+  auto widen_row = [&](const RawVec<T, VE> (&raw)[NC], acc_t (&row)[NC][VE]) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) row[j][e] = widen_word<T>(raw[j].w[e / PER], e);
+  };
+
+  acc_t rows[3][NC][VE];
+  RawVec<T, VE> nxt[NC];
+  {
+    const int hi0 = ho0 - g.ph;
+    fetch_row(hi0, nxt);
+    widen_row(nxt, rows[0]);
+    fetch_row(hi0 + 1, nxt);
+    widen_row(nxt, rows[1]);
+    fetch_row(hi0 + 2, nxt);
+  }
+
+  float bsf[VE];
+  int bsi[VE];
+  float scl[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) {
+    if constexpr (ESZ == 1) {
+      bsi[e] = a.e.ibias ? a.e.ibias[c0 + e] : 0;
+      scl[e] = a.e.scale ? a.e.scale[c0 + e] : 0.f;
+    } else {
+      bsf[e] = a.e.bias ? a.e.bias[c0 + e] : 0.f;
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < TH; ++i) {
+    const int ho = ho0 + i;
+    if (ho >= g.ho) break;
+    // the row loaded last becomes window row (i + 2) % 3, then the next
+    // row's loads go out before this row's multiply-adds
+    widen_row(nxt, rows[(i + 2) % 3]);
+    if (i + 1 < TH) fetch_row(ho - g.ph + 3, nxt);
+    acc_t acc[PW][VE];
+#pragma unroll
+    for (int p = 0; p < PW; ++p)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[p][e] = 0;
+#pragma unroll
+    for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+      for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+        for (int p = 0; p < PW; ++p)
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[p][e] += rows[(i + kh) % 3][p + kw][e] * wr[e][kh * 3 + kw];
+    // fused epilogue, VE channels of PW pixels
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      const int wo = wo0 + p;
+      if (wo >= g.wo) break;
+      const size_t off = ((size_t)(n * g.ho + ho) * g.wo + wo) * g.cout + c0;
+      if constexpr (ESZ == 1) {
+        if (a.out_kind == OUT_I32) {
+          int32_t* yp = reinterpret_cast<int32_t*>(a.y) + off;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) {
+            int v = acc[p][e] + bsi[e];
+            if (a.e.act == ACT_RELU) v = v > 0 ? v : 0;
+            yp[e] = v;
+          }
+        } else {
+          uint32_t wd[VE / 4];
+#pragma unroll
+          for (int q = 0; q < VE / 4; ++q) wd[q] = 0;
+#pragma unroll
+          for (int e = 0; e < VE; ++e)
+            wd[e >> 2] |= ((uint32_t)requant_i8(acc[p][e] + bsi[e], scl[e], a.e.act) & 0xffu) << (8 * (e & 3));
+          if constexpr (VE == 4)
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(a.y) + off) = wd[0];
+          else if constexpr (VE == 8)
+            *reinterpret_cast<uint2*>(reinterpret_cast<int8_t*>(a.y) + off) = uint2{wd[0], wd[1]};
+          else
+            *reinterpret_cast<i32x4*>(reinterpret_cast<int8_t*>(a.y) + off) =
+                i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+        }
+      } else {
+        float v[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) v[e] = apply_act(acc[p][e] + bsf[e], a.e.act);
+        if constexpr (ESZ == 4) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.y) + off) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+          uint32_t wd[VE / 2];
+#pragma unroll
+          for (int q = 0; q < VE / 2; ++q)
+            wd[q] = (uint32_t)f32_to_bf16_bits(v[2 * q]) | ((uint32_t)f32_to_bf16_bits(v[2 * q + 1]) << 16);
+          uint16_t* yp = reinterpret_cast<uint16_t*>(a.y) + off;
+          if constexpr (VE == 8)
+            *reinterpret_cast<i32x4*>(yp) = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+          else
+            *reinterpret_cast<uint2*>(yp) = uint2{wd[0], wd[1]};
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int VE, int PW, int TH>
+hipError_t launch_rows_t(const DwArgs& base, hipStream_t s) {
+  DwArgs a = base;
+  a.cv = a.g.c / VE;
+  a.wgrp = (a.g.wo + PW - 1) / PW;
+  a.total = (long)a.g.n * ((a.g.ho + TH - 1) / TH) * a.wgrp * a.cv;
+  const long blocks = (a.total + 255) / 256;
+  hipLaunchKernelGGL((dw3x3_rows_kernel<T, VE, PW, TH>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int VE, int PW>
 hipError_t launch_dw_t(const DwArgs& base, hipStream_t s) {
   DwArgs a = base;
@@ -243,6 +458,22 @@ hipError_t launch_dw_t(const DwArgs& base, hipStream_t s) {
 
 }  // namespace
 
+// Lane shape of a depthwise plan: th > 0 selects the sliding-window kernel.
+void dw_shape(const conv_plan* p, int* ve, int* pw, int* th) {
+  const int c = p->g.c;
+  const bool s1 = p->g.sh == 1 && p->g.sw == 1;
+  const bool vec = p->loader == LOAD_VEC;
+  *th = 0;
+  if (s1 && c % 4 == 0) {
+    *ve = 4;
+    *pw = p->in_esz == 1 ? 4 : 2;
+    *th = p->in_esz == 1 ? 4 : 8;
+    return;
+  }
+  *ve = vec ? 16 / p->in_esz : 1;
+  *pw = (p->in_esz == 1 && vec) ? 2 : 4;
+}
+
 hipError_t launch_dw(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                      hipStream_t s) {
   DwArgs a;
@@ -252,7 +483,17 @@ hipError_t launch_dw(const conv_plan* p, const void* x, const void* w, const Epi
   a.e = e;
   a.g = p->g;
   a.out_kind = p->out_kind;
-  const bool vec = p->loader == LOAD_VEC;
+  a.x_bytes = (int)p->x_bytes;
+  int ve, pw, th;
+  dw_shape(p, &ve, &pw, &th);
+  if (th) {
+    switch (p->in_esz) {
+      case 4: return launch_rows_t<float, 4, 2, 8>(a, s);
+      case 2: return launch_rows_t<uint16_t, 4, 2, 8>(a, s);
+      default: return launch_rows_t<int8_t, 4, 4, 4>(a, s);
+    }
+  }
+  const bool vec = ve > 1;
   switch (p->in_esz) {
     case 4: return vec ? launch_dw_t<float, 4, 4>(a, s) : launch_dw_t<float, 1, 4>(a, s);
     case 2: return vec ? launch_dw_t<uint16_t, 8, 4>(a, s) : launch_dw_t<uint16_t, 1, 4>(a, s);

@@ -74,6 +74,7 @@ hipError_t launch_patch(const conv_plan* p, const void* x, const void* w, const 
                         hipStream_t s);
 bool patch_eligible(const Geometry& g, int esz, int groups);
 int patch_cb(const Geometry& g, int esz);
+void dw_shape(const conv_plan* p, int* ve, int* pw, int* th);
 hipError_t launch_dw(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                      hipStream_t s);
 hipError_t launch_f32(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,

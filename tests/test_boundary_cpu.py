@@ -97,7 +97,9 @@ def test_prepare_null():
     (dict(c_in=16, c_out=16, dtype="i8", out_dtype="i32"), "out=i32 loader=vec16"),
     (dict(c_in=64, c_out=64, groups=64, dtype="i8"), "dw3x3 dtype=i8"),
     (dict(c_in=1, c_out=8, dtype="f32"), "direct_f32"),
-    (dict(c_in=4, c_out=4, groups=4, dtype="f32"), "dw3x3 dtype=f32 out=f32 loader=vec16"),
+    (dict(c_in=4, c_out=4, groups=4, dtype="f32"), "dw3x3 dtype=f32 out=f32 stride=1x1 rows"),
+    (dict(c_in=4, c_out=4, groups=4, dtype="f32", stride=(2, 2)), "dw3x3 dtype=f32 out=f32 loader=vec16"),
+    (dict(c_in=6, c_out=6, groups=6, dtype="bf16"), "dw3x3 dtype=bf16 out=bf16 loader=generic"),
 ])
 def test_path_selection(layer, expect):
     args = dict(n=1, h=16, w=16, kh=3, kw=3, stride=(1, 1), pad=(1, 1), groups=1, act="relu")
