@@ -195,6 +195,10 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
   }
   p->path = path;
   p->tile = path == PATH_IGEMM ? (d->algo ? d->algo - 1 : choose_tile(g, in_esz)) : 0;
+  if (path == PATH_IGEMM && loader == LOAD_GENERIC && (kTiles[p->tile].tco > 256 || kTiles[p->tile].tpx > 256)) {
+    delete p;  // the element-wise gather needs a thread per tile row
+    return CONV_E_UNSUPPORTED;
+  }
   p->ksplit = 1;
   p->kt_per = (int)((g.k * (int64_t)in_esz + 127) / 128);
   if (path == PATH_IGEMM) plan_split_k(p);

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace convnhwc {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -56,6 +58,23 @@ __device__ __forceinline__ int requant_i8(int r, float s, int act) {
   const float q = fminf(fmaxf(__builtin_rintf(m), -127.0f), 127.0f);
   return (int)q;
 }
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = I .. N-1.
+// Unlike `#pragma unroll` it does not depend on the unroller's size limit, so
+// register arrays indexed by i stay in registers however long the body is.
+template <int I, int N>
+struct StaticFor {
+  template <class F>
+  __device__ __forceinline__ static void run(F&& f) {
+    f(std::integral_constant<int, I>{});
+    StaticFor<I + 1, N>::run(f);
+  }
+};
+template <int N>
+struct StaticFor<N, N> {
+  template <class F>
+  __device__ __forceinline__ static void run(F&&) {}
+};
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
   __bf16 h = (__bf16)v;  // v_cvt_pk_bf16_f32: round to nearest even

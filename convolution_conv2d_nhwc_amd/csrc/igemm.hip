@@ -50,6 +50,8 @@ const TileCfg kTiles[kNumTiles] = {
     {64, 64, 2, 2},    // 6: few pixels
     {256, 128, 2, 2},  // 7
     {128, 256, 2, 2},  // 8
+    {256, 256, 2, 2},  // 9: 128x128 per wave, long reductions
+    {128, 512, 1, 4},  // 10: 128x128 per wave, Cout = 128
 };
 
 namespace {
@@ -138,8 +140,15 @@ __device__ __forceinline__ int lds_off(int r, int c) { return r * kBKB + ((c ^ (
 
 // ---------------------------------------------------------------- kernel
 
+// The waves-per-SIMD hint lets the register allocator keep the accumulators
+// of the unrolled two-stage loop in place; with the default target it copies
+// them between AGPR ranges on every iteration.
+#ifndef IGEMM_WPE
+#define IGEMM_WPE 2
+#endif
+
 template <int ESZ, int TCO, int TPX, int WCO, int WPX, int LOADER, int D>
-__global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))) void igemm_kernel(IgArgs a) {
   constexpr int VE = 16 / ESZ;      // elements per 16-byte chunk
   constexpr int BKE = kBKB / ESZ;   // elements per K-tile row
   constexpr int FCO = TCO / WCO / 16;
@@ -491,17 +500,17 @@ __global__ __launch_bounds__(256) void igemm_kernel(IgArgs a) {
     }
     return;
   }
-#pragma unroll
-  for (int i = 0; i < FCO; ++i) {
+  StaticFor<0, FCO>::run([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
     const int co = co_w + 16 * i;
-    if (co >= g.cout) continue;
+    if (co >= g.cout) return;
     const QuadConsts q = load_quad_consts<ESZ>(a.e, co, g.cout);
-#pragma unroll
-    for (int j = 0; j < FPX; ++j) {
+    StaticFor<0, FPX>::run([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
       const int px = px_w + 16 * j;
       if (px < g.m) store_quad<ESZ>(acc[i][j], q, co, px, g.cout, a.out_kind, a.e.act, a.y);
-    }
-  }
+    });
+  });
 }
 
 // Sum of the K-split partials in split order (the same order on every run),
@@ -527,26 +536,30 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const void* ws, int 
 #ifndef IGEMM_STAGES
 #define IGEMM_STAGES 2
 #endif
-template <int LOADER>
-constexpr int kStages = LOADER == LOAD_GENERIC ? 1 : IGEMM_STAGES;
+template <int LOADER, int TCO, int TPX>
+constexpr int kStages = (LOADER == LOAD_GENERIC || TCO + TPX >= 512) ? 1 : IGEMM_STAGES;
 
 template <int ESZ, int TCO, int TPX, int WCO, int WPX>
 hipError_t launch_tile(int loader, const IgArgs& args, dim3 nwg, hipStream_t s) {
   switch (loader) {
     case LOAD_GENERIC:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_GENERIC, kStages<LOAD_GENERIC>>), dim3(nwg),
-                         dim3(256), 0, s, args);
+      // the element-wise gather maps at least one thread to each tile row
+      if constexpr (TCO <= 256 && TPX <= 256)
+        hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_GENERIC, kStages<LOAD_GENERIC, TCO, TPX>>),
+                           dim3(nwg), dim3(256), 0, s, args);
+      else
+        return hipErrorInvalidValue;  // refused by conv_prepare
       break;
     case LOAD_VEC:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_VEC, kStages<LOAD_VEC>>), dim3(nwg), dim3(256),
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_VEC, kStages<LOAD_VEC, TCO, TPX>>), dim3(nwg), dim3(256),
                          0, s, args);
       break;
     case LOAD_1X1:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_1X1, kStages<LOAD_1X1>>), dim3(nwg), dim3(256),
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_1X1, kStages<LOAD_1X1, TCO, TPX>>), dim3(nwg), dim3(256),
                          0, s, args);
       break;
     default:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_TAP, kStages<LOAD_TAP>>), dim3(nwg), dim3(256),
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_TAP, kStages<LOAD_TAP, TCO, TPX>>), dim3(nwg), dim3(256),
                          0, s, args);
       break;
   }
@@ -563,7 +576,9 @@ hipError_t launch_esz(int tile, int loader, const IgArgs& args, dim3 nwg, hipStr
     case 4: return launch_tile<ESZ, 128, 64, 2, 2>(loader, args, nwg, s);
     case 5: return launch_tile<ESZ, 64, 64, 2, 2>(loader, args, nwg, s);
     case 6: return launch_tile<ESZ, 256, 128, 2, 2>(loader, args, nwg, s);
-    default: return launch_tile<ESZ, 128, 256, 2, 2>(loader, args, nwg, s);
+    case 7: return launch_tile<ESZ, 128, 256, 2, 2>(loader, args, nwg, s);
+    case 8: return launch_tile<ESZ, 256, 256, 2, 2>(loader, args, nwg, s);
+    default: return launch_tile<ESZ, 128, 512, 1, 4>(loader, args, nwg, s);
   }
 }
 

@@ -33,7 +33,7 @@ struct TileCfg {
   int tco, tpx, wco, wpx;
 };
 
-constexpr int kNumTiles = 8;
+constexpr int kNumTiles = 10;
 constexpr int kAlgoPatch = kNumTiles + 1;  // desc.algo value forcing PATH_PATCH
 extern const TileCfg kTiles[kNumTiles];  // index = algo - 1
 

@@ -3,6 +3,7 @@ by element on the same seeded inputs (small shapes that span several tiles
 with ragged tails, every tile configuration of the MFMA kernel forced in
 turn), plus the hygiene checks: canary-filled outputs, guard bands,
 determinism, a non-default stream and HIP-graph replay."""
+import re
 from dataclasses import replace
 
 import numpy as np
@@ -16,7 +17,34 @@ from tests import helpers as H
 
 pytestmark = pytest.mark.gpu
 
-NTILES = 8
+NTILES = _lib.lib().conv_algo_count() - 1  # the last algo forces the patch kernel
+ALGO_PATCH = NTILES + 1
+
+
+# Tiles wider than 256 rows on either side need a 16-byte-vector loader; the
+# element-wise gather refuses them at prepare time.
+def _tile_dims(algo):
+    d = _lib.Conv2d(1, 20, 20, 64, 64, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=algo).describe()
+    co, px = re.search(r"co(\d+)xpx(\d+)", d).groups()
+    return int(co), int(px)
+
+
+BIG_TILES = {a for a in range(1, NTILES + 1) if max(_tile_dims(a)) > 256}
+
+
+def forced_tiles(layer):
+    """Every forced tile the layer accepts; only the generic loader may refuse,
+    and only the tiles wider than 256."""
+    out = []
+    for a in range(1, NTILES + 1):
+        try:
+            _lib.Conv2d.from_layer(layer, algo=a).close()
+            out.append(a)
+        except _lib.ConvError as e:
+            assert a in BIG_TILES and "CONV_E_UNSUPPORTED" in str(e), (layer.name, a, str(e))
+            d = _lib.Conv2d.from_layer(layer).describe()
+            assert "loader=generic" in d or "smallk" in d, (layer.name, a, d)
+    return out
 
 
 def L(name, n, h, w, cin, cout, kh, kw, s=(1, 1), p=(0, 0), groups=1, dtype="bf16", out=None, act="mish"):
@@ -80,7 +108,7 @@ def test_dense_all_tiles(layer):
     t = random_layer_tensors(layer, LAW[layer.dtype], seed=11)
     ref = H.oracle_full(layer, t["x"], t)
     xg = t["x"].cuda()
-    for algo in [0] + list(range(1, NTILES + 1)):
+    for algo in [0] + forced_tiles(layer):
         y, conv = H.gpu_run(layer, xg, t, algo=algo)
         what = "%s algo=%d [%s]" % (layer.name, algo, conv.describe())
         yc = y.cpu()
@@ -155,7 +183,7 @@ PATCH = [
 def test_patch3x3(layer):
     t = random_layer_tensors(layer, LAW[layer.dtype], seed=20)
     ref = H.oracle_full(layer, t["x"], t)
-    y, conv = H.gpu_run(layer, t["x"], t, algo=9)
+    y, conv = H.gpu_run(layer, t["x"], t, algo=ALGO_PATCH)
     desc = conv.describe()
     assert desc.startswith("patch3x3"), desc
     what = "%s [%s]" % (layer.name, desc)
@@ -257,9 +285,9 @@ def _guarded_run(layer, t, algo=0):
                          ids=lambda l: l.name)
 def test_guard_bands_and_determinism(layer):
     t = random_layer_tensors(layer, LAW[layer.dtype], seed=16)
-    algos = [0] + (list(range(1, NTILES + 1)) if layer.groups == 1 and layer.dtype != "f32" else [])
+    algos = [0] + (forced_tiles(layer) if layer.groups == 1 and layer.dtype != "f32" else [])
     if layer.name.startswith("patch_"):
-        algos = [9]
+        algos = [ALGO_PATCH]
     for algo in algos:
         y1 = _guarded_run(layer, t, algo).clone()
         y2 = _guarded_run(layer, t, algo)
