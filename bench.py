@@ -173,36 +173,36 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # ---- per-kernel durations -------------------------------------------------
-    # Each layer (and the mosaic) is captured R times back to back into a graph
-    # of its own, on the stream its kernel runs on; HIP events around replays of
-    # that graph give the kernel's average launch duration without host launch
-    # gaps, which is what the profiler's per-dispatch durations measure.
-    R = 10
-    reps = max(5, min(args.steps // 10, 50))
-
-    def time_graph(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(R):
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1000.0 / (reps * R)
-
+    # ---- per-kernel durations, inside the stack ----------------------------------
+    # The step runs eagerly T more times with a timing event after every
+    # kernel. A spin kernel first holds the stream while the host enqueues all
+    # of it, so the kernels run back to back as in the graph, each reading what
+    # the previous one just wrote, and the interval between consecutive events
+    # is one kernel's duration (plus the event's own sub-microsecond cost). The
+    # profiler's per-dispatch average of the same command covers these
+    # launches and the graph replays alike.
     ins = [canvas if canvas is not None else x0] + bufs[:-1]
-    dur_us = []
+    seq = []
     if canvas is not None:
-        dur_us.append(time_graph(lambda: _lib.mosaic_pack(x0, canvas, out_dtype=torch.bfloat16)))
-    for i in range(len(convs)):
-        dur_us.append(time_graph(lambda i=i: launch(i, ins[i])))
+        seq.append(lambda: _lib.mosaic_pack(x0, canvas, out_dtype=torch.bfloat16))
+    seq += [lambda i=i: launch(i, ins[i]) for i in range(len(convs))]
+    # An event between two kernels delays the second by a few microseconds;
+    # a pair of events with nothing between them measures that delay, which
+    # is taken off every interval.
+    T = 20
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 2)] for _ in range(T)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    for t in range(T):
+        evs[t][0].record()
+        evs[t][1].record()
+        for k, fn in enumerate(seq):
+            fn()
+            evs[t][k + 2].record()
+    torch.cuda.synchronize()
+    ev_gap_us = sum(evs[t][0].elapsed_time(evs[t][1]) for t in range(T)) * 1000.0 / T
+    dur_us = [sum(evs[t][k + 1].elapsed_time(evs[t][k + 2]) for t in range(T)) * 1000.0 / T - ev_gap_us
+              for k in range(len(seq))]
 
     layers = []
     j = 0
@@ -247,6 +247,7 @@ def main():
     roof["launches_per_step"] = n_launch
     roof["avg_launch_us"] = avg_us
     roof["algorithmic_per_launch"] = {"flop": fl, "bytes": by}
+    roof["event_gap_us"] = ev_gap_us
 
     total_flop = wl.flops()
     value = total_flop / (ms_per_step * 1e-3) / 1e12

@@ -58,9 +58,25 @@ int choose_tile(const Geometry& g, int esz) {
 // applies the epilogue. If the workspace cannot be allocated (no device, out
 // of memory) the plan runs unsplit, which is slower but the same arithmetic
 // up to the order of the fp32 additions.
+// The large-layer kernel for long reductions over 128-byte channel blocks,
+// when its tiles still cover most of the chip: 256x256 when that gives at
+// least 160 workgroups, else 256x128 (measured on MI355X against the 64- and
+// 128-wide tiles: faster from about 8 KiB of K per output on).
+int choose_xl(const Geometry& g, int esz, int loader) {
+  const long kbytes = (long)g.k * esz;
+  if (kbytes < 8192) return -1;
+  auto nwg = [&](int ti) {
+    const TileCfg& t = kXlTiles[ti];
+    return (long)(g.cout / t.tco) * ((g.m + t.tpx - 1) / t.tpx);
+  };
+  if (xl_eligible(g, esz, loader, 0) && nwg(0) >= 160) return 0;
+  if (xl_eligible(g, esz, loader, 1) && nwg(1) >= 160) return 1;
+  return -1;
+}
+
 void plan_split_k(conv_plan* p) {
   const Geometry& g = p->g;
-  const TileCfg& t = kTiles[p->tile];
+  const TileCfg& t = p->path == PATH_XL ? kXlTiles[p->tile] : kTiles[p->tile];
   const long nwg = (long)((g.cout + t.tco - 1) / t.tco) * ((g.m + t.tpx - 1) / t.tpx);
   const int nkt = p->kt_per;
   if (nwg >= 128 || nkt < 16 || (g.cout & 3)) return;
@@ -151,7 +167,7 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
     path = PATH_DW;
     loader = (d->c_in * in_esz) % 16 == 0 ? LOAD_VEC : LOAD_GENERIC;
   }
-  if (d->algo != 0 && (path != PATH_IGEMM || d->algo < 1 || d->algo > kAlgoPatch)) return CONV_E_UNSUPPORTED;
+  if (d->algo != 0 && (path != PATH_IGEMM || d->algo < 1 || d->algo > kAlgoLast)) return CONV_E_UNSUPPORTED;
   // A short reduction over an odd channel count (the 3-channel and 1-channel
   // stems) goes to the LDS-free small-K kernel unless a tile is forced.
   if (path == PATH_IGEMM && loader == LOAD_GENERIC && d->algo == 0 &&
@@ -193,15 +209,32 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
     *out = nullptr;
     return CONV_E_UNSUPPORTED;
   }
+  if (d->algo >= kAlgoXl) {
+    if (!xl_eligible(g, in_esz, loader, d->algo - kAlgoXl)) {
+      delete p;
+      return CONV_E_UNSUPPORTED;
+    }
+    path = PATH_XL;
+  }
+  if (path == PATH_IGEMM && d->algo == 0) {
+    const int xt = choose_xl(g, in_esz, loader);
+    if (xt >= 0) {
+      path = PATH_XL;
+      p->tile = xt;
+    }
+  }
   p->path = path;
-  p->tile = path == PATH_IGEMM ? (d->algo ? d->algo - 1 : choose_tile(g, in_esz)) : 0;
+  p->tile = path == PATH_IGEMM ? (d->algo ? d->algo - 1 : choose_tile(g, in_esz))
+            : path == PATH_XL && d->algo == 0 ? p->tile
+            : path == PATH_XL  ? d->algo - kAlgoXl
+                               : 0;
   if (path == PATH_IGEMM && loader == LOAD_GENERIC && (kTiles[p->tile].tco > 256 || kTiles[p->tile].tpx > 256)) {
     delete p;  // the element-wise gather needs a thread per tile row
     return CONV_E_UNSUPPORTED;
   }
   p->ksplit = 1;
   p->kt_per = (int)((g.k * (int64_t)in_esz + 127) / 128);
-  if (path == PATH_IGEMM) plan_split_k(p);
+  if (path == PATH_IGEMM || path == PATH_XL) plan_split_k(p);
   p->x_bytes = x_bytes;
   p->w_bytes = w_bytes;
   p->y_bytes = y_bytes;
@@ -240,6 +273,7 @@ conv_status conv_run(const conv_plan* p, const void* x, const void* w, const voi
     case PATH_DW: err = launch_dw(p, x, w, e, y, s); break;
     case PATH_SMALLK: err = launch_smallk(p, x, w, e, y, s); break;
     case PATH_PATCH: err = launch_patch(p, x, w, e, y, s); break;
+    case PATH_XL: err = launch_xl(p, x, w, e, y, s); break;
     default: err = launch_f32(p, x, w, e, y, s); break;
   }
   if (err != hipSuccess) {
@@ -279,9 +313,18 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
     const long nwg = (long)((p->g.cout + t.tco - 1) / t.tco) * ((p->g.m + t.tpx - 1) / t.tpx);
     std::snprintf(buf, len,
                   "igemm dtype=%s out=%s loader=%s tile=%d co%dxpx%d waves=%dx%d wgs=%ld m=%d k=%d "
-                  "ksplit=%d kernel=igemm_kernel<%d, %d, %d, %d, %d, %d>",
+                  "ksplit=%d kernel=igemm_kernel<%d, %d, %d, %d, %d, %d, %d>",
                   kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], p->tile + 1, t.tco, t.tpx, t.wco,
-                  t.wpx, nwg, p->g.m, p->g.k, p->ksplit, p->in_esz, t.tco, t.tpx, t.wco, t.wpx, p->loader);
+                  t.wpx, nwg, p->g.m, p->g.k, p->ksplit, p->in_esz, t.tco, t.tpx, t.wco, t.wpx, p->loader,
+                  igemm_stages(p->loader, p->tile));
+  } else if (p->path == PATH_XL) {
+    const TileCfg& t = kXlTiles[p->tile];
+    const long nwg = (long)(p->g.cout / t.tco) * ((p->g.m + t.tpx - 1) / t.tpx);
+    std::snprintf(buf, len,
+                  "igemm_xl dtype=%s out=%s loader=%s tile=%d co%dxpx%d waves=2x2 wgs=%ld m=%d k=%d ksplit=%d "
+                  "kernel=igemm_xl_kernel<%d, %d, %d, %d, %d>",
+                  kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], kAlgoXl + p->tile, t.tco, t.tpx, nwg,
+                  p->g.m, p->g.k, p->ksplit, p->in_esz, t.tco, t.tpx, p->loader, xl_sets(p->tile));
   } else if (p->path == PATH_PATCH) {
     const int s = p->g.sh, bh = s == 1 ? 16 : 8, cb = patch_cb(p->g, p->in_esz);
     std::snprintf(buf, len, "patch3x3 dtype=%s out=%s tile=%d stride=%d block=%dx16 cb=%d m=%d k=%d "
@@ -309,7 +352,7 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
   return CONV_OK;
 }
 
-int32_t conv_algo_count(void) { return kAlgoPatch; }
+int32_t conv_algo_count(void) { return kAlgoLast; }
 
 conv_status conv_mosaic_pack(const void* tiles, int32_t in_dtype, void* canvas, int32_t out_dtype, int32_t m,
                              int32_t th, int32_t tw, int32_t c, int32_t c_pad, void* stream) {

@@ -1,0 +1,430 @@
+// igemm_xl.hip -- implicit-GEMM convolution for large layers: 256-wide
+// workgroup tiles, a 128x128 (or 128x64 / 64x128) output block per wave, and
+// a software pipeline that keeps the matrix cores fed from one wave per SIMD.
+//
+// The GEMM view, operand layout, buffer loads and LDS swizzle are those of
+// igemm.hip; this kernel differs in how it spends LDS bandwidth and latency.
+//
+// LDS bandwidth. Every MFMA operand is read from LDS once per wave, so the
+// bytes read per MFMA fall as the wave's output block grows: a 128x128 block
+// reads (128 + 128) rows per K-step for 64 MFMAs, a quarter of what a 32x32
+// block needs per MFMA. With 2x2 waves of 128x128 a K-tile of 128 bytes costs
+// 128 KiB of LDS reads and 64 KiB of LDS writes per workgroup against 128
+// MFMAs (2048 cycles) per SIMD, i.e. about 1536 cycles of the CU's 128
+// bytes/cycle: the matrix cores, not the LDS, set the pace.
+//
+// Latency. With one wave per SIMD nothing hides a stall, so each K-tile is
+// split at its single barrier into two halves that never wait on their own
+// loads:
+//   half 1: read the K-step-1 operands of tile t from LDS; run the K-step-0
+//           MFMAs of tile t (operands read during the previous half 2);
+//           between them, write tile t+1 from registers into the other LDS
+//           buffer and issue the global loads of tile t+2 into the freed
+//           registers;
+//   barrier (tile t+1 is visible; nobody reads the buffer of tile t-1);
+//   half 2: read the K-step-0 operands of tile t+1; run the K-step-1 MFMAs of
+//           tile t.
+// Global loads get a whole K-tile (about 2000 cycles) to land, LDS reads a
+// half.
+//
+// Only the tap and 1x1 loaders (Cin * elem_size a multiple of 128 bytes) are
+// offered, and Cout must be a multiple of the channel tile, so every weight
+// row of a tile exists and a K-tile never straddles two taps.
+#include "igemm_common.h"
+
+namespace convnhwc {
+
+const TileCfg kXlTiles[kNumXlTiles] = {
+    {256, 256, 2, 2},  // 128x128 per wave
+    {256, 128, 2, 2},  // 128x64 per wave
+    {128, 256, 2, 2},  // 64x128 per wave (Cout = 128)
+};
+
+namespace {
+
+#ifndef XL_SETS
+#define XL_SETS 2
+#endif
+#ifndef XL_FETCH_MODE
+#define XL_FETCH_MODE 0
+#endif
+
+struct XlArgs {
+  const char* x;
+  const char* w;
+  void* y;
+  Epi e;
+  Geometry g;
+  int out_kind;
+  int nco_tiles;
+  int x_bytes;
+  int w_bytes;
+  int x_shift;     // LOAD_TAP: bytes the x descriptor starts before x
+  int px_fastest;  // tile order: pixel tiles vary fastest (weights > activations)
+  int ksplit;      // K-splits (gridDim.y); > 1 writes raw partial sums to ws
+  int kt_per;      // K-tiles per split
+  void* ws;        // [ksplit][m][cout] fp32 / int32 partial sums
+};
+
+// MFMA with the accumulator tied to one AGPR quad (the compiler's own MFMA
+// selection gives the result a different AGPR quad than the input and copies
+// it back every iteration, which costs more issue slots than the MFMAs).
+// Operands A/B come straight from LDS reads; the accumulator is only ever
+// touched by MFMAs of the same opcode between the two guards below, for which
+// the hardware interlocks back-to-back dependent issue.
+template <int ESZ>
+struct MfmaAgpr;
+template <>
+struct MfmaAgpr<2> {
+  static __device__ __forceinline__ void run(f32x4& c, const i32x4& a, const i32x4& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
+  }
+};
+template <>
+struct MfmaAgpr<1> {
+  static __device__ __forceinline__ void run(i32x4& c, const i32x4& a, const i32x4& b) {
+    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
+  }
+};
+
+// Wait states between a VALU write of an accumulator and its first MFMA, and
+// between its last MFMA and a VALU read of it. The guards are volatile, so
+// they keep their order relative to the MFMAs: every accumulator gets its own
+// guard plus the guards of all accumulators after it.
+template <typename T>
+__device__ __forceinline__ void agpr_guard(T& c) {
+  asm volatile("s_nop 4" : "+a"(c));
+}
+
+template <int ESZ, int TCO, int TPX, int LOADER, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void igemm_xl_kernel(XlArgs a) {
+  constexpr int FCO = TCO / 32;  // 16-row fragments per wave (2x2 waves)
+  constexpr int FPX = TPX / 32;
+  constexpr int ACH = TCO / 32;  // 16-byte chunks per thread per K-tile
+  constexpr int BCH = TPX / 32;
+  constexpr int NMF = FCO * FPX;  // MFMAs per K-step per wave
+  static_assert(LOADER == LOAD_TAP || LOADER == LOAD_1X1, "vector loaders only");
+  typedef typename Mfma<ESZ>::acc_t acc_t;
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * (TCO + TPX) * kBKB];
+  char* const As = smem;
+  char* const Bs = smem + 2 * TCO * kBKB;
+
+  const Geometry g = a.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wco = wave >> 1;
+  const int wpx = wave & 1;
+
+  // XCD-aware tile order, as in igemm.hip.
+  int lin = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
+  const int npx_tiles = nwg / a.nco_tiles;
+  const int co0 = (a.px_fastest ? lin / npx_tiles : lin % a.nco_tiles) * TCO;
+  const int px0 = (a.px_fastest ? lin % npx_tiles : lin / a.nco_tiles) * TPX;
+  const int hw_o = g.ho * g.wo;
+
+  // ---- loader state: chunk j of this thread is (row tid/8 + 32 j, column tid%8)
+  const int row0 = tid >> 3;
+  const int c16 = (tid & 7) * 16;
+  const int cbytes = g.c * ESZ;
+  const int kbytes = g.k * ESZ;
+  const int nkt_all = kbytes / kBKB;
+  const int kt0 = blockIdx.y * a.kt_per;
+  const int nkt = min(a.kt_per, nkt_all - kt0);
+  const __amdgpu_buffer_rsrc_t rw = rsrc(a.w, a.w_bytes);
+  const __amdgpu_buffer_rsrc_t rx =
+      LOADER == LOAD_TAP ? rsrc(a.x - a.x_shift, a.x_bytes + a.x_shift) : rsrc(a.x, a.x_bytes);
+  // weight rows co0 + row0 + 32 j all exist (Cout % TCO == 0); row j is
+  // 32 * kbytes further on, which enters the load as its scalar offset
+  const uint32_t voff_a = (uint32_t)((co0 + row0) * kbytes + c16);
+  const int astride = 32 * kbytes;
+  uint32_t voff_b[BCH];
+  uint32_t tmask[BCH];  // LOAD_TAP: bit t = tap t of the row lies in the image
+#pragma unroll
+  for (int j = 0; j < BCH; ++j) {
+    const int p = px0 + row0 + 32 * j;
+    voff_b[j] = kOOB;
+    tmask[j] = 0;
+    if (p < g.m) {
+      const int n = p / hw_o;
+      const int r = p - n * hw_o;
+      const int ho = r / g.wo;
+      const int wo = r - ho * g.wo;
+      if constexpr (LOADER == LOAD_1X1) {
+        voff_b[j] = (uint32_t)(p * cbytes + c16);
+        tmask[j] = 1;
+      } else {
+        const int hi0 = ho * g.sh - g.ph;
+        const int wi0 = wo * g.sw - g.pw;
+        voff_b[j] = (uint32_t)(((n * g.h + hi0) * g.w + wi0) * cbytes + a.x_shift + c16);
+        uint32_t m = 0;
+        for (int kh = 0, tap = 0; kh < g.kh; ++kh)
+          for (int kw = 0; kw < g.kw; ++kw, ++tap)
+            if ((unsigned)(hi0 + kh) < (unsigned)g.h && (unsigned)(wi0 + kw) < (unsigned)g.w) m |= 1u << tap;
+        tmask[j] = m;
+      }
+    }
+  }
+  // Uniform position (channel block, tap) of the next K-tile to fetch.
+  // LOAD_TAP walks the K-tiles channel block by channel block, all taps of a
+  // block in turn: the taps of one block re-read the same input rows shifted
+  // by a pixel or a row, so those reads hit in L2 instead of coming back a
+  // whole channel sweep later. K-tile kt is block kt / taps, tap kt % taps;
+  // the weight bytes of (tap, block) are contiguous in every OHWI row.
+  const int ntaps = g.kh * g.kw;
+  int t_kh = 0, t_kw = 0, t_cb = 0;
+  if constexpr (LOADER == LOAD_TAP) {
+    const int cb0 = kt0 / ntaps;
+    const int tap0 = kt0 - cb0 * ntaps;
+    t_cb = cb0 * kBKB;
+    t_kh = tap0 / g.kw;
+    t_kw = tap0 - t_kh * g.kw;
+  }
+
+  // Global loads of K-tile kt, one 16-byte chunk at a time (tiles are
+  // fetched in increasing order). fetch_begin takes the tile's uniform
+  // offsets and advances the tap position; a tile past the reduction reads
+  // zeros and costs no memory traffic.
+  struct Fetch {
+    bool live;
+    int soff_a;  // K byte offset of the tile in a weight row
+    int soff_b;  // tap offset + channel block (LOAD_TAP), kt * 128 (LOAD_1X1)
+    int tap;
+  };
+  auto fetch_begin = [&](int kt) {
+    Fetch f;
+    f.live = kt < nkt_all;
+    f.tap = 0;
+    if constexpr (LOADER == LOAD_TAP) {
+      f.tap = t_kh * g.kw + t_kw;
+      f.soff_a = f.tap * cbytes + t_cb;
+      f.soff_b = f.live ? (t_kh * g.w + t_kw) * cbytes + t_cb : 0;
+      if (++t_kw == g.kw) {
+        t_kw = 0;
+        if (++t_kh == g.kh) {
+          t_kh = 0;
+          t_cb += kBKB;
+        }
+      }
+    } else {
+      f.soff_a = kt * kBKB;
+      f.soff_b = f.live ? kt * kBKB : 0;
+    }
+    return f;
+  };
+  // chunk c < ACH: weight row row0 + 32 c; else pixel row row0 + 32 (c - ACH)
+  auto fetch_chunk = [&](const Fetch& f, auto cc, i32x4 (&ga)[ACH], i32x4 (&gb)[BCH]) {
+    constexpr int c = decltype(cc)::value;
+    if constexpr (c < ACH) {
+      ga[c] = bload16s(rw, f.live ? voff_a : kOOB, f.live ? f.soff_a + c * astride : 0);
+    } else {
+      constexpr int j = c - ACH;
+      bool ok = f.live;
+      if constexpr (LOADER == LOAD_TAP) ok = ok && ((tmask[j] >> (f.tap & 31)) & 1u);
+      gb[j] = bload16s(rx, ok ? voff_b[j] : kOOB, f.soff_b);
+    }
+  };
+  auto stash_chunk = [&](int buf, auto cc, const i32x4 (&ga)[ACH], const i32x4 (&gb)[BCH]) {
+    constexpr int c = decltype(cc)::value;
+    const int col = tid & 7;
+    if constexpr (c < ACH)
+      *reinterpret_cast<i32x4*>(As + buf * TCO * kBKB + lds_off(row0 + 32 * c, col)) = ga[c];
+    else
+      *reinterpret_cast<i32x4*>(Bs + buf * TPX * kBKB + lds_off(row0 + 32 * (c - ACH), col)) = gb[c - ACH];
+  };
+  auto fetch_all = [&](int kt, i32x4 (&ga)[ACH], i32x4 (&gb)[BCH]) {
+    const Fetch f = fetch_begin(kt);
+    StaticFor<0, ACH + BCH>::run([&](auto cc) { fetch_chunk(f, cc, ga, gb); });
+  };
+
+  // MFMA operand r of K-step s (0 or 1) of the tile in LDS buffer buf
+  // (r < FCO: weight fragment r, else pixel fragment r - FCO): row (lane & 15)
+  // of the 16-row fragment, chunk 4 s + lane / 16.
+  const int a_row0 = wco * (TCO / 2) + (lane & 15);
+  const int b_row0 = wpx * (TPX / 2) + (lane & 15);
+  auto read_frag = [&](int buf, int s, auto rc, i32x4 (&af)[FCO], i32x4 (&bf)[FPX]) {
+    constexpr int r = decltype(rc)::value;
+    const int c = 4 * s + (lane >> 4);
+    if constexpr (r < FCO)
+      af[r] = *reinterpret_cast<const i32x4*>(As + buf * TCO * kBKB + lds_off(a_row0 + 16 * r, c));
+    else
+      bf[r - FCO] = *reinterpret_cast<const i32x4*>(Bs + buf * TPX * kBKB + lds_off(b_row0 + 16 * (r - FCO), c));
+  };
+  auto read_all = [&](int buf, int s, i32x4 (&af)[FCO], i32x4 (&bf)[FPX]) {
+    StaticFor<0, FCO + FPX>::run([&](auto rc) { read_frag(buf, s, rc, af, bf); });
+  };
+
+  acc_t acc[FCO][FPX];
+#pragma unroll
+  for (int i = 0; i < FCO; ++i)
+#pragma unroll
+    for (int j = 0; j < FPX; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+
+  // The accumulators live in AGPRs and every MFMA updates its accumulator in
+  // place (see MfmaAgpr). The hazard guards order the AGPR zero-fill before
+  // the first MFMA and the last MFMA before the epilogue reads.
+  StaticFor<0, FCO>::run([&](auto ic) {
+    StaticFor<0, FPX>::run([&](auto jc) { agpr_guard(acc[decltype(ic)::value][decltype(jc)::value]); });
+  });
+  // MFMAs number B .. E-1 of a K-step, in (i, j) row-major order
+  auto mfma_range = [&](auto bc, auto ec, const i32x4 (&af)[FCO], const i32x4 (&bf)[FPX]) {
+    StaticFor<decltype(bc)::value, decltype(ec)::value>::run([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      MfmaAgpr<ESZ>::run(acc[k / FPX][k % FPX], af[k / FPX], bf[k % FPX]);
+    });
+  };
+  auto mfmas = [&](const i32x4 (&af)[FCO], const i32x4 (&bf)[FPX]) {
+    mfma_range(std::integral_constant<int, 0>{}, std::integral_constant<int, NMF>{}, af, bf);
+  };
+
+  // G register sets hold the next tiles in flight: set r holds tiles
+  // kt0 + 1 + r, kt0 + 1 + r + G, ... Tile t+1 leaves set t % G for LDS
+  // during step t, and the set is re-issued for tile t+1+G.
+  i32x4 ga[G][ACH], gb[G][BCH];
+  i32x4 a0[FCO], b0[FPX], a1[FCO], b1[FPX];
+  fetch_all(kt0, ga[0], gb[0]);
+  StaticFor<0, ACH + BCH>::run([&](auto cc) { stash_chunk(0, cc, ga[0], gb[0]); });
+#pragma unroll
+  for (int r = 0; r < G; ++r) fetch_all(kt0 + 1 + r, ga[r], gb[r]);
+  __syncthreads();
+  read_all(0, 0, a0, b0);
+
+  // One K-tile. Half 1 spreads, over the K-step-0 MFMAs, the K-step-1 operand
+  // reads, the LDS writes of tile t+1 and the global loads of tile t+1+G
+  // (chunk by chunk: the write frees the register the load refills). Half 2
+  // spreads the K-step-0 operand reads of tile t+1 over the K-step-1 MFMAs.
+  // The MFMA statements are ordered memory barriers for the compiler, so the
+  // interleaving is issued as written.
+  constexpr int CH = ACH + BCH;
+  constexpr int NR = FCO + FPX;
+  auto step = [&](int t, i32x4 (&sa)[ACH], i32x4 (&sb)[BCH]) {
+    const int buf = t & 1;
+    const Fetch f = fetch_begin(kt0 + t + 1 + G);
+    StaticFor<0, CH>::run([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      mfma_range(std::integral_constant<int, c * NMF / CH>{}, std::integral_constant<int, (c + 1) * NMF / CH>{}, a0,
+                 b0);
+      if constexpr (c < NR) read_frag(buf, 1, cc, a1, b1);
+      stash_chunk(buf ^ 1, cc, sa, sb);
+      if constexpr (XL_FETCH_MODE == 0 || (XL_FETCH_MODE == 1 && c < ACH)) fetch_chunk(f, cc, sa, sb);
+    });
+    StaticFor<CH, NR>::run([&](auto rc) { read_frag(buf, 1, rc, a1, b1); });
+    __syncthreads();
+    StaticFor<0, NR>::run([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      read_frag(buf ^ 1, 0, rc, a0, b0);
+      if constexpr (XL_FETCH_MODE == 1 && r < BCH) fetch_chunk(f, std::integral_constant<int, ACH + r>{}, sa, sb);
+      if constexpr (XL_FETCH_MODE == 2 && r < CH) fetch_chunk(f, rc, sa, sb);
+      mfma_range(std::integral_constant<int, r * NMF / NR>{}, std::integral_constant<int, (r + 1) * NMF / NR>{}, a1,
+                 b1);
+    });
+  };
+  // K-tiles 0 .. nkt-2 of this split: the next tile always exists
+  int t = 0;
+  for (; t + G < nkt; t += G) {
+#pragma unroll
+    for (int r = 0; r < G; ++r) step(t + r, ga[r], gb[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < G - 1; ++r)
+    if (t + 1 < nkt) {
+      step(t, ga[r], gb[r]);
+      ++t;
+    }
+  // last K-tile
+  read_all(t & 1, 1, a1, b1);
+  mfmas(a0, b0);
+  mfmas(a1, b1);
+  StaticFor<0, FCO>::run([&](auto ic) {
+    StaticFor<0, FPX>::run([&](auto jc) { agpr_guard(acc[decltype(ic)::value][decltype(jc)::value]); });
+  });
+
+  // ---- fused epilogue -------------------------------------------------
+  const int co_w = co0 + wco * (TCO / 2) + 4 * (lane >> 4);
+  const int px_w = px0 + wpx * (TPX / 2) + (lane & 15);
+  if (a.ksplit > 1) {
+    acc_t* ws = reinterpret_cast<acc_t*>(a.ws) + (size_t)blockIdx.y * g.m * (g.cout / 4);
+    StaticFor<0, FCO>::run([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int co = co_w + 16 * i;
+      StaticFor<0, FPX>::run([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        const int px = px_w + 16 * j;
+        if (px < g.m) ws[(size_t)px * (g.cout / 4) + co / 4] = acc[i][j];
+      });
+    });
+    return;
+  }
+  StaticFor<0, FCO>::run([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int co = co_w + 16 * i;
+    const QuadConsts q = load_quad_consts<ESZ>(a.e, co, g.cout);
+    StaticFor<0, FPX>::run([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int px = px_w + 16 * j;
+      if (px < g.m) store_quad<ESZ>(acc[i][j], q, co, px, g.cout, a.out_kind, a.e.act, a.y);
+    });
+  });
+}
+
+// Register sets of global prefetch: two where the registers allow it.
+template <int TCO, int TPX>
+constexpr int kXlSets = TCO + TPX > 384 ? 1 : XL_SETS;  // xl_sets() states the same rule
+
+template <int ESZ, int TCO, int TPX>
+hipError_t launch_cfg(int loader, const XlArgs& args, dim3 grid, hipStream_t s) {
+  if (loader == LOAD_TAP)
+    hipLaunchKernelGGL((igemm_xl_kernel<ESZ, TCO, TPX, LOAD_TAP, kXlSets<TCO, TPX>>), grid, dim3(256), 0, s, args);
+  else
+    hipLaunchKernelGGL((igemm_xl_kernel<ESZ, TCO, TPX, LOAD_1X1, kXlSets<TCO, TPX>>), grid, dim3(256), 0, s, args);
+  return hipGetLastError();
+}
+
+template <int ESZ>
+hipError_t launch_esz(int tile, int loader, const XlArgs& args, dim3 grid, hipStream_t s) {
+  switch (tile) {
+    case 0: return launch_cfg<ESZ, 256, 256>(loader, args, grid, s);
+    case 1: return launch_cfg<ESZ, 256, 128>(loader, args, grid, s);
+    default: return launch_cfg<ESZ, 128, 256>(loader, args, grid, s);
+  }
+}
+
+}  // namespace
+
+int xl_sets(int tile) { return kXlTiles[tile].tco + kXlTiles[tile].tpx > 384 ? 1 : XL_SETS; }
+
+bool xl_eligible(const Geometry& g, int esz, int loader, int tile) {
+  if (loader != LOAD_TAP && loader != LOAD_1X1) return false;
+  if (tile < 0 || tile >= kNumXlTiles) return false;
+  return g.cout % kXlTiles[tile].tco == 0 && (int64_t)g.k * esz % kBKB == 0;
+}
+
+hipError_t launch_xl(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s) {
+  XlArgs args;
+  args.x = static_cast<const char*>(x);
+  args.w = static_cast<const char*>(w);
+  args.y = y;
+  args.e = e;
+  args.g = p->g;
+  args.out_kind = p->out_kind;
+  args.x_bytes = (int)p->x_bytes;
+  args.w_bytes = (int)p->w_bytes;
+  args.x_shift = (p->g.ph * p->g.w + p->g.pw) * p->g.c * p->in_esz;
+  const TileCfg& t = kXlTiles[p->tile];
+  args.nco_tiles = p->g.cout / t.tco;
+  const int npx = (p->g.m + t.tpx - 1) / t.tpx;
+  args.px_fastest = p->w_bytes > p->x_bytes;
+  args.ksplit = p->ksplit;
+  args.kt_per = p->kt_per;
+  args.ws = p->ws;
+  const dim3 grid(npx * args.nco_tiles, p->ksplit);
+  hipError_t err = p->in_esz == 2 ? launch_esz<2>(p->tile, p->loader, args, grid, s)
+                                  : launch_esz<1>(p->tile, p->loader, args, grid, s);
+  if (err != hipSuccess || p->ksplit == 1) return err;
+  return launch_splitk_reduce(p, e, y, s);
+}
+
+}  // namespace convnhwc

@@ -14,7 +14,8 @@ enum Path {
   PATH_DW = 2,     // depthwise 3x3, VALU stencil
   PATH_F32 = 3,    // true-fp32 direct convolution, VALU
   PATH_SMALLK = 4, // MFMA, operands straight from global memory: short K, odd Cin
-  PATH_PATCH = 5   // MFMA 3x3 with the input halo patch staged in LDS
+  PATH_PATCH = 5,  // MFMA 3x3 with the input halo patch staged in LDS
+  PATH_XL = 6      // MFMA, 256-wide tiles, software-pipelined (large layers)
 };
 
 // How the implicit-GEMM kernel gathers its activation operand.
@@ -36,6 +37,13 @@ struct TileCfg {
 constexpr int kNumTiles = 10;
 constexpr int kAlgoPatch = kNumTiles + 1;  // desc.algo value forcing PATH_PATCH
 extern const TileCfg kTiles[kNumTiles];  // index = algo - 1
+
+// Tile configurations of the large-layer kernel; desc.algo kAlgoXl + i forces
+// configuration i.
+constexpr int kNumXlTiles = 3;
+constexpr int kAlgoXl = kAlgoPatch + 1;
+constexpr int kAlgoLast = kAlgoXl + kNumXlTiles - 1;
+extern const TileCfg kXlTiles[kNumXlTiles];
 
 struct Geometry {
   int n, h, w, c;        // input
@@ -67,6 +75,10 @@ namespace convnhwc {
 
 hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                         hipStream_t s);
+bool xl_eligible(const Geometry& g, int esz, int loader, int tile);
+int xl_sets(int tile);  // register sets of global prefetch of XL tile configuration `tile`
+int igemm_stages(int loader, int tile);  // register stages of the implicit-GEMM kernel
+hipError_t launch_xl(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);
 hipError_t launch_smallk(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                          hipStream_t s);
 void smallk_shape(const Geometry& g, int esz, int* fco, int* ks);

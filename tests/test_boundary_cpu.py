@@ -100,6 +100,11 @@ def test_prepare_null():
     (dict(c_in=4, c_out=4, groups=4, dtype="f32"), "dw3x3 dtype=f32 out=f32 stride=1x1 rows"),
     (dict(c_in=4, c_out=4, groups=4, dtype="f32", stride=(2, 2)), "dw3x3 dtype=f32 out=f32 loader=vec16"),
     (dict(c_in=6, c_out=6, groups=6, dtype="bf16"), "dw3x3 dtype=bf16 out=bf16 loader=generic"),
+    # long reductions over 128-byte channel blocks: the large-layer kernel
+    (dict(n=16, h=40, w=40, c_in=512, c_out=512, dtype="bf16"), "igemm_xl dtype=bf16 out=bf16 loader=tap tile=12"),
+    (dict(n=16, h=20, w=20, c_in=512, c_out=1024, dtype="bf16"), "igemm_xl dtype=bf16 out=bf16 loader=tap tile=13"),
+    (dict(n=16, h=40, w=40, c_in=512, c_out=512, dtype="i8"), "igemm dtype=i8"),
+    (dict(n=16, h=40, w=40, c_in=512, c_out=384, dtype="bf16"), "igemm dtype=bf16"),  # Cout % 256
 ])
 def test_path_selection(layer, expect):
     args = dict(n=1, h=16, w=16, kh=3, kw=3, stride=(1, 1), pad=(1, 1), groups=1, act="relu")
@@ -121,12 +126,26 @@ def test_out_shape_floor_rule_and_per_axis_pads():
 
 
 def test_forced_algo_and_count():
+    """Every algo id forces its own kernel configuration on a layer all of them
+    accept (3x3, 128-byte channel blocks, Cout = 256); the large-layer kernel
+    refuses a Cout that is not a multiple of its channel tile."""
     n = _lib.lib().conv_algo_count()
     assert n >= 1
+    kinds = set()
     for a in range(1, n + 1):
-        c = Conv2d(1, 20, 20, 64, 64, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=a)
-        assert "tile=%d " % a in c.describe()
+        c = Conv2d(1, 20, 20, 64, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=a)
+        d = c.describe()
+        assert "tile=%d " % a in d
+        kinds.add(d.split()[0])
         c.close()
+    assert kinds == {"igemm", "igemm_xl", "patch3x3"}
+    xl = [a for a in range(1, n + 1)
+          if Conv2d(1, 20, 20, 64, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=a).describe().startswith("igemm_xl")]
+    for a in xl:
+        with pytest.raises(ConvError):
+            Conv2d(1, 20, 20, 64, 64, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=a)   # Cout 64
+        with pytest.raises(ConvError):
+            Conv2d(1, 20, 20, 48, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=a)  # 96-byte channel blocks
 
 
 def fake(addr):

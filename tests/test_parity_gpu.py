@@ -17,33 +17,44 @@ from tests import helpers as H
 
 pytestmark = pytest.mark.gpu
 
-NTILES = _lib.lib().conv_algo_count() - 1  # the last algo forces the patch kernel
-ALGO_PATCH = NTILES + 1
+ALGO_COUNT = _lib.lib().conv_algo_count()
 
+
+def _algo_describe(algo):
+    # a layer every forced algorithm accepts: 3x3, 128-byte channel blocks, Cout = 256
+    return _lib.Conv2d(1, 20, 20, 64, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=algo).describe()
+
+
+ALGO_DESC = {a: _algo_describe(a) for a in range(1, ALGO_COUNT + 1)}
+TILE_ALGOS = [a for a, d in ALGO_DESC.items() if d.startswith("igemm ")]
+XL_ALGOS = [a for a, d in ALGO_DESC.items() if d.startswith("igemm_xl ")]
+ALGO_PATCH = next(a for a, d in ALGO_DESC.items() if d.startswith("patch3x3 "))
+assert len(TILE_ALGOS) + len(XL_ALGOS) + 1 == ALGO_COUNT
 
 # Tiles wider than 256 rows on either side need a 16-byte-vector loader; the
 # element-wise gather refuses them at prepare time.
-def _tile_dims(algo):
-    d = _lib.Conv2d(1, 20, 20, 64, 64, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=algo).describe()
-    co, px = re.search(r"co(\d+)xpx(\d+)", d).groups()
-    return int(co), int(px)
-
-
-BIG_TILES = {a for a in range(1, NTILES + 1) if max(_tile_dims(a)) > 256}
+BIG_TILES = {a for a in TILE_ALGOS if max(map(int, re.search(r"co(\d+)xpx(\d+)", ALGO_DESC[a]).groups())) > 256}
 
 
 def forced_tiles(layer):
-    """Every forced tile the layer accepts; only the generic loader may refuse,
-    and only the tiles wider than 256."""
+    """Every forced MFMA tile the layer accepts. Only the generic loader may
+    refuse a tile wider than 256; the large-layer kernel refuses layers
+    without 128-byte channel blocks or with Cout not a multiple of its tile."""
     out = []
-    for a in range(1, NTILES + 1):
+    for a in TILE_ALGOS + XL_ALGOS:
         try:
             _lib.Conv2d.from_layer(layer, algo=a).close()
             out.append(a)
         except _lib.ConvError as e:
-            assert a in BIG_TILES and "CONV_E_UNSUPPORTED" in str(e), (layer.name, a, str(e))
+            assert "CONV_E_UNSUPPORTED" in str(e), (layer.name, a, str(e))
             d = _lib.Conv2d.from_layer(layer).describe()
-            assert "loader=generic" in d or "smallk" in d, (layer.name, a, d)
+            if a in BIG_TILES:
+                assert "loader=generic" in d or "smallk" in d, (layer.name, a, d)
+            else:
+                assert a in XL_ALGOS, (layer.name, a, d)
+                cbytes = layer.cin * (2 if layer.dtype == "bf16" else 1)
+                tco = int(re.search(r"co(\d+)x", ALGO_DESC[a]).group(1))
+                assert cbytes % 128 or layer.cout % tco or layer.kh * layer.kw > 32, (layer.name, a, d)
     return out
 
 
@@ -111,6 +122,43 @@ def test_dense_all_tiles(layer):
     for algo in [0] + forced_tiles(layer):
         y, conv = H.gpu_run(layer, xg, t, algo=algo)
         what = "%s algo=%d [%s]" % (layer.name, algo, conv.describe())
+        yc = y.cpu()
+        if layer.dtype == "i8":
+            H.check_int(yc.numpy(), ref, layer, what)
+        else:
+            H.check_float(yc.float().numpy(), ref[0], ref[1], layer.dtype, what)
+        conv.close()
+
+
+# Layers for the large-layer kernel: 128-byte channel blocks, Cout a multiple
+# of 128 or 256, one, two and many K-tiles, stride and padding, int8 outputs,
+# and a layer small enough to be split along K.
+XL = [
+    L("xl_bf16_3x3_c64", 1, 19, 23, 64, 256, 3, 3, (1, 1), (1, 1)),
+    L("xl_bf16_1x1_nkt1", 2, 15, 17, 64, 128, 1, 1, act="none"),
+    L("xl_bf16_1x1_nkt2", 1, 20, 20, 128, 256, 1, 1, act="relu"),
+    L("xl_bf16_s2_pad", 1, 33, 31, 128, 256, 3, 3, (2, 2), (1, 1), act="relu6"),
+    L("xl_bf16_5x3_pad21", 1, 23, 17, 64, 128, 5, 3, (2, 1), (2, 1), act="relu"),
+    L("xl_i8_3x3_mish", 1, 21, 19, 128, 256, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="mish"),
+    L("xl_i8_3x3_i32", 2, 11, 13, 256, 128, 3, 3, (1, 1), (1, 1), dtype="i8", out="i32", act="none"),
+    L("xl_i8_1x1_relu", 1, 17, 18, 256, 512, 1, 1, dtype="i8", out="i8", act="relu"),
+    L("xl_bf16_splitk", 1, 10, 10, 512, 256, 3, 3, (1, 1), (1, 1)),
+]
+
+
+@pytest.mark.parametrize("layer", XL, ids=[l.name for l in XL])
+def test_xl_all_tiles(layer):
+    t = random_layer_tensors(layer, LAW[layer.dtype], seed=19)
+    ref = H.oracle_full(layer, t["x"], t)
+    xg = t["x"].cuda()
+    algos = [a for a in forced_tiles(layer) if a in XL_ALGOS]
+    assert algos, layer.name
+    for algo in algos:
+        y, conv = H.gpu_run(layer, xg, t, algo=algo)
+        what = "%s algo=%d [%s]" % (layer.name, algo, conv.describe())
+        assert "igemm_xl" in conv.describe()
+        if layer.name.endswith("splitk"):
+            assert "ksplit=1 " not in conv.describe(), what
         yc = y.cpu()
         if layer.dtype == "i8":
             H.check_int(yc.numpy(), ref, layer, what)
