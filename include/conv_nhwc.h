@@ -41,12 +41,15 @@
  *   MISH = v * tanh(ln(1 + e^v))   (the real function, not HardMish).
  *
  * Ownership: every device buffer (x, w, b, y, mosaic tiles and canvas) is
- * owned by the caller. A plan owns only host metadata; it is immutable after
- * conv_prepare and may be used from any thread and on any stream. conv_run
- * only enqueues work on the given stream: it allocates nothing, never
- * synchronises, copies nothing between host and device and caches nothing
- * between calls (x, w, b are read afresh every call), so it can be captured
- * into a HIP graph.
+ * owned by the caller. A plan owns host metadata and, for a layer whose
+ * reduction is split across workgroups (few output tiles, long K; conv_describe
+ * shows ksplit > 1), one device workspace for the partial sums, allocated by
+ * conv_prepare on the device current at that call and freed by conv_destroy.
+ * A plan is immutable after conv_prepare and may be used from any thread.
+ * conv_run only enqueues work on the given stream: it allocates nothing,
+ * never synchronises, copies nothing between host and device and caches
+ * nothing between calls (x, w, b are read afresh every call), so it can be
+ * captured into a HIP graph.
  *
  * Errors: every entry point returns a conv_status; a negative value names
  * the failure and nothing was enqueued. Faults inside an enqueued kernel
@@ -98,15 +101,22 @@ typedef struct conv_desc {
   int32_t dtype;          /* conv_dtype of x and w: F32, BF16 or I8 */
   int32_t out_dtype;      /* F32 for F32; BF16 for BF16; I8 or I32 for I8 */
   int32_t act;            /* conv_act */
-  int32_t algo;           /* 0 = the library chooses the kernel and tile;
-                             k > 0 forces tile configuration k of the
-                             implicit-GEMM kernel (see conv_algo_count) */
+  int32_t algo;           /* 0 = the library chooses the kernel and tile.
+                             k > 0 forces one kernel configuration of a
+                             dense bf16/int8 layer (for tests and tuning):
+                             1..10 the implicit-GEMM tiles, 11 the 3x3
+                             halo-patch kernel, 12..14 the large-layer
+                             kernel's tiles (conv_describe names the one
+                             chosen). A configuration that cannot run the
+                             layer gives CONV_E_UNSUPPORTED. */
 } conv_desc;
 
 typedef struct conv_plan conv_plan;
 
-/* Validate d and choose the kernel and its launch shape. Host only: touches
- * no device. On success *out holds a new plan (free with conv_destroy). */
+/* Validate d and choose the kernel and its launch shape. On success *out
+ * holds a new plan (free with conv_destroy). The only device call is the
+ * allocation of a split-K workspace when the plan splits the reduction; if
+ * that allocation fails the plan runs unsplit instead. */
 conv_status conv_prepare(const conv_desc* d, conv_plan** out);
 
 /* Enqueue the layer on `stream` (a hipStream_t; NULL = the default stream).
@@ -120,7 +130,10 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out);
  *   y : device pointer, NHWC of out_dtype, 16-byte aligned; must not overlap
  *       x, w or b (a layer reads its input while it writes its output, the
  *       planner-aliasing bug of the nanoinfer README).
- * Calls on different streams may run concurrently with one plan. */
+ * Calls on different streams may run concurrently with one plan, except for
+ * a plan with a split-K workspace (ksplit > 1 in conv_describe): its calls
+ * share that workspace and must be ordered (one stream, or events). Run it
+ * with the device of conv_prepare current. */
 conv_status conv_run(const conv_plan* p, const void* x, const void* w,
                      const void* b, void* y, void* stream);
 
@@ -134,7 +147,7 @@ conv_status conv_out_shape(const conv_plan* p, int64_t nhwc[4]);
  * into buf (NUL-terminated, truncated to len). */
 conv_status conv_describe(const conv_plan* p, char* buf, int32_t len);
 
-/* Number of forceable tile configurations (valid algo values are
+/* Number of forceable kernel configurations (valid algo values are
  * 1..conv_algo_count()). */
 int32_t conv_algo_count(void);
 
