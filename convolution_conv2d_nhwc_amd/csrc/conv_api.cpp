@@ -45,9 +45,12 @@ int choose_tile(const Geometry& g, int esz) {
     const TileCfg& t = kTiles[ti];
     return (long)((g.cout + t.tco - 1) / t.tco) * ((g.m + t.tpx - 1) / t.tpx);
   };
-  const int t128x128 = 3, t128x64 = 4, t64x64 = 5;
-  if (kbytes >= 2048 && g.cout >= 128 && nwg(t128x128) >= 384)
-    return nwg(t128x64) >= 2000 ? t128x64 : t128x128;
+  // Measured on MI355X over every tile: 128x128 wins whenever it still gives
+  // at least 384 workgroups (1.5 per CU); below that the 64x64 tile keeps
+  // the CUs busy.
+  (void)kbytes;
+  const int t128x128 = 3, t64x64 = 5;
+  if (g.cout >= 128 && nwg(t128x128) >= 384) return t128x128;
   return t64x64;
 }
 
@@ -61,10 +64,10 @@ int choose_tile(const Geometry& g, int esz) {
 // The large-layer kernel for long reductions over 128-byte channel blocks,
 // when its tiles still cover most of the chip: 256x256 when that gives at
 // least 160 workgroups, else 256x128 (measured on MI355X against the 64- and
-// 128-wide tiles: faster from about 8 KiB of K per output on).
+// 128-wide tiles: faster from about 4 KiB of K per output on).
 int choose_xl(const Geometry& g, int esz, int loader) {
   const long kbytes = (long)g.k * esz;
-  if (kbytes < 8192) return -1;
+  if (kbytes < 4096) return -1;
   auto nwg = [&](int ti) {
     const TileCfg& t = kXlTiles[ti];
     return (long)(g.cout / t.tco) * ((g.m + t.tpx - 1) / t.tpx);

@@ -436,6 +436,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
     }
     return;
   }
+  if ((g.cout & 3) == 0) {
+    const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1));
+    with_epilogue<ESZ>(a.out_kind, a.e.act, [&](auto oc, auto ac) {
+      constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
+      StaticFor<0, FCO>::run([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int co = co_w + 16 * i;
+        const QuadConsts q = load_quad_consts_t<ESZ>(a.e, co, g.cout);
+        StaticFor<0, FPX>::run([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          store_quad_t<ESZ, OUT, ACT>(acc[i][j], q, co, px_w + 16 * j, o);
+        });
+      });
+    });
+    return;
+  }
+  // Cout not a multiple of 4: per-element stores
   StaticFor<0, FCO>::run([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     const int co = co_w + 16 * i;

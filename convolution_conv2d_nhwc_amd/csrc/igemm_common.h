@@ -85,13 +85,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const void* ws, int 
   const int nq = cout / 4;
   const long total = (long)m * nq;
   const acc_t* w = reinterpret_cast<const acc_t*>(ws);
-  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (long)gridDim.x * blockDim.x) {
-    acc_t acc = w[q];
-    for (int s = 1; s < ksplit; ++s) acc += w[(size_t)s * total + q];
-    const int px = (int)(q / nq);
-    const int co = (int)(q - (long)px * nq) * 4;
-    store_quad<ESZ>(acc, load_quad_consts<ESZ>(e, co, cout), co, px, cout, out_kind, e.act, y);
-  }
+  const OutRef o = out_ref(y, m, cout, ESZ == 2 ? 2 : (out_kind == OUT_I32 ? 4 : 1));
+  with_epilogue<ESZ>(out_kind, e.act, [&](auto oc, auto ac) {
+    constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
+    for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (long)gridDim.x * blockDim.x) {
+      acc_t acc = w[q];
+      for (int s = 1; s < ksplit; ++s) acc += w[(size_t)s * total + q];
+      const int px = (int)(q / nq);
+      const int co = (int)(q - (long)px * nq) * 4;
+      store_quad_t<ESZ, OUT, ACT>(acc, load_quad_consts_t<ESZ>(e, co, cout), co, px, o);
+    }
+  });
 }
 
 }  // namespace

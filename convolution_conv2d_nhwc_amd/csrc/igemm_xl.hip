@@ -87,6 +87,17 @@ struct MfmaAgpr<1> {
   }
 };
 
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16 l (lds is wave-uniform); an out-of-range offset writes zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, soff, 0,
+                                           0);
+}
+
+// Wait until every vector-memory load of this wave, the direct-to-LDS ones
+// included, has completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Wait states between a VALU write of an accumulator and its first MFMA, and
 // between its last MFMA and a VALU read of it. The guards are volatile, so
 // they keep their order relative to the MFMAs: every accumulator gets its own
@@ -128,7 +139,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // ---- loader state: chunk j of this thread is (row tid/8 + 32 j, column tid%8)
   const int row0 = tid >> 3;
-  const int c16 = (tid & 7) * 16;
+  // The direct-to-LDS load writes lane l's 16 bytes at position l of the
+  // wave's 1 KiB LDS block (row l / 8, chunk l % 8); to land the swizzled
+  // layout (chunk c of row r at c ^ (r & 7)) lane l fetches chunk
+  // (l % 8) ^ (l / 8) of its row (row & 7 == l / 8 for every block).
+  const int c16 = ((tid & 7) ^ ((tid >> 3) & 7)) * 16;
   const int cbytes = g.c * ESZ;
   const int kbytes = g.k * ESZ;
   const int nkt_all = kbytes / kBKB;
@@ -215,29 +230,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     return f;
   };
-  // chunk c < ACH: weight row row0 + 32 c; else pixel row row0 + 32 (c - ACH)
-  auto fetch_chunk = [&](const Fetch& f, auto cc, i32x4 (&ga)[ACH], i32x4 (&gb)[BCH]) {
+  // Chunk c < ACH: weight rows row0 + 32 c; else pixel rows row0 + 32 (c - ACH).
+  // One instruction per wave moves 8 rows (1 KiB) from global memory straight
+  // into LDS buffer buf, bypassing registers.
+  const int wave_blk = (tid >> 6) * 1024;  // this wave's 1 KiB block of each 32-row group
+  auto dma_chunk = [&](const Fetch& f, int buf, auto cc) {
     constexpr int c = decltype(cc)::value;
     if constexpr (c < ACH) {
-      ga[c] = bload16s(rw, f.live ? voff_a : kOOB, f.live ? f.soff_a + c * astride : 0);
+      dma16(rw, As + buf * TCO * kBKB + c * 4096 + wave_blk, f.live ? voff_a : kOOB,
+            f.live ? f.soff_a + c * astride : 0);
     } else {
       constexpr int j = c - ACH;
       bool ok = f.live;
       if constexpr (LOADER == LOAD_TAP) ok = ok && ((tmask[j] >> (f.tap & 31)) & 1u);
-      gb[j] = bload16s(rx, ok ? voff_b[j] : kOOB, f.soff_b);
+      dma16(rx, Bs + buf * TPX * kBKB + j * 4096 + wave_blk, ok ? voff_b[j] : kOOB, f.soff_b);
     }
   };
-  auto stash_chunk = [&](int buf, auto cc, const i32x4 (&ga)[ACH], const i32x4 (&gb)[BCH]) {
-    constexpr int c = decltype(cc)::value;
-    const int col = tid & 7;
-    if constexpr (c < ACH)
-      *reinterpret_cast<i32x4*>(As + buf * TCO * kBKB + lds_off(row0 + 32 * c, col)) = ga[c];
-    else
-      *reinterpret_cast<i32x4*>(Bs + buf * TPX * kBKB + lds_off(row0 + 32 * (c - ACH), col)) = gb[c - ACH];
-  };
-  auto fetch_all = [&](int kt, i32x4 (&ga)[ACH], i32x4 (&gb)[BCH]) {
+  auto dma_all = [&](int kt, int buf) {
     const Fetch f = fetch_begin(kt);
-    StaticFor<0, ACH + BCH>::run([&](auto cc) { fetch_chunk(f, cc, ga, gb); });
+    StaticFor<0, ACH + BCH>::run([&](auto cc) { dma_chunk(f, buf, cc); });
   };
 
   // MFMA operand r of K-step s (0 or 1) of the tile in LDS buffer buf
@@ -280,64 +291,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     mfma_range(std::integral_constant<int, 0>{}, std::integral_constant<int, NMF>{}, af, bf);
   };
 
-  // G register sets hold the next tiles in flight: set r holds tiles
-  // kt0 + 1 + r, kt0 + 1 + r + G, ... Tile t+1 leaves set t % G for LDS
-  // during step t, and the set is re-issued for tile t+1+G.
-  i32x4 ga[G][ACH], gb[G][BCH];
+  // LDS buffer t % 2 holds K-tile t. Tile t+1's loads were issued one
+  // K-tile earlier; each step waits for them at its barrier.
   i32x4 a0[FCO], b0[FPX], a1[FCO], b1[FPX];
-  fetch_all(kt0, ga[0], gb[0]);
-  StaticFor<0, ACH + BCH>::run([&](auto cc) { stash_chunk(0, cc, ga[0], gb[0]); });
-#pragma unroll
-  for (int r = 0; r < G; ++r) fetch_all(kt0 + 1 + r, ga[r], gb[r]);
+  dma_all(kt0, 0);
+  dma_all(kt0 + 1, 1);
+  wait_vmem();
   __syncthreads();
   read_all(0, 0, a0, b0);
 
-  // One K-tile. Half 1 spreads, over the K-step-0 MFMAs, the K-step-1 operand
-  // reads, the LDS writes of tile t+1 and the global loads of tile t+1+G
-  // (chunk by chunk: the write frees the register the load refills). Half 2
-  // spreads the K-step-0 operand reads of tile t+1 over the K-step-1 MFMAs.
-  // The MFMA statements are ordered memory barriers for the compiler, so the
-  // interleaving is issued as written.
+  // One K-tile. Half 1 spreads the K-step-1 operand reads over the
+  // K-step-0 MFMAs. After the barrier (tile t+1 complete and visible, every
+  // read of buffer t % 2 done), half 2 issues the loads of tile t+2 into
+  // buffer t % 2 and spreads the K-step-0 operand reads of tile t+1 over the
+  // K-step-1 MFMAs. The MFMA statements are ordered memory barriers for the
+  // compiler, so the interleaving is issued as written.
   constexpr int CH = ACH + BCH;
   constexpr int NR = FCO + FPX;
-  auto step = [&](int t, i32x4 (&sa)[ACH], i32x4 (&sb)[BCH]) {
+  auto step = [&](int t) {
     const int buf = t & 1;
-    const Fetch f = fetch_begin(kt0 + t + 1 + G);
-    StaticFor<0, CH>::run([&](auto cc) {
-      constexpr int c = decltype(cc)::value;
-      mfma_range(std::integral_constant<int, c * NMF / CH>{}, std::integral_constant<int, (c + 1) * NMF / CH>{}, a0,
-                 b0);
-      if constexpr (c < NR) read_frag(buf, 1, cc, a1, b1);
-      stash_chunk(buf ^ 1, cc, sa, sb);
-      if constexpr (XL_FETCH_MODE == 0 || (XL_FETCH_MODE == 1 && c < ACH)) fetch_chunk(f, cc, sa, sb);
-    });
-    StaticFor<CH, NR>::run([&](auto rc) { read_frag(buf, 1, rc, a1, b1); });
-    __syncthreads();
     StaticFor<0, NR>::run([&](auto rc) {
       constexpr int r = decltype(rc)::value;
+      mfma_range(std::integral_constant<int, r * NMF / NR>{}, std::integral_constant<int, (r + 1) * NMF / NR>{}, a0,
+                 b0);
+      read_frag(buf, 1, rc, a1, b1);
+    });
+    wait_vmem();
+    __syncthreads();
+    const Fetch f = fetch_begin(kt0 + t + 2);
+    StaticFor<0, NR>::run([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      if constexpr (r < CH) dma_chunk(f, buf, rc);
       read_frag(buf ^ 1, 0, rc, a0, b0);
-      if constexpr (XL_FETCH_MODE == 1 && r < BCH) fetch_chunk(f, std::integral_constant<int, ACH + r>{}, sa, sb);
-      if constexpr (XL_FETCH_MODE == 2 && r < CH) fetch_chunk(f, rc, sa, sb);
       mfma_range(std::integral_constant<int, r * NMF / NR>{}, std::integral_constant<int, (r + 1) * NMF / NR>{}, a1,
                  b1);
     });
   };
   // K-tiles 0 .. nkt-2 of this split: the next tile always exists
   int t = 0;
-  for (; t + G < nkt; t += G) {
-#pragma unroll
-    for (int r = 0; r < G; ++r) step(t + r, ga[r], gb[r]);
-  }
-#pragma unroll
-  for (int r = 0; r < G - 1; ++r)
-    if (t + 1 < nkt) {
-      step(t, ga[r], gb[r]);
-      ++t;
-    }
-  // last K-tile
+  for (; t + 1 < nkt; ++t) step(t);
+  // last K-tile; the loads issued past it read nothing anybody uses
   read_all(t & 1, 1, a1, b1);
   mfmas(a0, b0);
   mfmas(a1, b1);
+  wait_vmem();
   StaticFor<0, FCO>::run([&](auto ic) {
     StaticFor<0, FPX>::run([&](auto jc) { agpr_guard(acc[decltype(ic)::value][decltype(jc)::value]); });
   });
@@ -358,14 +355,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     });
     return;
   }
-  StaticFor<0, FCO>::run([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    const int co = co_w + 16 * i;
-    const QuadConsts q = load_quad_consts<ESZ>(a.e, co, g.cout);
-    StaticFor<0, FPX>::run([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      const int px = px_w + 16 * j;
-      if (px < g.m) store_quad<ESZ>(acc[i][j], q, co, px, g.cout, a.out_kind, a.e.act, a.y);
+  const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1));
+  with_epilogue<ESZ>(a.out_kind, a.e.act, [&](auto oc, auto ac) {
+    constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
+    StaticFor<0, FCO>::run([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int co = co_w + 16 * i;
+      const QuadConsts q = load_quad_consts_t<ESZ>(a.e, co, g.cout);
+      StaticFor<0, FPX>::run([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        store_quad_t<ESZ, OUT, ACT>(acc[i][j], q, co, px_w + 16 * j, o);
+      });
     });
   });
 }

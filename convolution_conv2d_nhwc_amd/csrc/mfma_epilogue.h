@@ -7,6 +7,8 @@
 // int32 checkpoint (acc + bias, optional ReLU).
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace convnhwc {
@@ -84,6 +86,144 @@ __device__ __forceinline__ void store_quad(const acc_t& v, const QuadConsts& q, 
       for (int r = 0; r < 4; ++r)
         if (co + r < cout) yp[r] = (int8_t)b[r];
     }
+  }
+}
+
+// ---- compile-time epilogue ------------------------------------------------
+// The per-element form above decides the activation and the output kind at
+// run time for every element; across the 64-256 accumulator quads of a
+// large tile those uniform branches cost more than the arithmetic. The forms
+// below take both as template arguments (with_epilogue turns the layer's run
+// time values into them once per tile) and store through buffer
+// instructions, whose out-of-range offsets are dropped, so a ragged tile
+// needs no branch either.
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int ACT>
+__device__ __forceinline__ float act_t(float v) {
+  if constexpr (ACT == ACT_RELU)
+    return fmaxf(v, 0.0f);
+  else if constexpr (ACT == ACT_RELU6)
+    return fminf(fmaxf(v, 0.0f), 6.0f);
+  else if constexpr (ACT == ACT_MISH)
+    return mish_f32(v);
+  else
+    return v;
+}
+
+template <int ACT>
+__device__ __forceinline__ int requant_i8_t(int r, float s) {
+  const float v = __fmul_rn((float)r, s);
+  const float m = act_t<ACT>(v);
+  return (int)fminf(fmaxf(__builtin_rintf(m), -127.0f), 127.0f);
+}
+
+// f(out_kind, act) with both as std::integral_constant, for the output kinds
+// and activations an element size supports (bf16 -> bf16; int8 -> int8, or
+// the int32 checkpoint with NONE/RELU).
+template <int ESZ, class F>
+__device__ __forceinline__ void with_epilogue(int out_kind, int act, F&& f) {
+  using std::integral_constant;
+  if constexpr (ESZ == 2) {
+    switch (act) {
+      case ACT_RELU: f(integral_constant<int, OUT_BF16>{}, integral_constant<int, ACT_RELU>{}); break;
+      case ACT_RELU6: f(integral_constant<int, OUT_BF16>{}, integral_constant<int, ACT_RELU6>{}); break;
+      case ACT_MISH: f(integral_constant<int, OUT_BF16>{}, integral_constant<int, ACT_MISH>{}); break;
+      default: f(integral_constant<int, OUT_BF16>{}, integral_constant<int, ACT_NONE>{}); break;
+    }
+  } else if (out_kind == OUT_I32) {
+    if (act == ACT_RELU)
+      f(integral_constant<int, OUT_I32>{}, integral_constant<int, ACT_RELU>{});
+    else
+      f(integral_constant<int, OUT_I32>{}, integral_constant<int, ACT_NONE>{});
+  } else {
+    switch (act) {
+      case ACT_RELU: f(integral_constant<int, OUT_I8>{}, integral_constant<int, ACT_RELU>{}); break;
+      case ACT_RELU6: f(integral_constant<int, OUT_I8>{}, integral_constant<int, ACT_RELU6>{}); break;
+      case ACT_MISH: f(integral_constant<int, OUT_I8>{}, integral_constant<int, ACT_MISH>{}); break;
+      default: f(integral_constant<int, OUT_I8>{}, integral_constant<int, ACT_NONE>{}); break;
+    }
+  }
+}
+
+// The output tensor as a buffer: y, its size in bytes, m pixels x cout
+// channels (cout % 4 == 0 for store_quad_t).
+struct OutRef {
+  __amdgpu_buffer_rsrc_t r;
+  int m, cout;
+};
+
+__device__ __forceinline__ OutRef out_ref(void* y, int m, int cout, int out_esz) {
+  OutRef o;
+  o.r = __builtin_amdgcn_make_buffer_rsrc(y, 0, m * cout * out_esz, 0x00020000);
+  o.m = m;
+  o.cout = cout;
+  return o;
+}
+
+// Per-channel constants of channels co..co+3 for store_quad_t (cout % 4 ==
+// 0, co % 4 == 0): one 16-byte buffer load per array; a NULL array or a quad
+// past cout reads as zeros.
+template <int ESZ>
+__device__ __forceinline__ QuadConsts load_quad_consts_t(const Epi& e, int co, int cout) {
+  QuadConsts q;
+  const uint32_t off = (uint32_t)co * 4u;
+  if constexpr (ESZ == 2) {
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(e.bias), 0, e.bias ? cout * 4 : 0, 0x00020000);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      q.bsf[r] = __builtin_bit_cast(float, (uint32_t)b[r]);
+      q.bsi[r] = 0;
+      q.scl[r] = 0.0f;
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(e.ibias), 0, e.ibias ? cout * 4 : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(e.scale), 0, e.scale ? cout * 4 : 0, 0x00020000);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+    const u32x4 sc = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      q.bsf[r] = 0.0f;
+      q.bsi[r] = (int)b[r];
+      q.scl[r] = __builtin_bit_cast(float, (uint32_t)sc[r]);
+    }
+  }
+  return q;
+}
+
+// Store quad v (channels co..co+3 of pixel px); nothing is written when
+// px >= m or co >= cout. Requires cout % 4 == 0.
+template <int ESZ, int OUT, int ACT, typename acc_t>
+__device__ __forceinline__ void store_quad_t(const acc_t& v, const QuadConsts& q, int co, int px, const OutRef& o) {
+  constexpr uint32_t kNowhere = 0x80000000u;  // past any output buffer
+  const bool in = px < o.m && co < o.cout;
+  const uint32_t idx = (uint32_t)(px * o.cout + co);
+  if constexpr (ESZ == 2) {
+    uint32_t h[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_bits(act_t<ACT>(v[r] + q.bsf[r]));
+    const u32x2 d = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    __builtin_amdgcn_raw_buffer_store_b64(d, o.r, in ? idx * 2u : kNowhere, 0, 0);
+  } else if constexpr (OUT == OUT_I32) {
+    u32x4 d;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int w = v[r] + q.bsi[r];
+      if constexpr (ACT == ACT_RELU) w = w > 0 ? w : 0;
+      d[r] = (uint32_t)w;
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(d, o.r, in ? idx * 4u : kNowhere, 0, 0);
+  } else {
+    uint32_t b = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b |= ((uint32_t)requant_i8_t<ACT>(v[r] + q.bsi[r], q.scl[r]) & 0xffu) << (8 * r);
+    __builtin_amdgcn_raw_buffer_store_b32(b, o.r, in ? idx : kNowhere, 0, 0);
   }
 }
 

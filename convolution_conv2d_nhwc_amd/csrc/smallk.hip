@@ -145,6 +145,7 @@ __global__ __launch_bounds__(256) void smallk_kernel(SkArgs a) {
   for (int i = 0; i < FCO; ++i) q[i] = load_quad_consts<ESZ>(a.e, co0 + 16 * i + 4 * kg, g.cout);
 
   const int hw_o = g.ho * g.wo;
+  const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1));
   const int nwaves = gridDim.x * 4;
   for (int pt = blockIdx.x * 4 + (threadIdx.x >> 6); pt < a.npx_tiles; pt += nwaves) {
     const int pbase = pt * 64;
@@ -183,6 +184,17 @@ __global__ __launch_bounds__(256) void smallk_kernel(SkArgs a) {
 #pragma unroll
         for (int i = 0; i < FCO; ++i) acc[i][j] = Mfma<ESZ>::run(af[i][ks], bf, acc[i][j]);
       }
+    if ((g.cout & 3) == 0) {
+      with_epilogue<ESZ>(a.out_kind, a.e.act, [&](auto oc, auto ac) {
+        constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
+#pragma unroll
+        for (int i = 0; i < FCO; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            store_quad_t<ESZ, OUT, ACT>(acc[i][j], q[i], co0 + 16 * i + 4 * kg, pbase + 16 * j + lr, o);
+      });
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < FCO; ++i) {
       const int co = co0 + 16 * i + 4 * kg;
