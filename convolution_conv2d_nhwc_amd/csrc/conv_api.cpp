@@ -342,13 +342,18 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
     static const char* kT[] = {"", "signed char", "unsigned short", "", "float"};
     int ve, pw, th = 0;
     dw_shape(p, &ve, &pw, &th);
+    // the kernels' last two template arguments: activation, and the int8
+    // output kind (the int32 checkpoint or not; also 2 for float layers)
+    const int act = p->out_kind == OUT_I32 && p->d.act != CONV_ACT_RELU ? CONV_ACT_NONE : p->d.act;
+    const int ok = p->out_kind == OUT_I32 ? OUT_I32 : OUT_I8;
     if (th)
-      std::snprintf(buf, len, "dw3x3 dtype=%s out=%s stride=%dx%d rows kernel=dw3x3_rows_kernel<%s, %d, %d, %d>",
-                    kDt[p->d.dtype], kDt[p->d.out_dtype], p->g.sh, p->g.sw, kT[p->in_esz], ve, pw, th);
+      std::snprintf(buf, len,
+                    "dw3x3 dtype=%s out=%s stride=%dx%d rows kernel=dw3x3_rows_kernel<%s, %d, %d, %d, %d, %d>",
+                    kDt[p->d.dtype], kDt[p->d.out_dtype], p->g.sh, p->g.sw, kT[p->in_esz], ve, pw, th, act, ok);
     else
-      std::snprintf(buf, len, "dw3x3 dtype=%s out=%s loader=%s stride=%dx%d kernel=dw3x3_kernel<%s, %d, %d>",
+      std::snprintf(buf, len, "dw3x3 dtype=%s out=%s loader=%s stride=%dx%d kernel=dw3x3_kernel<%s, %d, %d, %d, %d>",
                     kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], p->g.sh, p->g.sw, kT[p->in_esz], ve,
-                    pw);
+                    pw, act, ok);
   } else {
     std::snprintf(buf, len, "direct_f32 m=%d k=%d kernel=conv_f32_kernel", p->g.m, p->g.k);
   }

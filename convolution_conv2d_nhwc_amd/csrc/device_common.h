@@ -76,6 +76,27 @@ struct StaticFor<N, N> {
   __device__ __forceinline__ static void run(F&&) {}
 };
 
+// The same with the activation and, for requant_i8_t, the clamp fixed at
+// compile time (no per-element branch).
+template <int ACT>
+__device__ __forceinline__ float act_t(float v) {
+  if constexpr (ACT == ACT_RELU)
+    return fmaxf(v, 0.0f);
+  else if constexpr (ACT == ACT_RELU6)
+    return fminf(fmaxf(v, 0.0f), 6.0f);
+  else if constexpr (ACT == ACT_MISH)
+    return mish_f32(v);
+  else
+    return v;
+}
+
+template <int ACT>
+__device__ __forceinline__ int requant_i8_t(int r, float s) {
+  const float v = __fmul_rn((float)r, s);
+  const float m = act_t<ACT>(v);
+  return (int)fminf(fmaxf(__builtin_rintf(m), -127.0f), 127.0f);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
   __bf16 h = (__bf16)v;  // v_cvt_pk_bf16_f32: round to nearest even
   return __builtin_bit_cast(uint16_t, h);

@@ -77,7 +77,9 @@ struct Elt<int8_t> {
 };
 
 // VE = channels per lane (16 bytes worth, or 1 for the scalar fallback).
-template <typename T, int VE, int PW>
+// ACT and OUT (the int8 output kind) are compile-time: the epilogue runs once
+// per output vector and a per-element branch on them would cost more than it.
+template <typename T, int VE, int PW, int ACT, int OUT>
 __global__ __launch_bounds__(256) void dw3x3_kernel(DwArgs a) {
   typedef typename Elt<T>::acc_t acc_t;
   constexpr int ESZ = sizeof(T);
@@ -180,12 +182,12 @@ __global__ __launch_bounds__(256) void dw3x3_kernel(DwArgs a) {
       int rv[VE];
 #pragma unroll
       for (int e = 0; e < VE; ++e) rv[e] = acc[p][e] + (a.e.ibias ? a.e.ibias[c0 + e] : 0);
-      if (a.out_kind == OUT_I32) {
+      if constexpr (OUT == OUT_I32) {
         int32_t* yp = reinterpret_cast<int32_t*>(a.y) + off;
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
           int v = rv[e];
-          if (a.e.act == ACT_RELU) v = v > 0 ? v : 0;
+          if constexpr (ACT == ACT_RELU) v = v > 0 ? v : 0;
           yp[e] = v;
         }
       } else {
@@ -194,18 +196,18 @@ __global__ __launch_bounds__(256) void dw3x3_kernel(DwArgs a) {
           uint32_t wd[4] = {0, 0, 0, 0};
 #pragma unroll
           for (int e = 0; e < VE; ++e)
-            wd[e >> 2] |= ((uint32_t)requant_i8(rv[e], a.e.scale[c0 + e], a.e.act) & 0xffu) << (8 * (e & 3));
+            wd[e >> 2] |= ((uint32_t)requant_i8_t<ACT>(rv[e], a.e.scale[c0 + e]) & 0xffu) << (8 * (e & 3));
           *reinterpret_cast<i32x4*>(yp) = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
         } else {
 #pragma unroll
-          for (int e = 0; e < VE; ++e) yp[e] = (int8_t)requant_i8(rv[e], a.e.scale[c0 + e], a.e.act);
+          for (int e = 0; e < VE; ++e) yp[e] = (int8_t)requant_i8_t<ACT>(rv[e], a.e.scale[c0 + e]);
         }
       }
     } else {
       float v[VE];
 #pragma unroll
       for (int e = 0; e < VE; ++e)
-        v[e] = apply_act(acc[p][e] + (a.e.bias ? a.e.bias[c0 + e] : 0.0f), a.e.act);
+        v[e] = act_t<ACT>(acc[p][e] + (a.e.bias ? a.e.bias[c0 + e] : 0.0f));
       if constexpr (sizeof(T) == 4) {
         float* yp = reinterpret_cast<float*>(a.y) + off;
         if constexpr (VE == 4) {
@@ -287,7 +289,7 @@ __device__ __forceinline__ typename Elt<T>::acc_t widen_word(uint32_t wd, int e)
   }
 }
 
-template <typename T, int VE, int PW, int TH>
+template <typename T, int VE, int PW, int TH, int ACT, int OUT>
 __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
   typedef typename Elt<T>::acc_t acc_t;
   constexpr int ESZ = sizeof(T);
@@ -389,12 +391,12 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
       if (wo >= g.wo) break;
       const size_t off = ((size_t)(n * g.ho + ho) * g.wo + wo) * g.cout + c0;
       if constexpr (ESZ == 1) {
-        if (a.out_kind == OUT_I32) {
+        if constexpr (OUT == OUT_I32) {
           int32_t* yp = reinterpret_cast<int32_t*>(a.y) + off;
 #pragma unroll
           for (int e = 0; e < VE; ++e) {
             int v = acc[p][e] + bsi[e];
-            if (a.e.act == ACT_RELU) v = v > 0 ? v : 0;
+            if constexpr (ACT == ACT_RELU) v = v > 0 ? v : 0;
             yp[e] = v;
           }
         } else {
@@ -403,7 +405,7 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
           for (int q = 0; q < VE / 4; ++q) wd[q] = 0;
 #pragma unroll
           for (int e = 0; e < VE; ++e)
-            wd[e >> 2] |= ((uint32_t)requant_i8(acc[p][e] + bsi[e], scl[e], a.e.act) & 0xffu) << (8 * (e & 3));
+            wd[e >> 2] |= ((uint32_t)requant_i8_t<ACT>(acc[p][e] + bsi[e], scl[e]) & 0xffu) << (8 * (e & 3));
           if constexpr (VE == 4)
             *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(a.y) + off) = wd[0];
           else if constexpr (VE == 8)
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
       } else {
         float v[VE];
 #pragma unroll
-        for (int e = 0; e < VE; ++e) v[e] = apply_act(acc[p][e] + bsf[e], a.e.act);
+        for (int e = 0; e < VE; ++e) v[e] = act_t<ACT>(acc[p][e] + bsf[e]);
         if constexpr (ESZ == 4) {
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.y) + off) = f32x4{v[0], v[1], v[2], v[3]};
         } else {
@@ -434,6 +436,23 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
   }
 }
 
+// f(OUT, ACT) as compile-time constants for a layer's output kind and
+// activation (the int32 checkpoint allows NONE and RELU only).
+template <class F>
+hipError_t with_act(int out_kind, int act, F&& f) {
+  using std::integral_constant;
+  if (out_kind == OUT_I32) {
+    if (act == ACT_RELU) return f(integral_constant<int, OUT_I32>{}, integral_constant<int, ACT_RELU>{});
+    return f(integral_constant<int, OUT_I32>{}, integral_constant<int, ACT_NONE>{});
+  }
+  switch (act) {
+    case ACT_RELU: return f(integral_constant<int, OUT_I8>{}, integral_constant<int, ACT_RELU>{});
+    case ACT_RELU6: return f(integral_constant<int, OUT_I8>{}, integral_constant<int, ACT_RELU6>{});
+    case ACT_MISH: return f(integral_constant<int, OUT_I8>{}, integral_constant<int, ACT_MISH>{});
+    default: return f(integral_constant<int, OUT_I8>{}, integral_constant<int, ACT_NONE>{});
+  }
+}
+
 template <typename T, int VE, int PW, int TH>
 hipError_t launch_rows_t(const DwArgs& base, hipStream_t s) {
   DwArgs a = base;
@@ -441,8 +460,11 @@ hipError_t launch_rows_t(const DwArgs& base, hipStream_t s) {
   a.wgrp = (a.g.wo + PW - 1) / PW;
   a.total = (long)a.g.n * ((a.g.ho + TH - 1) / TH) * a.wgrp * a.cv;
   const long blocks = (a.total + 255) / 256;
-  hipLaunchKernelGGL((dw3x3_rows_kernel<T, VE, PW, TH>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return with_act(a.out_kind, a.e.act, [&](auto oc, auto ac) {
+    hipLaunchKernelGGL((dw3x3_rows_kernel<T, VE, PW, TH, decltype(ac)::value, decltype(oc)::value>),
+                       dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+  });
 }
 
 template <typename T, int VE, int PW>
@@ -452,8 +474,11 @@ hipError_t launch_dw_t(const DwArgs& base, hipStream_t s) {
   a.wgrp = (a.g.wo + PW - 1) / PW;
   a.total = (long)a.g.n * a.g.ho * a.wgrp * a.cv;
   const long blocks = (a.total + 255) / 256;
-  hipLaunchKernelGGL((dw3x3_kernel<T, VE, PW>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return with_act(a.out_kind, a.e.act, [&](auto oc, auto ac) {
+    hipLaunchKernelGGL((dw3x3_kernel<T, VE, PW, decltype(ac)::value, decltype(oc)::value>), dim3((unsigned)blocks),
+                       dim3(256), 0, s, a);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace

@@ -101,25 +101,6 @@ __device__ __forceinline__ void store_quad(const acc_t& v, const QuadConsts& q, 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <int ACT>
-__device__ __forceinline__ float act_t(float v) {
-  if constexpr (ACT == ACT_RELU)
-    return fmaxf(v, 0.0f);
-  else if constexpr (ACT == ACT_RELU6)
-    return fminf(fmaxf(v, 0.0f), 6.0f);
-  else if constexpr (ACT == ACT_MISH)
-    return mish_f32(v);
-  else
-    return v;
-}
-
-template <int ACT>
-__device__ __forceinline__ int requant_i8_t(int r, float s) {
-  const float v = __fmul_rn((float)r, s);
-  const float m = act_t<ACT>(v);
-  return (int)fminf(fmaxf(__builtin_rintf(m), -127.0f), 127.0f);
-}
-
 // f(out_kind, act) with both as std::integral_constant, for the output kinds
 // and activations an element size supports (bf16 -> bf16; int8 -> int8, or
 // the int32 checkpoint with NONE/RELU).
