@@ -231,6 +231,26 @@ __global__ __launch_bounds__(256) void patch3x3_kernel(PatchArgs a) {
   }
 
   // ---- fused epilogue --------------------------------------------------------
+  // A quad outside the image is sent past the output (px = m: not stored).
+  const int wo = wo0 + lr;
+  if ((g.cout & 3) == 0) {
+    const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1));
+    with_epilogue<ESZ>(a.out_kind, a.e.act, [&](auto oc, auto ac) {
+      constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
+#pragma unroll
+      for (int i = 0; i < FCO; ++i) {
+        const int co = co0 + 16 * i + 4 * kg;
+        const QuadConsts q = load_quad_consts_t<ESZ>(a.e, co, g.cout);
+#pragma unroll
+        for (int f = 0; f < FPX; ++f) {
+          const int ho = ho0 + wave * FPX + f;
+          const int px = (ho < g.ho && wo < g.wo) ? (n * g.ho + ho) * g.wo + wo : g.m;
+          store_quad_t<ESZ, OUT, ACT>(acc[i][f], q, co, px, o);
+        }
+      }
+    });
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FCO; ++i) {
     const int co = co0 + 16 * i + 4 * kg;
@@ -239,7 +259,6 @@ __global__ __launch_bounds__(256) void patch3x3_kernel(PatchArgs a) {
 #pragma unroll
     for (int f = 0; f < FPX; ++f) {
       const int ho = ho0 + wave * FPX + f;
-      const int wo = wo0 + lr;
       if (ho < g.ho && wo < g.wo)
         store_quad<ESZ>(acc[i][f], q, co, (n * g.ho + ho) * g.wo + wo, g.cout, a.out_kind, a.e.act, a.y);
     }
