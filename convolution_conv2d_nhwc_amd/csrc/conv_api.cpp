@@ -61,20 +61,38 @@ int choose_tile(const Geometry& g, int esz) {
 // applies the epilogue. If the workspace cannot be allocated (no device, out
 // of memory) the plan runs unsplit, which is slower but the same arithmetic
 // up to the order of the fp32 additions.
-// The large-layer kernel for long reductions over 128-byte channel blocks,
-// when its tiles still cover most of the chip: 256x256 when that gives at
-// least 160 workgroups, else 256x128 (measured on MI355X against the 64- and
-// 128-wide tiles: faster from about 4 KiB of K per output on).
+// The large-layer kernel for long reductions over 128-byte channel blocks.
+// One workgroup fills a CU (its LDS), so a configuration's time is its number
+// of rounds of 256 workgroups times one workgroup's time, modelled per K-tile
+// as the MFMA cycles of a wave (32 per 16x16 fragment pair) plus the cycles
+// the CU's load path needs for the tile's rows (about 17 per 1 KiB, measured
+// on MI355X; the two do not overlap), plus the epilogue (about 70 cycles per
+// output element of a lane). The cheapest configuration is taken when it keeps
+// at least 160 workgroups busy and the reduction is at least 2 KiB per output
+// for 256-channel tiles, 4 KiB for 128-channel tiles (below that the
+// implicit-GEMM tiles measured faster).
 int choose_xl(const Geometry& g, int esz, int loader) {
   const long kbytes = (long)g.k * esz;
-  if (kbytes < 4096) return -1;
-  auto nwg = [&](int ti) {
+  if (kbytes < 2048) return -1;
+  const double nkt = (double)(kbytes / 128);
+  int best = -1;
+  double best_t = 0;
+  for (int ti = 0; ti < kNumXlTiles; ++ti) {
+    if (!xl_eligible(g, esz, loader, ti)) continue;
     const TileCfg& t = kXlTiles[ti];
-    return (long)(g.cout / t.tco) * ((g.m + t.tpx - 1) / t.tpx);
-  };
-  if (xl_eligible(g, esz, loader, 0) && nwg(0) >= 160) return 0;
-  if (xl_eligible(g, esz, loader, 1) && nwg(1) >= 160) return 1;
-  return -1;
+    if (t.tco < 256 && kbytes < 4096) continue;
+    const long nwg = (long)(g.cout / t.tco) * ((g.m + t.tpx - 1) / t.tpx);
+    if (nwg < 160) continue;
+    const double rounds = (double)((nwg + 255) / 256);
+    const double per_kt = (t.tco / 32.0) * (t.tpx / 32.0) * 32.0 + (t.tco + t.tpx) / 8.0 * 17.0;
+    const double wg = nkt * per_kt + 7000.0 + 70.0 * t.tco * t.tpx / 256.0;
+    const double tt = rounds * wg;
+    if (best < 0 || tt < best_t) {
+      best = ti;
+      best_t = tt;
+    }
+  }
+  return best;
 }
 
 void plan_split_k(conv_plan* p) {
@@ -325,9 +343,9 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
     const long nwg = (long)(p->g.cout / t.tco) * ((p->g.m + t.tpx - 1) / t.tpx);
     std::snprintf(buf, len,
                   "igemm_xl dtype=%s out=%s loader=%s tile=%d co%dxpx%d waves=2x2 wgs=%ld m=%d k=%d ksplit=%d "
-                  "kernel=igemm_xl_kernel<%d, %d, %d, %d, %d>",
+                  "kernel=igemm_xl_kernel<%d, %d, %d, %d>",
                   kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], kAlgoXl + p->tile, t.tco, t.tpx, nwg,
-                  p->g.m, p->g.k, p->ksplit, p->in_esz, t.tco, t.tpx, p->loader, xl_sets(p->tile));
+                  p->g.m, p->g.k, p->ksplit, p->in_esz, t.tco, t.tpx, p->loader);
   } else if (p->path == PATH_PATCH) {
     const int s = p->g.sh, bh = s == 1 ? 16 : 8, cb = patch_cb(p->g, p->in_esz);
     std::snprintf(buf, len, "patch3x3 dtype=%s out=%s tile=%d stride=%d block=%dx16 cb=%d m=%d k=%d "

@@ -38,16 +38,13 @@ const TileCfg kXlTiles[kNumXlTiles] = {
     {256, 256, 2, 2},  // 128x128 per wave
     {256, 128, 2, 2},  // 128x64 per wave
     {128, 256, 2, 2},  // 64x128 per wave (Cout = 128)
+    {256, 224, 2, 2},  // 128x112 per wave: fills a few more CUs than 256x256
+    {128, 224, 2, 2},  // 64x112 per wave
+    {256, 160, 2, 2},  // 128x80 per wave
 };
 
 namespace {
 
-#ifndef XL_SETS
-#define XL_SETS 2
-#endif
-#ifndef XL_FETCH_MODE
-#define XL_FETCH_MODE 0
-#endif
 
 struct XlArgs {
   const char* x;
@@ -107,7 +104,7 @@ __device__ __forceinline__ void agpr_guard(T& c) {
   asm volatile("s_nop 4" : "+a"(c));
 }
 
-template <int ESZ, int TCO, int TPX, int LOADER, int G>
+template <int ESZ, int TCO, int TPX, int LOADER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void igemm_xl_kernel(XlArgs a) {
   constexpr int FCO = TCO / 32;  // 16-row fragments per wave (2x2 waves)
   constexpr int FPX = TPX / 32;
@@ -370,16 +367,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   });
 }
 
-// Register sets of global prefetch: two where the registers allow it.
-template <int TCO, int TPX>
-constexpr int kXlSets = TCO + TPX > 384 ? 1 : XL_SETS;  // xl_sets() states the same rule
-
 template <int ESZ, int TCO, int TPX>
 hipError_t launch_cfg(int loader, const XlArgs& args, dim3 grid, hipStream_t s) {
   if (loader == LOAD_TAP)
-    hipLaunchKernelGGL((igemm_xl_kernel<ESZ, TCO, TPX, LOAD_TAP, kXlSets<TCO, TPX>>), grid, dim3(256), 0, s, args);
+    hipLaunchKernelGGL((igemm_xl_kernel<ESZ, TCO, TPX, LOAD_TAP>), grid, dim3(256), 0, s, args);
   else
-    hipLaunchKernelGGL((igemm_xl_kernel<ESZ, TCO, TPX, LOAD_1X1, kXlSets<TCO, TPX>>), grid, dim3(256), 0, s, args);
+    hipLaunchKernelGGL((igemm_xl_kernel<ESZ, TCO, TPX, LOAD_1X1>), grid, dim3(256), 0, s, args);
   return hipGetLastError();
 }
 
@@ -388,13 +381,14 @@ hipError_t launch_esz(int tile, int loader, const XlArgs& args, dim3 grid, hipSt
   switch (tile) {
     case 0: return launch_cfg<ESZ, 256, 256>(loader, args, grid, s);
     case 1: return launch_cfg<ESZ, 256, 128>(loader, args, grid, s);
-    default: return launch_cfg<ESZ, 128, 256>(loader, args, grid, s);
+    case 2: return launch_cfg<ESZ, 128, 256>(loader, args, grid, s);
+    case 3: return launch_cfg<ESZ, 256, 224>(loader, args, grid, s);
+    case 4: return launch_cfg<ESZ, 128, 224>(loader, args, grid, s);
+    default: return launch_cfg<ESZ, 256, 160>(loader, args, grid, s);
   }
 }
 
 }  // namespace
-
-int xl_sets(int tile) { return kXlTiles[tile].tco + kXlTiles[tile].tpx > 384 ? 1 : XL_SETS; }
 
 bool xl_eligible(const Geometry& g, int esz, int loader, int tile) {
   if (loader != LOAD_TAP && loader != LOAD_1X1) return false;

@@ -40,7 +40,7 @@ extern const TileCfg kTiles[kNumTiles];  // index = algo - 1
 
 // Tile configurations of the large-layer kernel; desc.algo kAlgoXl + i forces
 // configuration i.
-constexpr int kNumXlTiles = 3;
+constexpr int kNumXlTiles = 6;
 constexpr int kAlgoXl = kAlgoPatch + 1;
 constexpr int kAlgoLast = kAlgoXl + kNumXlTiles - 1;
 extern const TileCfg kXlTiles[kNumXlTiles];
@@ -76,7 +76,6 @@ namespace convnhwc {
 hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                         hipStream_t s);
 bool xl_eligible(const Geometry& g, int esz, int loader, int tile);
-int xl_sets(int tile);  // register sets of global prefetch of XL tile configuration `tile`
 int igemm_stages(int loader, int tile);  // register stages of the implicit-GEMM kernel
 hipError_t launch_xl(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);
 hipError_t launch_smallk(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,

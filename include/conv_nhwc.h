@@ -105,7 +105,7 @@ typedef struct conv_desc {
                              k > 0 forces one kernel configuration of a
                              dense bf16/int8 layer (for tests and tuning):
                              1..10 the implicit-GEMM tiles, 11 the 3x3
-                             halo-patch kernel, 12..14 the large-layer
+                             halo-patch kernel, 12 and up the large-layer
                              kernel's tiles (conv_describe names the one
                              chosen). A configuration that cannot run the
                              layer gives CONV_E_UNSUPPORTED. */

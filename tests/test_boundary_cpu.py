@@ -101,12 +101,13 @@ def test_prepare_null():
     (dict(c_in=4, c_out=4, groups=4, dtype="f32", stride=(2, 2)), "dw3x3 dtype=f32 out=f32 loader=vec16"),
     (dict(c_in=6, c_out=6, groups=6, dtype="bf16"), "dw3x3 dtype=bf16 out=bf16 loader=generic"),
     # long reductions over 128-byte channel blocks: the large-layer kernel
-    (dict(n=16, h=40, w=40, c_in=512, c_out=512, dtype="bf16"), "igemm_xl dtype=bf16 out=bf16 loader=tap tile=12"),
-    (dict(n=16, h=20, w=20, c_in=512, c_out=1024, dtype="bf16"), "igemm_xl dtype=bf16 out=bf16 loader=tap tile=13"),
-    (dict(n=16, h=40, w=40, c_in=512, c_out=512, dtype="i8"), "igemm_xl dtype=i8 out=i8 loader=tap tile=12"),
-    (dict(n=16, h=80, w=80, c_in=256, c_out=256, dtype="i8"), "igemm dtype=i8 out=i8 loader=tap tile=4"),  # short K
+    (dict(n=16, h=40, w=40, c_in=512, c_out=512, dtype="bf16"), "igemm_xl dtype=bf16 out=bf16 loader=tap tile=15"),
+    (dict(n=16, h=20, w=20, c_in=512, c_out=1024, dtype="bf16"), "igemm_xl dtype=bf16 out=bf16 loader=tap tile=16"),
+    (dict(n=16, h=40, w=40, c_in=512, c_out=512, dtype="i8"), "igemm_xl dtype=i8 out=i8 loader=tap tile=15"),
+    (dict(n=16, h=80, w=80, c_in=256, c_out=256, dtype="i8"), "igemm_xl dtype=i8 out=i8 loader=tap tile=15"),
+    (dict(n=16, h=80, w=80, c_in=128, c_out=128, dtype="i8"), "igemm dtype=i8 out=i8 loader=tap"),  # short K, 128 channels
     (dict(n=16, h=160, w=160, c_in=128, c_out=128, dtype="bf16"), "loader=tap tile=4 co128xpx128"),
-    (dict(n=16, h=40, w=40, c_in=512, c_out=384, dtype="bf16"), "igemm dtype=bf16"),  # Cout % 256
+    (dict(n=16, h=40, w=40, c_in=512, c_out=320, dtype="bf16"), "igemm dtype=bf16"),  # Cout % 128
 ])
 def test_path_selection(layer, expect):
     args = dict(n=1, h=16, w=16, kh=3, kw=3, stride=(1, 1), pad=(1, 1), groups=1, act="relu")
