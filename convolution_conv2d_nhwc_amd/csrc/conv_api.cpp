@@ -54,13 +54,6 @@ int choose_tile(const Geometry& g, int esz) {
   return t64x64;
 }
 
-// Split the reduction when the output tiles alone would fill fewer than half
-// of the 256 CUs and each split still has >= 8 K-tiles of 128 bytes: aim at
-// ~512 workgroups, at most 8 splits. The splits' raw partial sums go to a device
-// workspace owned by the plan; a second kernel adds them in split order and
-// applies the epilogue. If the workspace cannot be allocated (no device, out
-// of memory) the plan runs unsplit, which is slower but the same arithmetic
-// up to the order of the fp32 additions.
 // The large-layer kernel for long reductions over 128-byte channel blocks.
 // One workgroup fills a CU (its LDS), so a configuration's time is its number
 // of rounds of 256 workgroups times one workgroup's time, modelled per K-tile
@@ -95,6 +88,13 @@ int choose_xl(const Geometry& g, int esz, int loader) {
   return best;
 }
 
+// Split the reduction when the output tiles alone would fill fewer than half
+// of the 256 CUs and each split still has >= 8 K-tiles of 128 bytes: aim at
+// ~512 workgroups, at most 8 splits. The splits' raw partial sums go to a device
+// workspace owned by the plan; a second kernel adds them in split order and
+// applies the epilogue. If the workspace cannot be allocated (no device, out
+// of memory) the plan runs unsplit, which is slower but the same arithmetic
+// up to the order of the fp32 additions.
 void plan_split_k(conv_plan* p) {
   const Geometry& g = p->g;
   const TileCfg& t = p->path == PATH_XL ? kXlTiles[p->tile] : kTiles[p->tile];
@@ -188,7 +188,13 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
     path = PATH_DW;
     loader = (d->c_in * in_esz) % 16 == 0 ? LOAD_VEC : LOAD_GENERIC;
   }
-  if (d->algo != 0 && (path != PATH_IGEMM || d->algo < 1 || d->algo > kAlgoLast)) return CONV_E_UNSUPPORTED;
+  if (path == PATH_DW) {
+    // algo 1..4 forces 1, 2, 4 or 8 rows per lane of the row-window kernels
+    const bool rows = d->stride_h == 1 && d->stride_w == 1 && d->c_in % 4 == 0;
+    if (d->algo != 0 && (!rows || d->algo < 1 || d->algo > 4)) return CONV_E_UNSUPPORTED;
+  } else if (d->algo != 0 && (path != PATH_IGEMM || d->algo < 1 || d->algo > kAlgoLast)) {
+    return CONV_E_UNSUPPORTED;
+  }
   // A short reduction over an odd channel count (the 3-channel and 1-channel
   // stems) goes to the LDS-free small-K kernel unless a tile is forced.
   if (path == PATH_IGEMM && loader == LOAD_GENERIC && d->algo == 0 &&
@@ -248,6 +254,7 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
   p->tile = path == PATH_IGEMM ? (d->algo ? d->algo - 1 : choose_tile(g, in_esz))
             : path == PATH_XL && d->algo == 0 ? p->tile
             : path == PATH_XL  ? d->algo - kAlgoXl
+            : path == PATH_DW && d->algo ? 1 << (d->algo - 1)
                                : 0;
   if (path == PATH_IGEMM && loader == LOAD_GENERIC && (kTiles[p->tile].tco > 256 || kTiles[p->tile].tpx > 256)) {
     delete p;  // the element-wise gather needs a thread per tile row
@@ -364,10 +371,15 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
     // output kind (the int32 checkpoint or not; also 2 for float layers)
     const int act = p->out_kind == OUT_I32 && p->d.act != CONV_ACT_RELU ? CONV_ACT_NONE : p->d.act;
     const int ok = p->out_kind == OUT_I32 ? OUT_I32 : OUT_I8;
-    if (th)
+    const int pf = dw_prefetch_rows();
+    if (th && p->in_esz == 1)
       std::snprintf(buf, len,
-                    "dw3x3 dtype=%s out=%s stride=%dx%d rows kernel=dw3x3_rows_kernel<%s, %d, %d, %d, %d, %d>",
-                    kDt[p->d.dtype], kDt[p->d.out_dtype], p->g.sh, p->g.sw, kT[p->in_esz], ve, pw, th, act, ok);
+                    "dw3x3 dtype=%s out=%s stride=%dx%d rows dot4 kernel=dw3x3_i8_kernel<%d, %d, %d, %d, %d>",
+                    kDt[p->d.dtype], kDt[p->d.out_dtype], p->g.sh, p->g.sw, pw, th, act, ok, pf);
+    else if (th)
+      std::snprintf(buf, len,
+                    "dw3x3 dtype=%s out=%s stride=%dx%d rows kernel=dw3x3_rows_kernel<%s, %d, %d, %d, %d, %d, %d>",
+                    kDt[p->d.dtype], kDt[p->d.out_dtype], p->g.sh, p->g.sw, kT[p->in_esz], ve, pw, th, act, ok, pf);
     else
       std::snprintf(buf, len, "dw3x3 dtype=%s out=%s loader=%s stride=%dx%d kernel=dw3x3_kernel<%s, %d, %d, %d, %d>",
                     kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], p->g.sh, p->g.sw, kT[p->in_esz], ve,

@@ -40,6 +40,21 @@ __device__ __forceinline__ float mish_f32(float v) {
   return v * (n * __builtin_amdgcn_rcpf(n + 2.0f));
 }
 
+// Mish for outputs that are rounded to bf16 or to an integer afterwards, in
+// seven instructions (two of them transcendental) instead of nine: the same
+// function written as v - 2v / ((1 + e^v)^2 + 1), the section 9 form. No
+// clamp is needed: e^v = inf gives v, e^v = 0 gives 0. For v < 0 the
+// subtraction loses relative accuracy (the absolute error stays about
+// |v| * 2^-22), which is far below the rounding of a bf16 output at the scale
+// of its layer, and an int8 output never rounds near there (|Mish(v)| < 0.31
+// for v < 0). For v > 0 the quotient is at most 0.2 and there is no
+// cancellation.
+__device__ __forceinline__ float mish_lo(float v) {
+  const float u = __builtin_amdgcn_exp2f(v * 1.44269504088896341f) + 1.0f;
+  const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(u, u, 1.0f));
+  return __builtin_fmaf(-2.0f * v, r, v);
+}
+
 __device__ __forceinline__ float apply_act(float v, int act) {
   switch (act) {
     case ACT_RELU: return fmaxf(v, 0.0f);
@@ -90,11 +105,36 @@ __device__ __forceinline__ float act_t(float v) {
     return v;
 }
 
+// act_t with mish_lo: for bf16 and int8 outputs
+template <int ACT>
+__device__ __forceinline__ float act_lo_t(float v) {
+  if constexpr (ACT == ACT_MISH)
+    return mish_lo(v);
+  else
+    return act_t<ACT>(v);
+}
+
+// The int8 requantisation with the activation fixed at compile time. The
+// saturation comes first (the bounds are integers, so clamping before or
+// after rounding is the same); adding 1.5 * 2^23 then rounds half to even in
+// the adder and leaves the integer in the low mantissa bits. The low byte of
+// the returned word is the int8 result (two's complement); requant_i8_t
+// gives it as an int.
+template <int ACT>
+__device__ __forceinline__ uint32_t requant_i8_word_t(int r, float s) {
+  const float v = __fmul_rn((float)r, s);
+  float c;  // the activation and the saturation, one clamp where they merge
+  if constexpr (ACT == ACT_RELU)
+    c = __builtin_amdgcn_fmed3f(v, 0.0f, 127.0f);
+  else if constexpr (ACT == ACT_RELU6)
+    c = __builtin_amdgcn_fmed3f(v, 0.0f, 6.0f);
+  else
+    c = __builtin_amdgcn_fmed3f(act_lo_t<ACT>(v), -127.0f, 127.0f);
+  return __builtin_bit_cast(uint32_t, c + 12582912.0f);
+}
 template <int ACT>
 __device__ __forceinline__ int requant_i8_t(int r, float s) {
-  const float v = __fmul_rn((float)r, s);
-  const float m = act_t<ACT>(v);
-  return (int)fminf(fmaxf(__builtin_rintf(m), -127.0f), 127.0f);
+  return (int)(requant_i8_word_t<ACT>(r, s) - 0x4B400000u);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {

@@ -21,6 +21,19 @@
 #include "device_common.h"
 #include "plan.h"
 
+// Lane shape of the row-window kernels (timed on the depthwise probe on
+// MI355X): input rows in flight per lane, bf16 output columns per lane, and
+// the lane count (per CU) below which a lane walks fewer rows.
+#ifndef DW_PF
+#define DW_PF 2
+#endif
+#ifndef DW_BF16_PW
+#define DW_BF16_PW 2
+#endif
+#ifndef DW_MIN_LANES_PER_CU
+#define DW_MIN_LANES_PER_CU 256
+#endif
+
 namespace convnhwc {
 namespace {
 
@@ -35,6 +48,7 @@ struct DwArgs {
   int wgrp;    // pixel groups per output row
   long total;  // threads doing work
   int x_bytes;
+  int y_bytes;
 };
 
 // Element loads/stores for the three input types, widened to the
@@ -196,7 +210,7 @@ __global__ __launch_bounds__(256) void dw3x3_kernel(DwArgs a) {
           uint32_t wd[4] = {0, 0, 0, 0};
 #pragma unroll
           for (int e = 0; e < VE; ++e)
-            wd[e >> 2] |= ((uint32_t)requant_i8_t<ACT>(rv[e], a.e.scale[c0 + e]) & 0xffu) << (8 * (e & 3));
+            wd[e >> 2] |= (requant_i8_word_t<ACT>(rv[e], a.e.scale[c0 + e]) & 0xffu) << (8 * (e & 3));
           *reinterpret_cast<i32x4*>(yp) = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
         } else {
 #pragma unroll
@@ -207,7 +221,8 @@ __global__ __launch_bounds__(256) void dw3x3_kernel(DwArgs a) {
       float v[VE];
 #pragma unroll
       for (int e = 0; e < VE; ++e)
-        v[e] = act_t<ACT>(acc[p][e] + (a.e.bias ? a.e.bias[c0 + e] : 0.0f));
+        v[e] = (sizeof(T) == 4 ? act_t<ACT>(acc[p][e] + (a.e.bias ? a.e.bias[c0 + e] : 0.0f))
+                               : act_lo_t<ACT>(acc[p][e] + (a.e.bias ? a.e.bias[c0 + e] : 0.0f)));
       if constexpr (sizeof(T) == 4) {
         float* yp = reinterpret_cast<float*>(a.y) + off;
         if constexpr (VE == 4) {
@@ -239,16 +254,35 @@ __global__ __launch_bounds__(256) void dw3x3_kernel(DwArgs a) {
 // input rows it needs sit in registers already widened to the accumulator
 // type, each new input row is loaded (PW+2 vectors) and widened once, and the
 // next row's loads are in flight during the current row's multiply-adds, so
-// memory latency overlaps arithmetic. The lane shapes
-// (channels, columns, rows) were chosen by timing the depthwise probe on
-// MI355X: bf16 4x2x8, int8 4x4x4, fp32 4x2x8. Loads are buffer loads: rows and
-// columns outside the image read zero (the zero padding). Weights are widened
-// once per lane.
+// memory latency overlaps arithmetic. Loads and stores are buffer accesses
+// with 32-bit offsets: rows and columns outside the image read zero (the
+// zero padding) and stores past the last column are dropped. Weights are
+// widened once per lane and the accumulators start at the bias.
+//
+// Per output element the work is 9 multiply-adds, the activation and the
+// conversion, against 2 (bf16) or 1 (int8) bytes of HBM traffic each way, so
+// on MI355X these kernels are bounded by vector-ALU issue about as much as by
+// HBM (Mish alone is two transcendental and seven plain operations): the
+// kernels therefore minimise operations per output, not only bytes.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dw_rsrc(const void* p, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
 constexpr uint32_t kDwOOB = 0x80000000u;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Buffer offsets as a row part plus a column part, each 2^31 or more when its
+// row or column lies outside the image (or past the output's last column).
+// Their saturating sum is then out of range whenever either part is, and the
+// exact offset otherwise (every valid offset is below 2^31): one instruction
+// per access instead of a select.
+__device__ __forceinline__ uint32_t dw_add_sat(uint32_t a, uint32_t b) { return __builtin_elementwise_add_sat(a, b); }
+__device__ __forceinline__ uint32_t dw_col_off(int wi, const Geometry& g, int cbyte0, int esz) {
+  return (unsigned)wi < (unsigned)g.w ? (uint32_t)(wi * g.c * esz + cbyte0) : kDwOOB;
+}
+__device__ __forceinline__ uint32_t dw_row_off(int hi, int n, const Geometry& g, int rowbytes) {
+  return (unsigned)hi < (unsigned)g.h ? (uint32_t)((n * g.h + hi) * rowbytes) : kDwOOB;
+}
 
 // raw vector of VE elements of T
 template <typename T, int VE>
@@ -289,48 +323,75 @@ __device__ __forceinline__ typename Elt<T>::acc_t widen_word(uint32_t wd, int e)
   }
 }
 
-template <typename T, int VE, int PW, int TH, int ACT, int OUT>
+// two floats to a packed pair of bf16 (round to nearest even), one instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 h = __builtin_convertvector((f32x2{lo, hi}), bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Lane decomposition shared by the row-window kernels: channel vector
+// fastest, then the group of PW columns, then the block of TH rows, then the
+// image.
+struct DwLane {
+  int c0, wo0, ho0, n;
+};
+// 32-bit arithmetic: the lane count is below the output's element count,
+// itself below 2^31.
+template <int VE, int PW, int TH>
+__device__ __forceinline__ DwLane dw_lane(const DwArgs& a, uint32_t t) {
+  const Geometry& g = a.g;
+  DwLane l;
+  const uint32_t cv = (uint32_t)a.cv, wgrp = (uint32_t)a.wgrp, nhb = (uint32_t)((g.ho + TH - 1) / TH);
+  uint32_t r = t / cv;
+  l.c0 = (int)(t - r * cv) * VE;
+  uint32_t r2 = r / wgrp;
+  l.wo0 = (int)(r - r2 * wgrp) * PW;
+  r = r2 / nhb;
+  l.ho0 = (int)(r2 - r * nhb) * TH;
+  l.n = (int)r;
+  return l;
+}
+
+template <typename T, int VE, int PW, int TH, int ACT, int OUT, int PF>
 __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
   typedef typename Elt<T>::acc_t acc_t;
   constexpr int ESZ = sizeof(T);
   constexpr int PER = 4 / ESZ;  // elements per 32-bit word
   constexpr int NC = PW + 2;    // input columns per row
-  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= a.total) return;
+  static_assert(ESZ != 1 || OUT == OUT_I8 || OUT == OUT_I32, "int8 output kinds");
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  if (t >= (uint32_t)a.total) return;
   const Geometry& g = a.g;
-  const int cvi = (int)(t % a.cv);
-  long r = t / a.cv;
-  const int wgi = (int)(r % a.wgrp);
-  r /= a.wgrp;
-  const int nhb = (g.ho + TH - 1) / TH;
-  const int hb = (int)(r % nhb);
-  const int n = (int)(r / nhb);
-  const int c0 = cvi * VE;
-  const int wo0 = wgi * PW;
-  const int ho0 = hb * TH;
+  const DwLane l = dw_lane<VE, PW, TH>(a, t);
+  const int c0 = l.c0, wo0 = l.wo0, ho0 = l.ho0, n = l.n;
   const __amdgpu_buffer_rsrc_t rx = dw_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t ry = dw_rsrc(a.y, a.y_bytes);
 
+  // the 9 * VE weights of this lane's channels are contiguous ([VE][3][3])
+  // and 4-byte aligned (VE * 9 * ESZ is a multiple of 4): whole-word loads
+  static_assert(VE * 9 * ESZ % 4 == 0, "weight block of whole words");
+  constexpr int WW = VE * 9 * ESZ / 4;
+  uint32_t wraw[WW];
+  const uint32_t* wp = reinterpret_cast<const uint32_t*>(a.w + (size_t)c0 * 9 * ESZ);
+#pragma unroll
+  for (int q = 0; q < WW; ++q) wraw[q] = wp[q];
   acc_t wr[VE][9];
 #pragma unroll
   for (int e = 0; e < VE; ++e)
 #pragma unroll
-    for (int q = 0; q < 9; ++q) wr[e][q] = Elt<T>::get1(a.w + ((size_t)(c0 + e) * 9 + q) * ESZ);
+    for (int q = 0; q < 9; ++q) wr[e][q] = widen_word<T>(wraw[(e * 9 + q) / PER], e * 9 + q);
 
   // byte offsets of this lane's input columns within one input row
   const int rowbytes = g.w * g.c * ESZ;
   uint32_t coff[NC];
-  bool cok[NC];
 #pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    const int wi = wo0 - g.pw + j;
-    cok[j] = (unsigned)wi < (unsigned)g.w;
-    coff[j] = (uint32_t)((wi * g.c + c0) * ESZ);
-  }
+  for (int j = 0; j < NC; ++j) coff[j] = dw_col_off(wo0 - g.pw + j, g, c0 * ESZ, ESZ);
   auto fetch_row = [&](int hi, RawVec<T, VE> (&raw)[NC]) {
-    const bool rok = (unsigned)hi < (unsigned)g.h;
-    const uint32_t rbase = (uint32_t)((n * g.h + hi) * rowbytes);
+    const uint32_t rb = dw_row_off(hi, n, g, rowbytes);
 #pragma unroll
-    for (int j = 0; j < NC; ++j) raw[j] = load_raw<T, VE>(rx, (rok && cok[j]) ? rbase + coff[j] : kDwOOB);
+    for (int j = 0; j < NC; ++j) raw[j] = load_raw<T, VE>(rx, dw_add_sat(rb, coff[j]));
   };
   auto widen_row = [&](const RawVec<T, VE> (&raw)[NC], acc_t (&row)[NC][VE]) {
 #pragma unroll
@@ -339,43 +400,51 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
       for (int e = 0; e < VE; ++e) row[j][e] = widen_word<T>(raw[j].w[e / PER], e);
   };
 
+  // window rows in registers, widened; the next PF input rows in flight
   acc_t rows[3][NC][VE];
-  RawVec<T, VE> nxt[NC];
+  RawVec<T, VE> nxt[PF][NC];
   {
     const int hi0 = ho0 - g.ph;
-    fetch_row(hi0, nxt);
-    widen_row(nxt, rows[0]);
-    fetch_row(hi0 + 1, nxt);
-    widen_row(nxt, rows[1]);
-    fetch_row(hi0 + 2, nxt);
+    fetch_row(hi0, nxt[0]);
+    widen_row(nxt[0], rows[0]);
+    fetch_row(hi0 + 1, nxt[0]);
+    widen_row(nxt[0], rows[1]);
+#pragma unroll
+    for (int f = 0; f < PF && f < TH; ++f) fetch_row(hi0 + 2 + f, nxt[f]);
   }
 
-  float bsf[VE];
-  int bsi[VE];
+  acc_t bias[VE];
   float scl[VE];
 #pragma unroll
   for (int e = 0; e < VE; ++e) {
     if constexpr (ESZ == 1) {
-      bsi[e] = a.e.ibias ? a.e.ibias[c0 + e] : 0;
-      scl[e] = a.e.scale ? a.e.scale[c0 + e] : 0.f;
+      bias[e] = a.e.ibias ? a.e.ibias[c0 + e] : 0;
+      scl[e] = OUT == OUT_I8 ? a.e.scale[c0 + e] : 0.f;
     } else {
-      bsf[e] = a.e.bias ? a.e.bias[c0 + e] : 0.f;
+      bias[e] = a.e.bias ? a.e.bias[c0 + e] : 0.f;
     }
   }
+  // byte offset of (ho0, wo0, c0) in y; one row further is wo * cout
+  const int out_esz = ESZ == 1 ? (OUT == OUT_I32 ? 4 : 1) : ESZ;
+  uint32_t yoff = (uint32_t)((((n * g.ho + ho0) * g.wo + wo0) * g.cout + c0) * out_esz);
+  const uint32_t yrow = (uint32_t)(g.wo * g.cout * out_esz);
+  uint32_t poff[PW];  // output column p, or out of range past the last column
+#pragma unroll
+  for (int p = 0; p < PW; ++p) poff[p] = wo0 + p < g.wo ? (uint32_t)(p * g.cout * out_esz) : kDwOOB;
 
 #pragma unroll
   for (int i = 0; i < TH; ++i) {
     const int ho = ho0 + i;
     if (ho >= g.ho) break;
-    // the row loaded last becomes window row (i + 2) % 3, then the next
-    // row's loads go out before this row's multiply-adds
-    widen_row(nxt, rows[(i + 2) % 3]);
-    if (i + 1 < TH) fetch_row(ho - g.ph + 3, nxt);
+    // input row ho - ph + 2 becomes window row (i + 2) % 3, then the loads
+    // of the row PF further go out before this row's multiply-adds
+    widen_row(nxt[i % PF], rows[(i + 2) % 3]);
+    if (i + PF < TH) fetch_row(ho - g.ph + 2 + PF, nxt[i % PF]);
     acc_t acc[PW][VE];
 #pragma unroll
     for (int p = 0; p < PW; ++p)
 #pragma unroll
-      for (int e = 0; e < VE; ++e) acc[p][e] = 0;
+      for (int e = 0; e < VE; ++e) acc[p][e] = bias[e];
 #pragma unroll
     for (int kh = 0; kh < 3; ++kh)
 #pragma unroll
@@ -384,55 +453,161 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
         for (int p = 0; p < PW; ++p)
 #pragma unroll
           for (int e = 0; e < VE; ++e) acc[p][e] += rows[(i + kh) % 3][p + kw][e] * wr[e][kh * 3 + kw];
-    // fused epilogue, VE channels of PW pixels
+    // fused epilogue, VE channels of PW pixels; columns past the edge drop
 #pragma unroll
     for (int p = 0; p < PW; ++p) {
-      const int wo = wo0 + p;
-      if (wo >= g.wo) break;
-      const size_t off = ((size_t)(n * g.ho + ho) * g.wo + wo) * g.cout + c0;
+      const uint32_t off = dw_add_sat(yoff, poff[p]);
       if constexpr (ESZ == 1) {
         if constexpr (OUT == OUT_I32) {
-          int32_t* yp = reinterpret_cast<int32_t*>(a.y) + off;
+          int v[VE];
 #pragma unroll
-          for (int e = 0; e < VE; ++e) {
-            int v = acc[p][e] + bsi[e];
-            if constexpr (ACT == ACT_RELU) v = v > 0 ? v : 0;
-            yp[e] = v;
-          }
+          for (int e = 0; e < VE; ++e) v[e] = ACT == ACT_RELU ? max(acc[p][e], 0) : acc[p][e];
+#pragma unroll
+          for (int q = 0; q < VE / 4; ++q)
+            __builtin_amdgcn_raw_buffer_store_b128(i32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]}, ry,
+                                                   (int)(off + 16 * q), 0, 0);
         } else {
           uint32_t wd[VE / 4];
 #pragma unroll
           for (int q = 0; q < VE / 4; ++q) wd[q] = 0;
 #pragma unroll
           for (int e = 0; e < VE; ++e)
-            wd[e >> 2] |= ((uint32_t)requant_i8_t<ACT>(acc[p][e] + bsi[e], scl[e]) & 0xffu) << (8 * (e & 3));
-          if constexpr (VE == 4)
-            *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(a.y) + off) = wd[0];
-          else if constexpr (VE == 8)
-            *reinterpret_cast<uint2*>(reinterpret_cast<int8_t*>(a.y) + off) = uint2{wd[0], wd[1]};
-          else
-            *reinterpret_cast<i32x4*>(reinterpret_cast<int8_t*>(a.y) + off) =
-                i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+            wd[e >> 2] |= (requant_i8_word_t<ACT>(acc[p][e], scl[e]) & 0xffu) << (8 * (e & 3));
+#pragma unroll
+          for (int q = 0; q < VE / 4; ++q) __builtin_amdgcn_raw_buffer_store_b32((int)wd[q], ry, (int)(off + 4 * q), 0, 0);
         }
+      } else if constexpr (ESZ == 4) {
+#pragma unroll
+        for (int q = 0; q < VE / 4; ++q)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              i32x4{__builtin_bit_cast(int, act_t<ACT>(acc[p][4 * q])), __builtin_bit_cast(int, act_t<ACT>(acc[p][4 * q + 1])),
+                    __builtin_bit_cast(int, act_t<ACT>(acc[p][4 * q + 2])), __builtin_bit_cast(int, act_t<ACT>(acc[p][4 * q + 3]))},
+              ry, (int)(off + 16 * q), 0, 0);
       } else {
-        float v[VE];
+        uint32_t wd[VE / 2];
 #pragma unroll
-        for (int e = 0; e < VE; ++e) v[e] = act_t<ACT>(acc[p][e] + bsf[e]);
-        if constexpr (ESZ == 4) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.y) + off) = f32x4{v[0], v[1], v[2], v[3]};
-        } else {
-          uint32_t wd[VE / 2];
-#pragma unroll
-          for (int q = 0; q < VE / 2; ++q)
-            wd[q] = (uint32_t)f32_to_bf16_bits(v[2 * q]) | ((uint32_t)f32_to_bf16_bits(v[2 * q + 1]) << 16);
-          uint16_t* yp = reinterpret_cast<uint16_t*>(a.y) + off;
-          if constexpr (VE == 8)
-            *reinterpret_cast<i32x4*>(yp) = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
-          else
-            *reinterpret_cast<uint2*>(yp) = uint2{wd[0], wd[1]};
-        }
+        for (int q = 0; q < VE / 2; ++q) wd[q] = pack_bf16x2(act_lo_t<ACT>(acc[p][2 * q]), act_lo_t<ACT>(acc[p][2 * q + 1]));
+        if constexpr (VE == 8)
+          __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]}, ry, (int)off, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{wd[0], wd[1]}, ry, (int)off, 0, 0);
       }
     }
+    yoff += yrow;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// int8, stride 1: four channels per lane (one 32-bit word per pixel) and the
+// three window rows of each (column, channel) packed into one word, bytes
+// (row r-2, row r-1, row r, 0). A new row enters every word with one byte
+// permute, and each output then costs one 4-way int8 dot product per kernel
+// column against the word (w[c][0][kw], w[c][1][kw], w[c][2][kw], 0): three
+// instructions for the nine multiply-adds, exact in int32.
+template <int PW, int TH, int ACT, int OUT, int PF>
+__global__ __launch_bounds__(256) void dw3x3_i8_kernel(DwArgs a) {
+  constexpr int NC = PW + 2;
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  if (t >= (uint32_t)a.total) return;
+  const Geometry& g = a.g;
+  const DwLane l = dw_lane<4, PW, TH>(a, t);
+  const int c0 = l.c0, wo0 = l.wo0, ho0 = l.ho0, n = l.n;
+  const __amdgpu_buffer_rsrc_t rx = dw_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t ry = dw_rsrc(a.y, a.y_bytes);
+
+  // weights of channels c0..c0+3 are 36 contiguous bytes ([4][3][3]),
+  // 4-byte aligned because c0 is a multiple of 4
+  uint32_t wb[9];
+  const uint32_t* wp = reinterpret_cast<const uint32_t*>(a.w + (size_t)c0 * 9);
+#pragma unroll
+  for (int q = 0; q < 9; ++q) wb[q] = wp[q];
+  auto wbyte = [&](int i) { return (wb[i >> 2] >> (8 * (i & 3))) & 0xffu; };
+  int wk[3][4];  // wk[kw][e] = (w[e][0][kw], w[e][1][kw], w[e][2][kw], 0)
+#pragma unroll
+  for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      wk[kw][e] = (int)(wbyte(9 * e + kw) | (wbyte(9 * e + 3 + kw) << 8) | (wbyte(9 * e + 6 + kw) << 16));
+
+  const int rowbytes = g.w * g.c;
+  uint32_t coff[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) coff[j] = dw_col_off(wo0 - g.pw + j, g, c0, 1);
+  auto fetch_row = [&](int hi, uint32_t (&raw)[NC]) {
+    const uint32_t rb = dw_row_off(hi, n, g, rowbytes);
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+      raw[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rx, (int)dw_add_sat(rb, coff[j]), 0, 0);
+  };
+  // window words: shift out the oldest row, byte e of the new row's word in
+  // as byte 2 (selector bytes 4..7 pick the first operand, 0..3 the second,
+  // 12 gives zero)
+  uint32_t win[NC][4];
+  auto push_row = [&](const uint32_t (&raw)[NC]) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) win[j][e] = __builtin_amdgcn_perm(win[j][e], raw[j], 0x0C000605u | ((uint32_t)e << 16));
+  };
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) win[j][e] = 0;
+
+  uint32_t nxt[PF][NC];  // the next PF input rows in flight
+  {
+    const int hi0 = ho0 - g.ph;
+    fetch_row(hi0, nxt[0]);
+    push_row(nxt[0]);
+    fetch_row(hi0 + 1, nxt[0]);
+    push_row(nxt[0]);
+#pragma unroll
+    for (int f = 0; f < PF && f < TH; ++f) fetch_row(hi0 + 2 + f, nxt[f]);
+  }
+  int bias[4];
+  float scl[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bias[e] = a.e.ibias ? a.e.ibias[c0 + e] : 0;
+    scl[e] = OUT == OUT_I8 ? a.e.scale[c0 + e] : 0.f;
+  }
+  const int out_esz = OUT == OUT_I32 ? 4 : 1;
+  uint32_t yoff = (uint32_t)((((n * g.ho + ho0) * g.wo + wo0) * g.cout + c0) * out_esz);
+  const uint32_t yrow = (uint32_t)(g.wo * g.cout * out_esz);
+  uint32_t poff[PW];
+#pragma unroll
+  for (int p = 0; p < PW; ++p) poff[p] = wo0 + p < g.wo ? (uint32_t)(p * g.cout * out_esz) : kDwOOB;
+
+#pragma unroll
+  for (int i = 0; i < TH; ++i) {
+    if (ho0 + i >= g.ho) break;
+    push_row(nxt[i % PF]);
+    if (i + PF < TH) fetch_row(ho0 + i - g.ph + 2 + PF, nxt[i % PF]);
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      int acc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = bias[e];
+#pragma unroll
+        for (int kw = 0; kw < 3; ++kw) acc[e] = __builtin_amdgcn_sdot4((int)win[p + kw][e], wk[kw][e], acc[e], false);
+      }
+      const uint32_t off = dw_add_sat(yoff, poff[p]);
+      if constexpr (OUT == OUT_I32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = ACT == ACT_RELU ? max(acc[e], 0) : acc[e];
+        __builtin_amdgcn_raw_buffer_store_b128(i32x4{acc[0], acc[1], acc[2], acc[3]}, ry, (int)off, 0, 0);
+      } else {
+        uint32_t q[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = requant_i8_word_t<ACT>(acc[e], scl[e]);
+        // low bytes of q0..q3 into one word
+        const uint32_t lo = __builtin_amdgcn_perm(q[1], q[0], 0x0C0C0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(q[3], q[2], 0x0C0C0400u);
+        __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(hi, lo, 0x05040100u), ry, (int)off, 0, 0);
+      }
+    }
+    yoff += yrow;
   }
 }
 
@@ -461,10 +636,24 @@ hipError_t launch_rows_t(const DwArgs& base, hipStream_t s) {
   a.total = (long)a.g.n * ((a.g.ho + TH - 1) / TH) * a.wgrp * a.cv;
   const long blocks = (a.total + 255) / 256;
   return with_act(a.out_kind, a.e.act, [&](auto oc, auto ac) {
-    hipLaunchKernelGGL((dw3x3_rows_kernel<T, VE, PW, TH, decltype(ac)::value, decltype(oc)::value>),
-                       dim3((unsigned)blocks), dim3(256), 0, s, a);
+    if constexpr (sizeof(T) == 1)
+      hipLaunchKernelGGL((dw3x3_i8_kernel<PW, TH, decltype(ac)::value, decltype(oc)::value, DW_PF>),
+                         dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((dw3x3_rows_kernel<T, VE, PW, TH, decltype(ac)::value, decltype(oc)::value, DW_PF>),
+                         dim3((unsigned)blocks), dim3(256), 0, s, a);
     return hipGetLastError();
   });
+}
+
+template <typename T, int VE, int PW>
+hipError_t launch_rows_th(int th, const DwArgs& a, hipStream_t s) {
+  switch (th) {
+    case 8: return launch_rows_t<T, VE, PW, 8>(a, s);
+    case 4: return launch_rows_t<T, VE, PW, 4>(a, s);
+    case 2: return launch_rows_t<T, VE, PW, 2>(a, s);
+    default: return launch_rows_t<T, VE, PW, 1>(a, s);
+  }
 }
 
 template <typename T, int VE, int PW>
@@ -483,7 +672,13 @@ hipError_t launch_dw_t(const DwArgs& base, hipStream_t s) {
 
 }  // namespace
 
-// Lane shape of a depthwise plan: th > 0 selects the sliding-window kernel.
+int dw_prefetch_rows() { return DW_PF; }
+
+// Lane shape of a depthwise plan: th > 0 selects the sliding-window kernels.
+// A lane walks th output rows; th is the largest of 8, 4, 2 that still gives
+// the chip DW_MIN_LANES_PER_CU lanes per CU (fewer rows per lane re-read more
+// input rows from cache and repeat the lane's set-up, too few lanes leave CUs
+// idle), else 1.
 void dw_shape(const conv_plan* p, int* ve, int* pw, int* th) {
   const int c = p->g.c;
   const bool s1 = p->g.sh == 1 && p->g.sw == 1;
@@ -491,8 +686,18 @@ void dw_shape(const conv_plan* p, int* ve, int* pw, int* th) {
   *th = 0;
   if (s1 && c % 4 == 0) {
     *ve = 4;
-    *pw = p->in_esz == 1 ? 4 : 2;
-    *th = p->in_esz == 1 ? 4 : 8;
+    *pw = p->in_esz == 1 ? 4 : p->in_esz == 2 ? DW_BF16_PW : 2;
+    if (p->tile > 0) {
+      *th = p->tile;
+      return;
+    }
+    const long lanes_per_row = (long)p->g.n * ((p->g.wo + *pw - 1) / *pw) * (c / 4);
+    *th = 1;
+    for (int t = 8; t >= 2; t /= 2)
+      if (lanes_per_row * ((p->g.ho + t - 1) / t) >= 256L * DW_MIN_LANES_PER_CU) {
+        *th = t;
+        break;
+      }
     return;
   }
   *ve = vec ? 16 / p->in_esz : 1;
@@ -509,13 +714,14 @@ hipError_t launch_dw(const conv_plan* p, const void* x, const void* w, const Epi
   a.g = p->g;
   a.out_kind = p->out_kind;
   a.x_bytes = (int)p->x_bytes;
+  a.y_bytes = (int)p->y_bytes;
   int ve, pw, th;
   dw_shape(p, &ve, &pw, &th);
   if (th) {
     switch (p->in_esz) {
-      case 4: return launch_rows_t<float, 4, 2, 8>(a, s);
-      case 2: return launch_rows_t<uint16_t, 4, 2, 8>(a, s);
-      default: return launch_rows_t<int8_t, 4, 4, 4>(a, s);
+      case 4: return launch_rows_th<float, 4, 2>(th, a, s);
+      case 2: return launch_rows_th<uint16_t, 4, DW_BF16_PW>(th, a, s);
+      default: return launch_rows_th<int8_t, 4, 4>(th, a, s);
     }
   }
   const bool vec = ve > 1;

@@ -188,7 +188,7 @@ __device__ __forceinline__ void store_quad_t(const acc_t& v, const QuadConsts& q
   if constexpr (ESZ == 2) {
     uint32_t h[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_bits(act_t<ACT>(v[r] + q.bsf[r]));
+    for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_bits(act_lo_t<ACT>(v[r] + q.bsf[r]));
     const u32x2 d = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
     __builtin_amdgcn_raw_buffer_store_b64(d, o.r, in ? idx * 2u : kNowhere, 0, 0);
   } else if constexpr (OUT == OUT_I32) {
@@ -203,7 +203,7 @@ __device__ __forceinline__ void store_quad_t(const acc_t& v, const QuadConsts& q
   } else {
     uint32_t b = 0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) b |= ((uint32_t)requant_i8_t<ACT>(v[r] + q.bsi[r], q.scl[r]) & 0xffu) << (8 * r);
+    for (int r = 0; r < 4; ++r) b |= (requant_i8_word_t<ACT>(v[r] + q.bsi[r], q.scl[r]) & 0xffu) << (8 * r);
     __builtin_amdgcn_raw_buffer_store_b32(b, o.r, in ? idx : kNowhere, 0, 0);
   }
 }

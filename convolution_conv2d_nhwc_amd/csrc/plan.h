@@ -60,7 +60,7 @@ struct conv_plan {
   convnhwc::Geometry g;
   int path;
   int loader;   // PATH_IGEMM
-  int tile;     // PATH_IGEMM: index into kTiles
+  int tile;     // PATH_IGEMM: index into kTiles; PATH_XL: into kXlTiles; PATH_DW: forced rows per lane (0 = chosen)
   int out_kind; // convnhwc::OutKind
   int in_esz, out_esz;
   int64_t x_bytes, w_bytes, y_bytes, b_bytes;
@@ -86,6 +86,7 @@ hipError_t launch_patch(const conv_plan* p, const void* x, const void* w, const 
 bool patch_eligible(const Geometry& g, int esz, int groups);
 int patch_cb(const Geometry& g, int esz);
 void dw_shape(const conv_plan* p, int* ve, int* pw, int* th);
+int dw_prefetch_rows();  // input rows in flight per lane in the row-window kernels
 hipError_t launch_dw(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                      hipStream_t s);
 hipError_t launch_f32(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,

@@ -107,8 +107,11 @@ typedef struct conv_desc {
                              1..10 the implicit-GEMM tiles, 11 the 3x3
                              halo-patch kernel, 12 and up the large-layer
                              kernel's tiles (conv_describe names the one
-                             chosen). A configuration that cannot run the
-                             layer gives CONV_E_UNSUPPORTED. */
+                             chosen). For a depthwise layer with stride 1 and
+                             c_in % 4 == 0, k = 1..4 forces 1, 2, 4 or 8
+                             output rows per lane of the row-window kernel.
+                             A configuration that cannot run the layer gives
+                             CONV_E_UNSUPPORTED. */
 } conv_desc;
 
 typedef struct conv_plan conv_plan;

@@ -151,6 +151,23 @@ def test_forced_algo_and_count():
             Conv2d(1, 20, 20, 48, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=a)  # 96-byte channel blocks
 
 
+def test_depthwise_forced_rows():
+    """algo 1..4 on a stride-1 depthwise layer forces 1, 2, 4, 8 rows per lane
+    of the row-window kernel; other algos, strided layers and channel counts
+    that are not a multiple of 4 are refused."""
+    for a, th in ((1, 1), (2, 2), (3, 4), (4, 8)):
+        for dt, out, pat in (("bf16", None, r"dw3x3_rows_kernel<unsigned short, 4, \d+, %d, "),
+                             ("i8", "i8", r"dw3x3_i8_kernel<\d+, %d, "), ("f32", None, r"dw3x3_rows_kernel<float, 4, \d+, %d, ")):
+            c = Conv2d(1, 9, 9, 16, 16, 3, 3, (1, 1), (1, 1), groups=16, dtype=dt, out_dtype=out, algo=a)
+            assert re.search(pat % th, c.describe()), c.describe()
+            c.close()
+    for kw in (dict(algo=5), dict(algo=1, stride=(2, 2)), dict(algo=1, c=6)):
+        ch = kw.pop("c", 16)
+        st = kw.pop("stride", (1, 1))
+        with pytest.raises(ConvError):
+            Conv2d(1, 9, 9, ch, ch, 3, 3, st, (1, 1), groups=ch, dtype="bf16", **kw)
+
+
 def fake(addr):
     return ctypes.c_void_p(addr)
 

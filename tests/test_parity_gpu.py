@@ -188,6 +188,42 @@ def test_depthwise(layer):
     H.check_layer_full(layer, t["x"], t, y, "%s [%s]" % (layer.name, conv.describe()))
 
 
+# Stride-1 depthwise layers through the row-window kernels with every forced
+# rows-per-lane count (algo 1..4 = 1, 2, 4, 8 rows): output heights that no
+# row count divides, widths ragged against the lane's 2 (bf16, fp32) or 4
+# (int8) columns, both paddings, every int8 output kind.
+DW_ROWS = [
+    L("dwr_bf16_mish", 2, 19, 21, 32, 32, 3, 3, (1, 1), (1, 1), groups=32, act="mish"),
+    L("dwr_bf16_pad0_relu6", 1, 14, 9, 16, 16, 3, 3, (1, 1), (0, 0), groups=16, act="relu6"),
+    L("dwr_i8_mish", 2, 19, 18, 64, 64, 3, 3, (1, 1), (1, 1), groups=64, dtype="i8", out="i8", act="mish"),
+    L("dwr_i8_relu6", 1, 13, 7, 32, 32, 3, 3, (1, 1), (1, 1), groups=32, dtype="i8", out="i8", act="relu6"),
+    L("dwr_i8_i32_relu", 1, 11, 10, 16, 16, 3, 3, (1, 1), (1, 1), groups=16, dtype="i8", out="i32", act="relu"),
+    L("dwr_i8_none_pad0", 1, 12, 13, 8, 8, 3, 3, (1, 1), (0, 0), groups=8, dtype="i8", out="i8", act="none"),
+    L("dwr_f32_mish", 1, 17, 10, 8, 8, 3, 3, (1, 1), (1, 1), groups=8, dtype="f32", act="mish"),
+]
+
+
+@pytest.mark.parametrize("layer", DW_ROWS, ids=[l.name for l in DW_ROWS])
+def test_depthwise_rows_per_lane(layer):
+    t = random_layer_tensors(layer, LAW[layer.dtype], seed=14)
+    ref = H.oracle_full(layer, t["x"], t)
+    xg = t["x"].cuda()
+    for algo, th in ((1, 1), (2, 2), (3, 4), (4, 8)):
+        y, conv = H.gpu_run(layer, xg, t, algo=algo)
+        d = conv.describe()
+        what = "%s algo=%d [%s]" % (layer.name, algo, d)
+        m = re.search(r"kernel=dw3x3_(rows|i8)_kernel<(.*)>", d)
+        assert m, what
+        args = [a.strip() for a in m.group(2).split(",")]
+        assert int(args[3 if m.group(1) == "rows" else 1]) == th, what
+        yc = y.cpu()
+        if layer.dtype == "i8":
+            H.check_int(yc.numpy(), ref, layer, what)
+        else:
+            H.check_float(yc.float().numpy(), ref[0], ref[1], layer.dtype, what)
+        conv.close()
+
+
 F32 = [
     L("f32_mnist_like", 1, 28, 28, 1, 8, 3, 3, (1, 1), (1, 1), dtype="f32", act="relu"),
     L("f32_ragged", 2, 11, 9, 5, 7, 3, 2, (2, 1), (1, 0), dtype="f32", act="mish"),
