@@ -37,6 +37,9 @@
  * The loops are written in the order of the definition; OpenMP only splits
  * independent output rows across threads, which changes no arithmetic.
  *
+ * The file also holds the SPP max-pool block (oracle_spp, defined where it
+ * stands).
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no -ffast-math).
  */
 #include <math.h>
@@ -359,6 +362,73 @@ int oracle_mosaic(const float *tiles, int64_t m, int64_t th, int64_t tw,
             ((float *)canvas)[o + ch] = v;
         }
       }
+  return ORC_OK;
+}
+
+/*
+ * SPP max-pool block (zerolat.eu YOLOv4 report, section 10 kernel table, row
+ * K3: the 5, 9 and 13 spatial max-pool windows of the SPP block; section 3
+ * names SPP as the block that combines local and wider context with those
+ * three windows). Written from the definition of a stride-1 max pool whose
+ * output has the input's size, NOT from the cascade identity the report's
+ * kernel uses:
+ *
+ *   P_k[n,h,w,c] = max { X[n,h',w',c] : |h'-h| <= k/2, |w'-w| <= k/2,
+ *                        0 <= h' < H, 0 <= w' < W }          k = 5, 9, 13
+ *
+ * (positions outside the image never win: padding with -infinity).
+ * Output y[n,h,w, j*C + c], channel blocks j = 0, 1, 2, 3 = P13, P9, P5, X.
+ * dtype 0: float32; 1: bf16 bit patterns, compared as the values they
+ * encode; 2: int8. Values are compared with '>', so of equal values the first
+ * in (h', w') scan order is kept (this matters only for -0 against +0).
+ */
+static double spp_val(const void *x, int dtype, int64_t i) {
+  if (dtype == 0) return ((const float *)x)[i];
+  if (dtype == 1) {
+    uint32_t b = (uint32_t)((const uint16_t *)x)[i] << 16;
+    float f;
+    memcpy(&f, &b, 4);
+    return f;
+  }
+  return ((const int8_t *)x)[i];
+}
+
+static void spp_put(const void *x, int dtype, int64_t src, void *y, int64_t dst) {
+  if (dtype == 0)
+    ((float *)y)[dst] = ((const float *)x)[src];
+  else if (dtype == 1)
+    ((uint16_t *)y)[dst] = ((const uint16_t *)x)[src];
+  else
+    ((int8_t *)y)[dst] = ((const int8_t *)x)[src];
+}
+
+int oracle_spp(const void *x, int dtype, int64_t n, int64_t h, int64_t w, int64_t c, void *y) {
+  if (n <= 0 || h <= 0 || w <= 0 || c <= 0 || dtype < 0 || dtype > 2) return ORC_E_SHAPE;
+  static const int kWin[3] = {13, 9, 5};
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t in = 0; in < n; ++in)
+    for (int64_t ih = 0; ih < h; ++ih)
+      for (int64_t iw = 0; iw < w; ++iw)
+        for (int64_t ic = 0; ic < c; ++ic) {
+          const int64_t out_px = ((in * h + ih) * w + iw) * 4 * c;
+          for (int j = 0; j < 3; ++j) {
+            const int64_t r = kWin[j] / 2;
+            int64_t best = -1;
+            double bv = 0.0;
+            for (int64_t hh = ih - r; hh <= ih + r; ++hh)
+              for (int64_t ww = iw - r; ww <= iw + r; ++ww) {
+                if (hh < 0 || hh >= h || ww < 0 || ww >= w) continue;
+                const int64_t src = ((in * h + hh) * w + ww) * c + ic;
+                const double v = spp_val(x, dtype, src);
+                if (best < 0 || v > bv) {
+                  best = src;
+                  bv = v;
+                }
+              }
+            spp_put(x, dtype, best, y, out_px + j * c + ic);
+          }
+          spp_put(x, dtype, ((in * h + ih) * w + iw) * c + ic, y, out_px + 3 * c + ic);
+        }
   return ORC_OK;
 }
 

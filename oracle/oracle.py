@@ -58,6 +58,8 @@ def _load():
     lib.oracle_conv_i8_at.restype = I
     lib.oracle_mosaic.argtypes = [P] + [I64] * 5 + [I, P]
     lib.oracle_mosaic.restype = I
+    lib.oracle_spp.argtypes = [P, I] + [I64] * 4 + [P]
+    lib.oracle_spp.restype = I
     lib.oracle_mish.argtypes = [ctypes.c_double]
     lib.oracle_mish.restype = ctypes.c_double
     lib.oracle_act.argtypes = [ctypes.c_double, I]
@@ -216,6 +218,25 @@ def mosaic(tiles, c_pad=None, out="bf16"):
     if st:
         raise ValueError("oracle_mosaic failed: %d" % st)
     return canvas
+
+
+_SPP_DT = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1, np.dtype(np.int8): 2}
+
+
+def spp(x):
+    """SPP max-pool block of x [n,h,w,c] (float32, bf16 bit patterns as
+    uint16, or int8): returns [n,h,w,4c] of the same dtype, channel blocks
+    max13, max9, max5, x (see oracle_spp in the C file)."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    if x.dtype not in _SPP_DT or x.ndim != 4:
+        raise ValueError("spp takes a 4-d float32, uint16 (bf16) or int8 array")
+    n, h, w, c = x.shape
+    y = np.empty((n, h, w, 4 * c), x.dtype)
+    st = lib.oracle_spp(_ptr(x), _SPP_DT[x.dtype], n, h, w, c, _ptr(y))
+    if st:
+        raise ValueError("oracle_spp failed: %d" % st)
+    return y
 
 
 def mish(x: float) -> float:

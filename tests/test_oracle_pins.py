@@ -378,3 +378,62 @@ def test_requant_elementwise_matches_conv_path():
         exp = np.array([oracle.requant(int(v), float(s[i % 3]), act)[0]
                         for i, v in enumerate(r32.reshape(-1))]).reshape(q.shape)
         assert np.array_equal(q, exp)
+
+
+# ---------------------------------------------------------------- SPP ------
+# The SPP oracle is pinned to a library routine (torch's max_pool2d in
+# float64, stride 1, padding k // 2, which pads with -infinity), to a closed
+# form (one peak on a flat background spreads to exactly the k x k square
+# around it, clipped at the borders) and to the ordering of nested windows.
+
+def _bf16_bits(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _bits_to_f64(b):
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("shape", [(2, 9, 11, 5), (1, 20, 20, 16), (1, 3, 7, 4), (1, 1, 1, 3), (1, 16, 5, 2)])
+def test_spp_matches_torch_max_pool(dtype, shape):
+    rng = np.random.default_rng(hash((dtype, shape)) % 2 ** 32)
+    if dtype == "i8":
+        x = rng.integers(-127, 128, shape).astype(np.int8)
+        xf = x.astype(np.float64)
+    elif dtype == "bf16":
+        x = _bf16_bits(rng.standard_normal(shape) * 0.5)
+        xf = _bits_to_f64(x)
+    else:
+        x = rng.standard_normal(shape).astype(np.float32)
+        xf = x.astype(np.float64)
+    y = oracle.spp(x)
+    yf = y.astype(np.float64) if dtype != "bf16" else _bits_to_f64(y)
+    c = shape[3]
+    t = torch.from_numpy(xf).permute(0, 3, 1, 2)
+    for j, k in enumerate((13, 9, 5)):
+        ref = F.max_pool2d(t, k, stride=1, padding=k // 2).permute(0, 2, 3, 1).numpy()
+        assert np.array_equal(yf[..., j * c:(j + 1) * c], ref), (dtype, shape, k)
+    assert np.array_equal(y[..., 3 * c:], x)
+
+
+@pytest.mark.parametrize("h0,w0", [(0, 0), (3, 8), (10, 2), (6, 6)])
+def test_spp_single_peak_closed_form(h0, w0):
+    h, w = 11, 13
+    x = np.full((1, h, w, 2), -1.0, np.float32)
+    x[0, h0, w0, 1] = 5.0
+    y = oracle.spp(x)
+    for j, k in enumerate((13, 9, 5)):
+        r = k // 2
+        exp = np.full((h, w), -1.0)
+        exp[max(0, h0 - r):h0 + r + 1, max(0, w0 - r):w0 + r + 1] = 5.0
+        assert np.array_equal(y[0, :, :, 2 * j + 1], exp), k
+        assert np.all(y[0, :, :, 2 * j] == -1.0)
+
+
+def test_spp_nested_windows_are_ordered():
+    x = np.random.default_rng(3).integers(-127, 128, (2, 13, 10, 8)).astype(np.int8)
+    y = oracle.spp(x).astype(np.int32)
+    p13, p9, p5, x0 = (y[..., 8 * j:8 * (j + 1)] for j in range(4))
+    assert np.all(p13 >= p9) and np.all(p9 >= p5) and np.all(p5 >= x0)
+    assert np.array_equal(x0, x.astype(np.int32))
