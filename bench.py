@@ -361,7 +361,49 @@ def secondary_measurements():
             torch.cuda.empty_cache()
         out[name] = {"layers": rows, "total_us": round(tot_us, 2),
                      "tflops": round(tot_flop / (tot_us * 1e-6) / 1e12, 2)}
+    out["spp_bf16"] = spp_measurements(gen)
     return out
+
+
+def spp_measurements(gen):
+    """The SPP max-pool block (5/9/13 windows + the map) on YOLOv4's SPP maps:
+    10x10x512 (320-pixel input, the size of the pages' isolated benchmark),
+    20x20x512 (640-pixel input) and the N=16 batch of the latter. Cold buffer
+    sets as above; bytes = x read once + y (4x) written once."""
+    import torch
+
+    from convolution_conv2d_nhwc_amd import _lib
+
+    rows = []
+    for shape in ((1, 10, 10, 512), (1, 20, 20, 512), (16, 20, 20, 512)):
+        xb = 2 * shape[0] * shape[1] * shape[2] * shape[3]
+        nsets = max(2, min(64, -(-768 * 2 ** 20 // (5 * xb))))
+        xs = [(torch.randn(shape, generator=gen, device="cuda") * 0.5).to(torch.bfloat16) for _ in range(nsets)]
+        ys = [torch.empty(shape[:3] + (4 * shape[3],), dtype=torch.bfloat16, device="cuda") for _ in range(nsets)]
+        for i in range(nsets):
+            _lib.spp_maxpool(xs[i], ys[i])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(nsets):
+                _lib.spp_maxpool(xs[i], ys[i])
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / (reps * nsets)
+        by = 5 * xb
+        rows.append({"shape": "x".join(map(str, shape)), "kernel": "spp_kernel<1>", "us": round(us, 2),
+                     "gbs": round(by / (us * 1e-6) / 1e9, 1), "bound": "hbm",
+                     "frac_hbm_peak": round(by / (us * 1e-6) / 1e9 / HBM_GBS, 4), "buffer_sets": nsets})
+        del xs, ys, g
+        torch.cuda.empty_cache()
+    return {"layers": rows}
 
 
 def cpu_baseline(wl):

@@ -73,6 +73,8 @@ def lib():
     L.conv_algo_count.restype = ctypes.c_int32
     L.conv_mosaic_pack.argtypes = [P, ctypes.c_int32, P, ctypes.c_int32] + [ctypes.c_int32] * 5 + [P]
     L.conv_mosaic_pack.restype = ctypes.c_int
+    L.conv_spp_maxpool.argtypes = [P, ctypes.c_int32, P] + [ctypes.c_int32] * 4 + [P]
+    L.conv_spp_maxpool.restype = ctypes.c_int
     L.conv_status_str.argtypes = [ctypes.c_int32]
     L.conv_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -209,3 +211,21 @@ def mosaic_pack(tiles: torch.Tensor, canvas: Optional[torch.Tensor] = None, c_pa
                                 m, th, tw, c, c_pad, _stream_handle(stream))
     _check(st, "conv_mosaic_pack")
     return canvas
+
+
+def spp_maxpool(x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """SPP max-pool block of x [n, h, w, c] (float32, bfloat16 or int8):
+    y [n, h, w, 4c] = max13 | max9 | max5 | x along channels."""
+    codes = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2}
+    if x.dim() != 4 or x.dtype not in codes:
+        raise ValueError("x must be a [n, h, w, c] float32, bfloat16 or int8 tensor")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor")
+    n, h, w, c = x.shape
+    if y is None:
+        y = torch.empty((n, h, w, 4 * c), dtype=x.dtype, device=x.device)
+    if tuple(y.shape) != (n, h, w, 4 * c) or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [n, h, w, 4c] tensor of x's dtype")
+    st = lib().conv_spp_maxpool(x.data_ptr(), codes[x.dtype], y.data_ptr(), n, h, w, c, _stream_handle(stream))
+    _check(st, "conv_spp_maxpool")
+    return y

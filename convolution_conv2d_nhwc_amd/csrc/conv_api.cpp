@@ -412,6 +412,23 @@ conv_status conv_mosaic_pack(const void* tiles, int32_t in_dtype, void* canvas, 
   return CONV_OK;
 }
 
+conv_status conv_spp_maxpool(const void* x, int32_t dtype, void* y, int32_t n, int32_t h, int32_t w, int32_t c,
+                             void* stream) {
+  if (!x || !y) return CONV_E_NULL;
+  if (n <= 0 || h <= 0 || w <= 0 || c <= 0) return CONV_E_SHAPE;
+  if (dtype != CONV_F32 && dtype != CONV_BF16 && dtype != CONV_I8) return CONV_E_UNSUPPORTED;
+  const int64_t x_bytes = (int64_t)n * h * w * c * esz_of(dtype);
+  if (4 * x_bytes >= kMaxBytes || spp_chunks(n, h, w, c, dtype) == 0) return CONV_E_UNSUPPORTED;
+  if (((uintptr_t)x | (uintptr_t)y) & 15) return CONV_E_ALIGN;
+  if (ranges_overlap(x, x_bytes, y, 4 * x_bytes)) return CONV_E_ALIAS;
+  hipError_t err = launch_spp(x, dtype, y, n, h, w, c, x_bytes, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(err));
+    return CONV_E_HIP;
+  }
+  return CONV_OK;
+}
+
 const char* conv_status_str(int32_t status) {
   static thread_local char buf[320];
   switch (status) {

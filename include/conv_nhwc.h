@@ -167,6 +167,21 @@ conv_status conv_mosaic_pack(const void* tiles, int32_t in_dtype, void* canvas,
                              int32_t tw, int32_t c, int32_t c_pad,
                              void* stream);
 
+/* SPP max-pool block (YOLOv4 on Tenstorrent Wormhole, section 10 kernel
+ * table, K3; section 3 for the block's role): for each pixel, the maximum over
+ * the 13x13, 9x9 and 5x5 windows centred on it (stride 1, output the size of
+ * the input, positions outside the map ignored, i.e. padding with -infinity),
+ * concatenated with the map itself:
+ *   y[n][h][w][j*c + ch], j = 0, 1, 2, 3 = max13, max9, max5, x.
+ *   x : device [n][h][w][c] of dtype (F32, BF16 or I8)
+ *   y : device [n][h][w][4c] of the same dtype; every value is an input value
+ *       (bit-exact; of a -0 and a +0 in one window the +0 is returned).
+ * Both 16-byte aligned and non-overlapping. c must be a multiple of 8 (BF16,
+ * I8) or 4 (F32) and h*w at most 2048 (CONV_E_UNSUPPORTED otherwise); y must
+ * be smaller than 2^31 bytes. Enqueues one kernel on `stream`. */
+conv_status conv_spp_maxpool(const void* x, int32_t dtype, void* y, int32_t n,
+                             int32_t h, int32_t w, int32_t c, void* stream);
+
 /* Name of a status code ("CONV_OK", "CONV_E_SHAPE", ...). For CONV_E_HIP
  * the text of the last HIP error seen by this thread is appended. */
 const char* conv_status_str(int32_t status);

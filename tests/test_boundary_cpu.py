@@ -27,7 +27,7 @@ def header_functions():
 def test_header_symbols_are_exported():
     names = header_functions()
     assert {"conv_prepare", "conv_run", "conv_destroy", "conv_out_shape", "conv_mosaic_pack",
-            "conv_status_str", "conv_describe", "conv_algo_count"} <= set(names)
+            "conv_status_str", "conv_describe", "conv_algo_count", "conv_spp_maxpool"} <= set(names)
     L = ctypes.CDLL(_lib.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -170,6 +170,25 @@ def test_depthwise_forced_rows():
 
 def fake(addr):
     return ctypes.c_void_p(addr)
+
+
+def test_spp_argument_checks_before_launch():
+    """conv_spp_maxpool refuses bad arguments on the host, before any device
+    call; the fake addresses are never dereferenced."""
+    L = _lib.lib()
+    X, Y = 0x10000000, 0x20000000
+    ok = (1, 20, 20, 512)
+    assert L.conv_spp_maxpool(None, 1, Y, *ok, None) == -1
+    assert L.conv_spp_maxpool(X, 1, None, *ok, None) == -1
+    assert L.conv_spp_maxpool(X, 1, Y, 0, 20, 20, 512, None) == -2
+    assert L.conv_spp_maxpool(X, 1, Y, 1, 20, -1, 512, None) == -2
+    assert L.conv_spp_maxpool(X, 3, Y, *ok, None) == -3             # int32 is not a map dtype
+    assert L.conv_spp_maxpool(X, 1, Y, 1, 20, 20, 12, None) == -3    # bf16 channels not a multiple of 8
+    assert L.conv_spp_maxpool(X, 0, Y, 1, 20, 20, 6, None) == -3     # fp32 channels not a multiple of 4
+    assert L.conv_spp_maxpool(X, 1, Y, 1, 64, 33, 8, None) == -3     # 2112 pixels
+    assert L.conv_spp_maxpool(X + 8, 1, Y, *ok, None) == -4
+    assert L.conv_spp_maxpool(X, 1, Y + 4, *ok, None) == -4
+    assert L.conv_spp_maxpool(X, 1, X + 1024 * 16, *ok, None) == -5  # y overlaps x
 
 
 def test_run_pointer_checks_before_launch():

@@ -405,3 +405,42 @@ def test_side_stream_and_graph_replay():
         torch.cuda.synchronize()
         H.check_float(yg.cpu().float().numpy(), ref[0], ref[1], "bf16", "graph replay %d" % i)
         _ = (x.float() * 2).sum().item()  # unrelated eager work between replays
+
+
+# SPP max-pool block against the oracle, bit for bit (values: the oracle keeps
+# the first of equal values, the kernel the larger key, which differ only for
+# -0 against +0): the 320- and 640-input maps of YOLOv4's SPP, maps smaller
+# than the windows, a single pixel, odd sizes, all three dtypes, and the
+# chunk counts per workgroup that batch and channel count select.
+SPP = [
+    ((1, 10, 10, 512), "bf16"), ((1, 20, 20, 512), "bf16"), ((16, 20, 20, 512), "bf16"),
+    ((2, 13, 7, 24), "bf16"), ((1, 1, 1, 8), "bf16"), ((3, 3, 5, 16), "i8"), ((1, 19, 19, 256), "i8"),
+    ((2, 9, 14, 12), "f32"), ((1, 45, 45, 8), "bf16"), ((4, 6, 40, 64), "f32"),
+]
+
+
+def _spp_input(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    if dtype == "i8":
+        return torch.randint(-127, 128, shape, generator=g, dtype=torch.int8)
+    x = torch.randn(shape, generator=g) * 0.5
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("shape,dtype", SPP, ids=["%s_%s" % ("x".join(map(str, s)), d) for s, d in SPP])
+def test_spp_maxpool(shape, dtype):
+    x = _spp_input(shape, dtype, seed=31)
+    xn = x.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else x.numpy()
+    ref = oracle.spp(xn)
+    y = _lib.spp_maxpool(x.cuda())
+    torch.cuda.synchronize()
+    yc = y.cpu()
+    yn = yc.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else yc.numpy()
+    if dtype == "bf16":
+        yv = (yn.astype(np.uint32) << 16).view(np.float32)
+        rv = (ref.astype(np.uint32) << 16).view(np.float32)
+        assert np.array_equal(yv, rv), "values differ"
+        same_bits = yn == ref
+        assert np.all(same_bits | (yv == 0)), "bits differ on a nonzero value"
+    else:
+        assert np.array_equal(yn, ref)
