@@ -37,8 +37,9 @@
  * The loops are written in the order of the definition; OpenMP only splits
  * independent output rows across threads, which changes no arithmetic.
  *
- * The file also holds the SPP max-pool block (oracle_spp, defined where it
- * stands).
+ * The file also holds the SPP max-pool block (oracle_spp) and the
+ * upsample-and-concat of two maps (oracle_upcat), each defined where it
+ * stands.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no -ffast-math).
  */
@@ -428,6 +429,37 @@ int oracle_spp(const void *x, int dtype, int64_t n, int64_t h, int64_t w, int64_
             spp_put(x, dtype, best, y, out_px + j * c + ic);
           }
           spp_put(x, dtype, ((in * h + ih) * w + iw) * c + ic, y, out_px + 3 * c + ic);
+        }
+  return ORC_OK;
+}
+
+/*
+ * Upsample x2 + concat (zerolat.eu YOLOv4 report, section 10 kernel table,
+ * row K4: two neck feature maps, one repeated 2x in rows and columns, joined
+ * along channels into the next convolution's input). Two sources s = 0, 1,
+ * each [n][ho >> up_s][wo >> up_s][c_s] (up_s = 1: nearest-neighbour 2x
+ * upsampling, every source pixel feeds a 2x2 block; up_s = 0: same size),
+ * written one after the other along channels:
+ *   y[n,i,j, k]        = S0[n, i >> up0, j >> up0, k]          k < c0
+ *   y[n,i,j, c0 + k]   = S1[n, i >> up1, j >> up1, k]          k < c1
+ * A byte copy: esz is the element size (any dtype).
+ */
+int oracle_upcat(const void *s0, int64_t c0, int up0, const void *s1, int64_t c1, int up1, int64_t esz,
+                 int64_t n, int64_t ho, int64_t wo, void *y) {
+  if (n <= 0 || ho <= 0 || wo <= 0 || c0 <= 0 || c1 <= 0 || esz <= 0) return ORC_E_SHAPE;
+  if (((up0 || up1) && (ho % 2 || wo % 2)) || up0 < 0 || up0 > 1 || up1 < 0 || up1 > 1) return ORC_E_SHAPE;
+  const int64_t ct = c0 + c1;
+  for (int64_t in = 0; in < n; ++in)
+    for (int64_t i = 0; i < ho; ++i)
+      for (int64_t j = 0; j < wo; ++j)
+        for (int64_t k = 0; k < ct; ++k) {
+          const int s = k >= c0;
+          const int up = s ? up1 : up0;
+          const int64_t c = s ? c1 : c0, kk = s ? k - c0 : k;
+          const int64_t hs = ho >> up, ws = wo >> up;
+          const int64_t src = ((in * hs + (i >> up)) * ws + (j >> up)) * c + kk;
+          const int64_t dst = ((in * ho + i) * wo + j) * ct + k;
+          memcpy((char *)y + dst * esz, (const char *)(s ? s1 : s0) + src * esz, (size_t)esz);
         }
   return ORC_OK;
 }

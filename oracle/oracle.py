@@ -60,6 +60,8 @@ def _load():
     lib.oracle_mosaic.restype = I
     lib.oracle_spp.argtypes = [P, I] + [I64] * 4 + [P]
     lib.oracle_spp.restype = I
+    lib.oracle_upcat.argtypes = [P, I64, I, P, I64, I, I64, I64, I64, I64, P]
+    lib.oracle_upcat.restype = I
     lib.oracle_mish.argtypes = [ctypes.c_double]
     lib.oracle_mish.restype = ctypes.c_double
     lib.oracle_act.argtypes = [ctypes.c_double, I]
@@ -236,6 +238,24 @@ def spp(x):
     st = lib.oracle_spp(_ptr(x), _SPP_DT[x.dtype], n, h, w, c, _ptr(y))
     if st:
         raise ValueError("oracle_spp failed: %d" % st)
+    return y
+
+
+def upcat(s0, up0, s1, up1):
+    """Concatenate s0 and s1 ([n,h,w,c] arrays of one dtype) along channels
+    at the output size, each repeated 2x in rows and columns where its up
+    flag is set (see oracle_upcat in the C file)."""
+    lib = _load()
+    s0, s1 = np.ascontiguousarray(s0), np.ascontiguousarray(s1)
+    if s0.dtype != s1.dtype or s0.ndim != 4 or s1.ndim != 4:
+        raise ValueError("two 4-d arrays of one dtype")
+    n, ho, wo = s0.shape[0], s0.shape[1] << up0, s0.shape[2] << up0
+    if s1.shape[:3] != (n, ho >> up1, wo >> up1):
+        raise ValueError("source sizes do not match")
+    y = np.empty((n, ho, wo, s0.shape[3] + s1.shape[3]), s0.dtype)
+    st = lib.oracle_upcat(_ptr(s0), s0.shape[3], up0, _ptr(s1), s1.shape[3], up1, s0.itemsize, n, ho, wo, _ptr(y))
+    if st:
+        raise ValueError("oracle_upcat failed: %d" % st)
     return y
 
 

@@ -437,3 +437,28 @@ def test_spp_nested_windows_are_ordered():
     p13, p9, p5, x0 = (y[..., 8 * j:8 * (j + 1)] for j in range(4))
     assert np.all(p13 >= p9) and np.all(p9 >= p5) and np.all(p5 >= x0)
     assert np.array_equal(x0, x.astype(np.int32))
+
+
+# ------------------------------------------------------- upsample + concat --
+# Pinned to torch: nearest-neighbour interpolation at scale 2 (a library
+# routine) followed by torch.cat along channels, and to the closed form of
+# a 2x repeat (np.repeat on both axes).
+
+@pytest.mark.parametrize("dtype", [np.float32, np.uint16, np.int8])
+@pytest.mark.parametrize("up0,up1", [(1, 0), (0, 1), (0, 0), (1, 1)])
+def test_upcat_matches_torch_interpolate_and_cat(dtype, up0, up1):
+    rng = np.random.default_rng(up0 * 2 + up1)
+    n, ho, wo = 2, 6, 10
+    a = rng.integers(-100, 100, (n, ho >> up0, wo >> up0, 5)).astype(dtype)
+    b = rng.integers(-100, 100, (n, ho >> up1, wo >> up1, 3)).astype(dtype)
+    y = oracle.upcat(a, up0, b, up1)
+
+    def up(t, u):
+        tt = torch.from_numpy(t.astype(np.float64)).permute(0, 3, 1, 2)
+        if u:
+            tt = F.interpolate(tt, scale_factor=2, mode="nearest")
+        return tt
+    ref = torch.cat([up(a, up0), up(b, up1)], dim=1).permute(0, 2, 3, 1).numpy()
+    assert np.array_equal(y.astype(np.float64), ref)
+    rep = np.repeat(np.repeat(a, 2, axis=1), 2, axis=2) if up0 else a
+    assert np.array_equal(y[..., :5], rep)
