@@ -362,7 +362,57 @@ def secondary_measurements():
         out[name] = {"layers": rows, "total_us": round(tot_us, 2),
                      "tflops": round(tot_flop / (tot_us * 1e-6) / 1e12, 2)}
     out["spp_bf16"] = spp_measurements(gen)
+    out["upcat_bf16"] = upcat_measurements(gen)
     return out
+
+
+def _time_graph(fn_list):
+    """Average microseconds per call of a list of launches captured once and
+    replayed 10 times."""
+    import torch
+
+    for f in fn_list:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fn_list:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / (reps * len(fn_list))
+
+
+def upcat_measurements(gen):
+    """Upsample x2 + concat at YOLOv4's two neck joins for a 640-pixel input
+    (20x20x256 upsampled beside 40x40x256; 40x40x128 beside 80x80x128), N=1
+    and N=16. Cold buffer sets; bytes = both sources read once + y written."""
+    import torch
+
+    from convolution_conv2d_nhwc_amd import _lib
+
+    rows = []
+    for n, (hs, cs) in [(1, (20, 256)), (1, (40, 128)), (16, (20, 256)), (16, (40, 128))]:
+        a_shape, b_shape = (n, hs, hs, cs), (n, 2 * hs, 2 * hs, cs)
+        by = 2 * (n * hs * hs * cs + 2 * n * 4 * hs * hs * cs)
+        nsets = max(2, min(64, -(-768 * 2 ** 20 // by)))
+        srcs = [((torch.randn(a_shape, generator=gen, device="cuda")).to(torch.bfloat16),
+                 (torch.randn(b_shape, generator=gen, device="cuda")).to(torch.bfloat16)) for _ in range(nsets)]
+        ys = [torch.empty((n, 2 * hs, 2 * hs, 2 * cs), dtype=torch.bfloat16, device="cuda") for _ in range(nsets)]
+        us = _time_graph([lambda i=i: _lib.upsample_concat(srcs[i][0], 1, srcs[i][1], 0, ys[i]) for i in range(nsets)])
+        rows.append({"shape": "%dx%dx%dx%d up + %dx%dx%dx%d" % (a_shape + b_shape), "kernel": "upcat_kernel",
+                     "us": round(us, 2), "gbs": round(by / (us * 1e-6) / 1e9, 1), "bound": "hbm",
+                     "frac_hbm_peak": round(by / (us * 1e-6) / 1e9 / HBM_GBS, 4), "buffer_sets": nsets})
+        del srcs, ys
+        torch.cuda.empty_cache()
+    return {"layers": rows}
 
 
 def spp_measurements(gen):

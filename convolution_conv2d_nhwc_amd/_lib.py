@@ -75,6 +75,9 @@ def lib():
     L.conv_mosaic_pack.restype = ctypes.c_int
     L.conv_spp_maxpool.argtypes = [P, ctypes.c_int32, P] + [ctypes.c_int32] * 4 + [P]
     L.conv_spp_maxpool.restype = ctypes.c_int
+    I32 = ctypes.c_int32
+    L.conv_upsample_concat.argtypes = [P, I32, I32, P, I32, I32, I32, P, I32, I32, I32, P]
+    L.conv_upsample_concat.restype = ctypes.c_int
     L.conv_status_str.argtypes = [ctypes.c_int32]
     L.conv_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -228,4 +231,28 @@ def spp_maxpool(x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None) 
         raise ValueError("y must be a contiguous [n, h, w, 4c] tensor of x's dtype")
     st = lib().conv_spp_maxpool(x.data_ptr(), codes[x.dtype], y.data_ptr(), n, h, w, c, _stream_handle(stream))
     _check(st, "conv_spp_maxpool")
+    return y
+
+
+def upsample_concat(s0: torch.Tensor, up0: int, s1: torch.Tensor, up1: int, y: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """y [n, ho, wo, c0 + c1] = s0 | s1 along channels, each repeated 2x in
+    rows and columns (nearest) where its up flag is 1."""
+    codes = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2}
+    for t in (s0, s1):
+        if t.dim() != 4 or t.dtype not in codes or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("sources must be contiguous [n, h, w, c] device tensors (float32, bfloat16, int8)")
+    if s0.dtype != s1.dtype:
+        raise ValueError("sources must share a dtype")
+    n, ho, wo = s0.shape[0], s0.shape[1] << up0, s0.shape[2] << up0
+    if tuple(s1.shape[:3]) != (n, ho >> up1, wo >> up1) or (up1 and (s1.shape[1] << 1, s1.shape[2] << 1) != (ho, wo)):
+        raise ValueError("source sizes do not match")
+    c0, c1 = s0.shape[3], s1.shape[3]
+    if y is None:
+        y = torch.empty((n, ho, wo, c0 + c1), dtype=s0.dtype, device=s0.device)
+    if tuple(y.shape) != (n, ho, wo, c0 + c1) or y.dtype != s0.dtype or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [n, ho, wo, c0 + c1] tensor of the sources' dtype")
+    st = lib().conv_upsample_concat(s0.data_ptr(), c0, up0, s1.data_ptr(), c1, up1, codes[s0.dtype], y.data_ptr(),
+                                    n, ho, wo, _stream_handle(stream))
+    _check(st, "conv_upsample_concat")
     return y

@@ -429,6 +429,29 @@ conv_status conv_spp_maxpool(const void* x, int32_t dtype, void* y, int32_t n, i
   return CONV_OK;
 }
 
+conv_status conv_upsample_concat(const void* s0, int32_t c0, int32_t up0, const void* s1, int32_t c1, int32_t up1,
+                                 int32_t dtype, void* y, int32_t n, int32_t ho, int32_t wo, void* stream) {
+  if (!s0 || !s1 || !y) return CONV_E_NULL;
+  if (n <= 0 || ho <= 0 || wo <= 0 || c0 <= 0 || c1 <= 0 || up0 < 0 || up0 > 1 || up1 < 0 || up1 > 1 ||
+      ((up0 || up1) && (ho % 2 || wo % 2)))
+    return CONV_E_SHAPE;
+  if (dtype != CONV_F32 && dtype != CONV_BF16 && dtype != CONV_I8) return CONV_E_UNSUPPORTED;
+  const int64_t e = esz_of(dtype), b0 = (int64_t)c0 * e, b1 = (int64_t)c1 * e;
+  const int64_t s0_bytes = (int64_t)n * (ho >> up0) * (wo >> up0) * b0;
+  const int64_t s1_bytes = (int64_t)n * (ho >> up1) * (wo >> up1) * b1;
+  const int64_t y_bytes = (int64_t)n * ho * wo * (b0 + b1);
+  if (b0 % 16 || b1 % 16 || y_bytes >= kMaxBytes || (int64_t)n * ho > 65535 || (int64_t)wo * (b0 + b1) / 16 >= (1 << 22))
+    return CONV_E_UNSUPPORTED;
+  if (((uintptr_t)s0 | (uintptr_t)s1 | (uintptr_t)y) & 15) return CONV_E_ALIGN;
+  if (ranges_overlap(y, y_bytes, s0, s0_bytes) || ranges_overlap(y, y_bytes, s1, s1_bytes)) return CONV_E_ALIAS;
+  hipError_t err = launch_upcat(s0, b0, up0, s1, b1, up1, y, n, ho, wo, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(err));
+    return CONV_E_HIP;
+  }
+  return CONV_OK;
+}
+
 const char* conv_status_str(int32_t status) {
   static thread_local char buf[320];
   switch (status) {

@@ -94,6 +94,8 @@ hipError_t launch_f32(const conv_plan* p, const void* x, const void* w, const Ep
 int spp_chunks(int64_t n, int64_t h, int64_t w, int64_t c, int dtype);  // 0: map too large
 hipError_t launch_spp(const void* x, int dtype, void* y, int64_t n, int64_t h, int64_t w, int64_t c, int64_t x_bytes,
                       hipStream_t s);
+hipError_t launch_upcat(const void* s0, int64_t c0_bytes, int up0, const void* s1, int64_t c1_bytes, int up1, void* y,
+                        int64_t n, int64_t ho, int64_t wo, hipStream_t s);
 hipError_t launch_mosaic(const void* tiles, int in_f32, void* canvas, int out_f32, int m, int th,
                          int tw, int c, int c_pad, hipStream_t s);
 

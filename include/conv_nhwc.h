@@ -182,6 +182,25 @@ conv_status conv_mosaic_pack(const void* tiles, int32_t in_dtype, void* canvas,
 conv_status conv_spp_maxpool(const void* x, int32_t dtype, void* y, int32_t n,
                              int32_t h, int32_t w, int32_t c, void* stream);
 
+/* Upsample x2 + concat (YOLOv4 on Tenstorrent Wormhole, section 10 kernel
+ * table, K4): two maps joined along channels in the NHWC layout the next
+ * convolution reads, each repeated 2x in rows and columns (nearest
+ * neighbour) when its up flag is 1:
+ *   y[n][i][j][k]      = s0[n][i >> up0][j >> up0][k]       k < c0
+ *   y[n][i][j][c0 + k] = s1[n][i >> up1][j >> up1][k]       k < c1
+ *   s0 : device [n][ho >> up0][wo >> up0][c0] of dtype (F32, BF16 or I8)
+ *   s1 : device [n][ho >> up1][wo >> up1][c1] of dtype
+ *   y  : device [n][ho][wo][c0 + c1] of dtype; a byte copy (bit-exact).
+ * up flags 0 or 1; ho and wo even when either is 1 (CONV_E_SHAPE otherwise).
+ * All three pointers 16-byte aligned; y must not overlap s0 or s1. c0 and c1
+ * must be whole 16-byte chunks (multiples of 4 for F32, 8 for BF16, 16 for
+ * I8), n*ho at most 65535, y smaller than 2^31 bytes (CONV_E_UNSUPPORTED
+ * otherwise). Enqueues one kernel on `stream`. */
+conv_status conv_upsample_concat(const void* s0, int32_t c0, int32_t up0,
+                                 const void* s1, int32_t c1, int32_t up1,
+                                 int32_t dtype, void* y, int32_t n, int32_t ho,
+                                 int32_t wo, void* stream);
+
 /* Name of a status code ("CONV_OK", "CONV_E_SHAPE", ...). For CONV_E_HIP
  * the text of the last HIP error seen by this thread is appended. */
 const char* conv_status_str(int32_t status);

@@ -27,7 +27,8 @@ def header_functions():
 def test_header_symbols_are_exported():
     names = header_functions()
     assert {"conv_prepare", "conv_run", "conv_destroy", "conv_out_shape", "conv_mosaic_pack",
-            "conv_status_str", "conv_describe", "conv_algo_count", "conv_spp_maxpool"} <= set(names)
+            "conv_status_str", "conv_describe", "conv_algo_count", "conv_spp_maxpool",
+            "conv_upsample_concat"} <= set(names)
     L = ctypes.CDLL(_lib.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -170,6 +171,24 @@ def test_depthwise_forced_rows():
 
 def fake(addr):
     return ctypes.c_void_p(addr)
+
+
+def test_upcat_argument_checks_before_launch():
+    """conv_upsample_concat refuses bad arguments on the host."""
+    L = _lib.lib()
+    A, B, Y = 0x10000000, 0x20000000, 0x40000000
+    ok = (1, 40, 40, None)
+    assert L.conv_upsample_concat(None, 256, 1, B, 256, 0, 1, Y, *ok) == -1
+    assert L.conv_upsample_concat(A, 256, 1, B, 256, 0, 1, None, *ok) == -1
+    assert L.conv_upsample_concat(A, 256, 1, B, 256, 0, 1, Y, 1, 41, 40, None) == -2   # odd height, upsampled
+    assert L.conv_upsample_concat(A, 256, 2, B, 256, 0, 1, Y, *ok) == -2               # up flag not 0/1
+    assert L.conv_upsample_concat(A, 0, 1, B, 256, 0, 1, Y, *ok) == -2
+    assert L.conv_upsample_concat(A, 256, 1, B, 256, 0, 3, Y, *ok) == -3               # int32
+    assert L.conv_upsample_concat(A, 12, 1, B, 256, 0, 1, Y, *ok) == -3                # 24-byte pixel
+    assert L.conv_upsample_concat(A, 8, 1, B, 16, 0, 2, Y, *ok) == -3                  # int8, 8 bytes
+    assert L.conv_upsample_concat(A + 8, 256, 1, B, 256, 0, 1, Y, *ok) == -4
+    assert L.conv_upsample_concat(A, 256, 1, B, 256, 0, 1, B + 64, *ok) == -5          # y overlaps s1
+    assert L.conv_upsample_concat(A, 8, 0, B, 8, 0, 1, Y, 70000, 1, 2, None) == -3     # n * ho > 65535
 
 
 def test_spp_argument_checks_before_launch():

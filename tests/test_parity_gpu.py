@@ -444,3 +444,28 @@ def test_spp_maxpool(shape, dtype):
         assert np.all(same_bits | (yv == 0)), "bits differ on a nonzero value"
     else:
         assert np.array_equal(yn, ref)
+
+
+# Upsample x2 + concat against the oracle, byte for byte: YOLOv4's two neck
+# joins at 640 input (20x20x256 upsampled beside a 40x40x256 lateral map,
+# 40x40x128 beside 80x80x128) in both channel orders, both or neither source
+# upsampled, every dtype, odd chunk counts per pixel.
+UPCAT = [
+    ((1, 20, 20, 256), 1, (1, 40, 40, 256), 0, "bf16"), ((1, 80, 80, 128), 0, (1, 40, 40, 128), 1, "bf16"),
+    ((2, 5, 7, 24), 1, (2, 10, 14, 8), 0, "bf16"), ((3, 4, 6, 16), 0, (3, 4, 6, 48), 0, "i8"),
+    ((1, 3, 3, 32), 1, (1, 3, 3, 16), 1, "i8"), ((2, 6, 5, 12), 1, (2, 12, 10, 4), 0, "f32"),
+    ((16, 20, 20, 256), 1, (16, 40, 40, 256), 0, "bf16"),
+]
+
+
+@pytest.mark.parametrize("a_shape,up0,b_shape,up1,dtype", UPCAT,
+                         ids=["%s_up%d_%s_up%d_%s" % ("x".join(map(str, a)), u0, "x".join(map(str, b)), u1, d)
+                              for a, u0, b, u1, d in UPCAT])
+def test_upsample_concat(a_shape, up0, b_shape, up1, dtype):
+    a = _spp_input(a_shape, dtype, seed=41)
+    b = _spp_input(b_shape, dtype, seed=42)
+    to_np = (lambda t: t.view(torch.int16).numpy()) if dtype == "bf16" else (lambda t: t.numpy())
+    ref = oracle.upcat(to_np(a), up0, to_np(b), up1)
+    y = _lib.upsample_concat(a.cuda(), up0, b.cuda(), up1)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(y.cpu()), ref)
