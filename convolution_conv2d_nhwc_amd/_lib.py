@@ -63,6 +63,8 @@ def lib():
     L.conv_prepare.restype = ctypes.c_int
     L.conv_run.argtypes = [P, P, P, P, P, P]
     L.conv_run.restype = ctypes.c_int
+    L.conv_run_residual.argtypes = [P, P, P, P, P, P, P]
+    L.conv_run_residual.restype = ctypes.c_int
     L.conv_destroy.argtypes = [P]
     L.conv_destroy.restype = ctypes.c_int
     L.conv_out_shape.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
@@ -161,9 +163,11 @@ class Conv2d:
             raise ValueError("%s shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
 
     def run(self, x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor] = None,
-            y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+            y: Optional[torch.Tensor] = None, stream=None, residual: Optional[torch.Tensor] = None) -> torch.Tensor:
         """x NHWC, w OHWI, b as the header describes (float32[c_out] or the
-        packed int32 block for int8), y NHWC (allocated when None)."""
+        packed int32 block for int8), y NHWC (allocated when None). With
+        `residual` (y's dtype and shape; may be y itself) the layer computes
+        act(conv + b) + residual through conv_run_residual."""
         self._chk(x, "x", TORCH_DT[self.dtype], self.in_shape)
         self._chk(w, "w", TORCH_DT[self.dtype], self.w_shape)
         if b is not None:
@@ -172,9 +176,15 @@ class Conv2d:
         if y is None:
             y = self.empty_output(x.device)
         self._chk(y, "y", TORCH_DT[self.out_dtype], self.out_shape)
-        st = lib().conv_run(self._plan, x.data_ptr(), w.data_ptr(),
-                            None if b is None else b.data_ptr(), y.data_ptr(), _stream_handle(stream))
-        _check(st, "conv_run")
+        bp = None if b is None else b.data_ptr()
+        if residual is None:
+            st = lib().conv_run(self._plan, x.data_ptr(), w.data_ptr(), bp, y.data_ptr(), _stream_handle(stream))
+            _check(st, "conv_run")
+        else:
+            self._chk(residual, "residual", TORCH_DT[self.out_dtype], self.out_shape)
+            st = lib().conv_run_residual(self._plan, x.data_ptr(), w.data_ptr(), bp, residual.data_ptr(),
+                                         y.data_ptr(), _stream_handle(stream))
+            _check(st, "conv_run_residual")
         return y
 
     def run_ptrs(self, x: int, w: int, b: Optional[int], y: int, stream=None) -> int:

@@ -271,22 +271,28 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
   return CONV_OK;
 }
 
-conv_status conv_run(const conv_plan* p, const void* x, const void* w, const void* b, void* y,
-                     void* stream) {
+namespace {
+
+conv_status run_common(const conv_plan* p, const void* x, const void* w, const void* b, const void* r, void* y,
+                       void* stream) {
   if (!p || !x || !w || !y) return CONV_E_NULL;
   const bool i8out = p->d.dtype == CONV_I8 && p->d.out_dtype == CONV_I8;
   if (i8out && !b) return CONV_E_NULL;
-  if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) & 15) return CONV_E_ALIGN;
+  if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y | (uintptr_t)r) & 15) return CONV_E_ALIGN;
   if ((uintptr_t)b & 3) return CONV_E_ALIGN;
   if (ranges_overlap(y, p->y_bytes, x, p->x_bytes) || ranges_overlap(y, p->y_bytes, w, p->w_bytes) ||
       ranges_overlap(y, p->y_bytes, b, p->b_bytes))
     return CONV_E_ALIAS;
+  // the residual may be y itself (every output element reads its own
+  // residual element before it is written), but not partly overlap it
+  if (r && r != y && ranges_overlap(y, p->y_bytes, r, p->y_bytes)) return CONV_E_ALIAS;
 
   Epi e;
   e.act = p->d.act;
   e.bias = nullptr;
   e.ibias = nullptr;
   e.scale = nullptr;
+  e.res = r;
   if (p->d.dtype == CONV_I8) {
     e.ibias = static_cast<const int32_t*>(b);
     e.scale = b ? reinterpret_cast<const float*>(static_cast<const int32_t*>(b) + p->d.c_out) : nullptr;
@@ -309,6 +315,19 @@ conv_status conv_run(const conv_plan* p, const void* x, const void* w, const voi
     return CONV_E_HIP;
   }
   return CONV_OK;
+}
+
+}  // namespace
+
+conv_status conv_run(const conv_plan* p, const void* x, const void* w, const void* b, void* y, void* stream) {
+  return run_common(p, x, w, b, nullptr, y, stream);
+}
+
+conv_status conv_run_residual(const conv_plan* p, const void* x, const void* w, const void* b, const void* r,
+                              void* y, void* stream) {
+  if (!p || !r) return CONV_E_NULL;
+  if (p->out_kind == OUT_I32) return CONV_E_UNSUPPORTED;
+  return run_common(p, x, w, b, r, y, stream);
 }
 
 conv_status conv_destroy(conv_plan* p) {

@@ -74,6 +74,14 @@ __device__ __forceinline__ int requant_i8(int r, float s, int act) {
   return (int)q;
 }
 
+// With a residual rr added after the activation (see requant_i8_res_t).
+__device__ __forceinline__ int requant_i8_res(int r, float s, int act, int rr) {
+  const float v = __fmul_rn((float)r, s);
+  const float m = fminf(fmaxf(apply_act(v, act), -1048576.0f), 1048576.0f);
+  const int q = (int)__builtin_rintf(m);
+  return min(max(q + rr, -127), 127);
+}
+
 // Compile-time loop: f(std::integral_constant<int, i>) for i = I .. N-1.
 // Unlike `#pragma unroll` it does not depend on the unroller's size limit, so
 // register arrays indexed by i stay in registers however long the body is.
@@ -132,6 +140,27 @@ __device__ __forceinline__ uint32_t requant_i8_word_t(int r, float s) {
     c = __builtin_amdgcn_fmed3f(act_lo_t<ACT>(v), -127.0f, 127.0f);
   return __builtin_bit_cast(uint32_t, c + 12582912.0f);
 }
+// The same with a residual rr (an int8 value in the output's units) added
+// after the activation: Q = clamp(rne(act(v) + rr), -127, 127). rr is an
+// integer, so rne(m + rr) = rne(m) + rr exactly: the activation's value is
+// rounded first (clamped to +-2^20 so that the adder rounds it; beyond that
+// it saturates either way), then rr is added in integers before the
+// saturation.
+template <int ACT>
+__device__ __forceinline__ int requant_i8_res_t(int r, float s, int rr) {
+  const float v = __fmul_rn((float)r, s);
+  float m;
+  if constexpr (ACT == ACT_RELU)
+    m = fmaxf(v, 0.0f);
+  else if constexpr (ACT == ACT_RELU6)
+    m = __builtin_amdgcn_fmed3f(v, 0.0f, 6.0f);
+  else
+    m = act_lo_t<ACT>(v);
+  const float c = __builtin_amdgcn_fmed3f(m, -1048576.0f, 1048576.0f);
+  const int q = (int)(__builtin_bit_cast(uint32_t, c + 12582912.0f) - 0x4B400000u);
+  return min(max(q + rr, -127), 127);
+}
+
 template <int ACT>
 __device__ __forceinline__ int requant_i8_t(int r, float s) {
   return (int)(requant_i8_word_t<ACT>(r, s) - 0x4B400000u);
@@ -153,6 +182,7 @@ struct Epi {
   const float* bias;
   const int32_t* ibias;
   const float* scale;
+  const void* res;  // residual of the output's type and shape, added after the activation, or null
   int act;
 };
 

@@ -56,9 +56,10 @@ __global__ __launch_bounds__(256) void conv_f32_kernel(F32Args a) {
     }
   }
   float* yp = a.y + (size_t)px * g.cout + co0;
+  const float* rp = a.e.res ? static_cast<const float*>(a.e.res) + (size_t)px * g.cout + co0 : nullptr;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    if (r < nco) yp[r] = apply_act(acc[r] + (a.e.bias ? a.e.bias[co0 + r] : 0.0f), a.e.act);
+    if (r < nco) yp[r] = apply_act(acc[r] + (a.e.bias ? a.e.bias[co0 + r] : 0.0f), a.e.act) + (rp ? rp[r] : 0.0f);
 }
 
 }  // namespace

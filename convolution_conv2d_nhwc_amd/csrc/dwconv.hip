@@ -90,6 +90,15 @@ struct Elt<int8_t> {
   }
 };
 
+// int8 output of one element, with the residual (an int8 tensor of y's shape,
+// element idx) added after the activation when res is not null; the low
+// byte of the result is the output.
+template <int ACT>
+__device__ __forceinline__ int dw_q8(int r, float s, const void* res, size_t idx) {
+  if (res) return requant_i8_res_t<ACT>(r, s, static_cast<const int8_t*>(res)[idx]);
+  return (int)requant_i8_word_t<ACT>(r, s);
+}
+
 // VE = channels per lane (16 bytes worth, or 1 for the scalar fallback).
 // ACT and OUT (the int8 output kind) are compile-time: the epilogue runs once
 // per output vector and a per-element branch on them would cost more than it.
@@ -210,11 +219,11 @@ __global__ __launch_bounds__(256) void dw3x3_kernel(DwArgs a) {
           uint32_t wd[4] = {0, 0, 0, 0};
 #pragma unroll
           for (int e = 0; e < VE; ++e)
-            wd[e >> 2] |= (requant_i8_word_t<ACT>(rv[e], a.e.scale[c0 + e]) & 0xffu) << (8 * (e & 3));
+            wd[e >> 2] |= ((uint32_t)dw_q8<ACT>(rv[e], a.e.scale[c0 + e], a.e.res, off + e) & 0xffu) << (8 * (e & 3));
           *reinterpret_cast<i32x4*>(yp) = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
         } else {
 #pragma unroll
-          for (int e = 0; e < VE; ++e) yp[e] = (int8_t)requant_i8_t<ACT>(rv[e], a.e.scale[c0 + e]);
+          for (int e = 0; e < VE; ++e) yp[e] = (int8_t)dw_q8<ACT>(rv[e], a.e.scale[c0 + e], a.e.res, off + e);
         }
       }
     } else {
@@ -223,6 +232,10 @@ __global__ __launch_bounds__(256) void dw3x3_kernel(DwArgs a) {
       for (int e = 0; e < VE; ++e)
         v[e] = (sizeof(T) == 4 ? act_t<ACT>(acc[p][e] + (a.e.bias ? a.e.bias[c0 + e] : 0.0f))
                                : act_lo_t<ACT>(acc[p][e] + (a.e.bias ? a.e.bias[c0 + e] : 0.0f)));
+      if (a.e.res) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) v[e] += Elt<T>::get1(static_cast<const char*>(a.e.res) + (off + e) * sizeof(T));
+      }
       if constexpr (sizeof(T) == 4) {
         float* yp = reinterpret_cast<float*>(a.y) + off;
         if constexpr (VE == 4) {
@@ -360,7 +373,7 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
   constexpr int ESZ = sizeof(T);
   constexpr int PER = 4 / ESZ;  // elements per 32-bit word
   constexpr int NC = PW + 2;    // input columns per row
-  static_assert(ESZ != 1 || OUT == OUT_I8 || OUT == OUT_I32, "int8 output kinds");
+  static_assert(ESZ != 1, "int8 layers run dw3x3_i8_kernel");
   const uint32_t t = blockIdx.x * 256u + threadIdx.x;
   if (t >= (uint32_t)a.total) return;
   const Geometry& g = a.g;
@@ -368,6 +381,8 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
   const int c0 = l.c0, wo0 = l.wo0, ho0 = l.ho0, n = l.n;
   const __amdgpu_buffer_rsrc_t rx = dw_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t ry = dw_rsrc(a.y, a.y_bytes);
+  const bool has_res = a.e.res != nullptr;  // residual of y's type and shape, added after the activation
+  const __amdgpu_buffer_rsrc_t rr = dw_rsrc(a.e.res, has_res ? a.y_bytes : 0);
 
   // the 9 * VE weights of this lane's channels are contiguous ([VE][3][3])
   // and 4-byte aligned (VE * 9 * ESZ is a multiple of 4): whole-word loads
@@ -457,36 +472,39 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
 #pragma unroll
     for (int p = 0; p < PW; ++p) {
       const uint32_t off = dw_add_sat(yoff, poff[p]);
-      if constexpr (ESZ == 1) {
-        if constexpr (OUT == OUT_I32) {
-          int v[VE];
+      if constexpr (ESZ == 4) {
+        float v[VE];
 #pragma unroll
-          for (int e = 0; e < VE; ++e) v[e] = ACT == ACT_RELU ? max(acc[p][e], 0) : acc[p][e];
+        for (int e = 0; e < VE; ++e) v[e] = act_t<ACT>(acc[p][e]);
+        if (has_res) {
 #pragma unroll
-          for (int q = 0; q < VE / 4; ++q)
-            __builtin_amdgcn_raw_buffer_store_b128(i32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]}, ry,
-                                                   (int)(off + 16 * q), 0, 0);
-        } else {
-          uint32_t wd[VE / 4];
+          for (int q = 0; q < VE / 4; ++q) {
+            const i32x4 rv = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(off + 16 * q), 0, 0);
 #pragma unroll
-          for (int q = 0; q < VE / 4; ++q) wd[q] = 0;
-#pragma unroll
-          for (int e = 0; e < VE; ++e)
-            wd[e >> 2] |= (requant_i8_word_t<ACT>(acc[p][e], scl[e]) & 0xffu) << (8 * (e & 3));
-#pragma unroll
-          for (int q = 0; q < VE / 4; ++q) __builtin_amdgcn_raw_buffer_store_b32((int)wd[q], ry, (int)(off + 4 * q), 0, 0);
+            for (int e = 0; e < 4; ++e) {
+              const int bits = rv[e];  // a scalar copy: bit_cast of the subscript would read element 0
+              v[4 * q + e] += __builtin_bit_cast(float, bits);
+            }
+          }
         }
-      } else if constexpr (ESZ == 4) {
 #pragma unroll
         for (int q = 0; q < VE / 4; ++q)
           __builtin_amdgcn_raw_buffer_store_b128(
-              i32x4{__builtin_bit_cast(int, act_t<ACT>(acc[p][4 * q])), __builtin_bit_cast(int, act_t<ACT>(acc[p][4 * q + 1])),
-                    __builtin_bit_cast(int, act_t<ACT>(acc[p][4 * q + 2])), __builtin_bit_cast(int, act_t<ACT>(acc[p][4 * q + 3]))},
+              i32x4{__builtin_bit_cast(int, v[4 * q]), __builtin_bit_cast(int, v[4 * q + 1]),
+                    __builtin_bit_cast(int, v[4 * q + 2]), __builtin_bit_cast(int, v[4 * q + 3])},
               ry, (int)(off + 16 * q), 0, 0);
       } else {
+        float v[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) v[e] = act_lo_t<ACT>(acc[p][e]);
+        if (has_res) {
+          RawVec<T, VE> rv = load_raw<T, VE>(rr, off);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) v[e] += widen_word<T>(rv.w[e / PER], e);
+        }
         uint32_t wd[VE / 2];
 #pragma unroll
-        for (int q = 0; q < VE / 2; ++q) wd[q] = pack_bf16x2(act_lo_t<ACT>(acc[p][2 * q]), act_lo_t<ACT>(acc[p][2 * q + 1]));
+        for (int q = 0; q < VE / 2; ++q) wd[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
         if constexpr (VE == 8)
           __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]}, ry, (int)off, 0, 0);
         else
@@ -496,7 +514,6 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
     yoff += yrow;
   }
 }
-
 // ---------------------------------------------------------------------------
 // int8, stride 1: four channels per lane (one 32-bit word per pixel) and the
 // three window rows of each (column, channel) packed into one word, bytes
@@ -514,6 +531,8 @@ __global__ __launch_bounds__(256) void dw3x3_i8_kernel(DwArgs a) {
   const int c0 = l.c0, wo0 = l.wo0, ho0 = l.ho0, n = l.n;
   const __amdgpu_buffer_rsrc_t rx = dw_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t ry = dw_rsrc(a.y, a.y_bytes);
+  const bool has_res = a.e.res != nullptr;  // residual of y's type and shape, added after the activation
+  const __amdgpu_buffer_rsrc_t rr = dw_rsrc(a.e.res, has_res ? a.y_bytes : 0);
 
   // weights of channels c0..c0+3 are 36 contiguous bytes ([4][3][3]),
   // 4-byte aligned because c0 is a multiple of 4
@@ -599,8 +618,14 @@ __global__ __launch_bounds__(256) void dw3x3_i8_kernel(DwArgs a) {
         __builtin_amdgcn_raw_buffer_store_b128(i32x4{acc[0], acc[1], acc[2], acc[3]}, ry, (int)off, 0, 0);
       } else {
         uint32_t q[4];
+        if (has_res) {
+          const uint32_t rv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rr, (int)off, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) q[e] = requant_i8_word_t<ACT>(acc[e], scl[e]);
+          for (int e = 0; e < 4; ++e) q[e] = (uint32_t)requant_i8_res_t<ACT>(acc[e], scl[e], (int)(int8_t)(rv >> (8 * e)));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q[e] = requant_i8_word_t<ACT>(acc[e], scl[e]);
+        }
         // low bytes of q0..q3 into one word
         const uint32_t lo = __builtin_amdgcn_perm(q[1], q[0], 0x0C0C0400u);
         const uint32_t hi = __builtin_amdgcn_perm(q[3], q[2], 0x0C0C0400u);

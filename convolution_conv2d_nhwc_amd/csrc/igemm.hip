@@ -437,7 +437,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
     return;
   }
   if ((g.cout & 3) == 0) {
-    const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1));
+    const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1), a.e.res);
     with_epilogue<ESZ>(a.out_kind, a.e.act, [&](auto oc, auto ac) {
       constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
       StaticFor<0, FCO>::run([&](auto ic) {
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
     StaticFor<0, FPX>::run([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       const int px = px_w + 16 * j;
-      if (px < g.m) store_quad<ESZ>(acc[i][j], q, co, px, g.cout, a.out_kind, a.e.act, a.y);
+      if (px < g.m) store_quad<ESZ>(acc[i][j], q, co, px, g.cout, a.out_kind, a.e.act, a.y, a.e.res);
     });
   });
 }

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const void* ws, int 
   const int nq = cout / 4;
   const long total = (long)m * nq;
   const acc_t* w = reinterpret_cast<const acc_t*>(ws);
-  const OutRef o = out_ref(y, m, cout, ESZ == 2 ? 2 : (out_kind == OUT_I32 ? 4 : 1));
+  const OutRef o = out_ref(y, m, cout, ESZ == 2 ? 2 : (out_kind == OUT_I32 ? 4 : 1), e.res);
   with_epilogue<ESZ>(out_kind, e.act, [&](auto oc, auto ac) {
     constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
     for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (long)gridDim.x * blockDim.x) {

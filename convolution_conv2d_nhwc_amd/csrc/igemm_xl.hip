@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     });
     return;
   }
-  const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1));
+  const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1), a.e.res);
   with_epilogue<ESZ>(a.out_kind, a.e.act, [&](auto oc, auto ac) {
     constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
     StaticFor<0, FCO>::run([&](auto ic) {

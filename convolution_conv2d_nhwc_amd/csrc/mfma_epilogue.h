@@ -41,16 +41,21 @@ __device__ __forceinline__ QuadConsts load_quad_consts(const Epi& e, int co, int
 }
 
 // Store the quad v (channels co..co+3 of pixel px). The caller guarantees
-// px < m and co < cout; channels at or beyond cout are not written.
+// px < m and co < cout; channels at or beyond cout are not written. res is
+// the residual (y's type and shape) added after the activation, or null.
 template <int ESZ, typename acc_t>
 __device__ __forceinline__ void store_quad(const acc_t& v, const QuadConsts& q, int co, int px, int cout,
-                                           int out_kind, int act, void* y) {
+                                           int out_kind, int act, void* y, const void* res) {
   const size_t off = (size_t)px * cout + co;
   const bool vec4 = (cout & 3) == 0;
   if constexpr (ESZ == 2) {
     uint32_t h[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_bits(apply_act(v[r] + q.bsf[r], act));
+    for (int r = 0; r < 4; ++r) {
+      float f = apply_act(v[r] + q.bsf[r], act);
+      if (res && co + r < cout) f += bf16_bits_to_f32(static_cast<const uint16_t*>(res)[off + r]);
+      h[r] = f32_to_bf16_bits(f);
+    }
     uint16_t* yp = reinterpret_cast<uint16_t*>(y) + off;
     if (vec4) {
       uint2 w;
@@ -78,7 +83,11 @@ __device__ __forceinline__ void store_quad(const acc_t& v, const QuadConsts& q, 
   } else {
     uint32_t b[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) b[r] = (uint32_t)(requant_i8(v[r] + q.bsi[r], q.scl[r], act) & 0xff);
+    for (int r = 0; r < 4; ++r)
+      b[r] = (uint32_t)((res ? requant_i8_res(v[r] + q.bsi[r], q.scl[r], act,
+                                              co + r < cout ? static_cast<const int8_t*>(res)[off + r] : 0)
+                             : requant_i8(v[r] + q.bsi[r], q.scl[r], act)) &
+                        0xff);
     int8_t* yp = reinterpret_cast<int8_t*>(y) + off;
     if (vec4) {
       *reinterpret_cast<uint32_t*>(yp) = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
@@ -130,17 +139,23 @@ __device__ __forceinline__ void with_epilogue(int out_kind, int act, F&& f) {
 }
 
 // The output tensor as a buffer: y, its size in bytes, m pixels x cout
-// channels (cout % 4 == 0 for store_quad_t).
+// channels (cout % 4 == 0 for store_quad_t), and the residual added after the
+// activation (same type and shape as y; has_res is uniform, so the test is a
+// scalar branch).
 struct OutRef {
   __amdgpu_buffer_rsrc_t r;
+  __amdgpu_buffer_rsrc_t rr;
   int m, cout;
+  bool has_res;
 };
 
-__device__ __forceinline__ OutRef out_ref(void* y, int m, int cout, int out_esz) {
+__device__ __forceinline__ OutRef out_ref(void* y, int m, int cout, int out_esz, const void* res) {
   OutRef o;
   o.r = __builtin_amdgcn_make_buffer_rsrc(y, 0, m * cout * out_esz, 0x00020000);
+  o.rr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(res), 0, res ? m * cout * out_esz : 0, 0x00020000);
   o.m = m;
   o.cout = cout;
+  o.has_res = res != nullptr;
   return o;
 }
 
@@ -186,9 +201,17 @@ __device__ __forceinline__ void store_quad_t(const acc_t& v, const QuadConsts& q
   const bool in = px < o.m && co < o.cout;
   const uint32_t idx = (uint32_t)(px * o.cout + co);
   if constexpr (ESZ == 2) {
+    float f[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[r] = act_lo_t<ACT>(v[r] + q.bsf[r]);
+    if (o.has_res) {
+      const u32x2 rv = __builtin_amdgcn_raw_buffer_load_b64(o.rr, in ? idx * 2u : kNowhere, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) f[r] += bf16_bits_to_f32((r & 1) ? (rv[r >> 1] >> 16) : (rv[r >> 1] & 0xffffu));
+    }
     uint32_t h[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_bits(act_lo_t<ACT>(v[r] + q.bsf[r]));
+    for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_bits(f[r]);
     const u32x2 d = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
     __builtin_amdgcn_raw_buffer_store_b64(d, o.r, in ? idx * 2u : kNowhere, 0, 0);
   } else if constexpr (OUT == OUT_I32) {
@@ -202,8 +225,16 @@ __device__ __forceinline__ void store_quad_t(const acc_t& v, const QuadConsts& q
     __builtin_amdgcn_raw_buffer_store_b128(d, o.r, in ? idx * 4u : kNowhere, 0, 0);
   } else {
     uint32_t b = 0;
+    if (o.has_res) {
+      const uint32_t rv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(o.rr, in ? idx : kNowhere, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) b |= (requant_i8_word_t<ACT>(v[r] + q.bsi[r], q.scl[r]) & 0xffu) << (8 * r);
+      for (int r = 0; r < 4; ++r)
+        b |= ((uint32_t)requant_i8_res_t<ACT>(v[r] + q.bsi[r], q.scl[r], (int)(int8_t)(rv >> (8 * r))) & 0xffu)
+             << (8 * r);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b |= (requant_i8_word_t<ACT>(v[r] + q.bsi[r], q.scl[r]) & 0xffu) << (8 * r);
+    }
     __builtin_amdgcn_raw_buffer_store_b32(b, o.r, in ? idx : kNowhere, 0, 0);
   }
 }

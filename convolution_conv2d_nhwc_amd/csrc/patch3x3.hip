@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void patch3x3_kernel(PatchArgs a) {
   // A quad outside the image is sent past the output (px = m: not stored).
   const int wo = wo0 + lr;
   if ((g.cout & 3) == 0) {
-    const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1));
+    const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1), a.e.res);
     with_epilogue<ESZ>(a.out_kind, a.e.act, [&](auto oc, auto ac) {
       constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
 #pragma unroll
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void patch3x3_kernel(PatchArgs a) {
     for (int f = 0; f < FPX; ++f) {
       const int ho = ho0 + wave * FPX + f;
       if (ho < g.ho && wo < g.wo)
-        store_quad<ESZ>(acc[i][f], q, co, (n * g.ho + ho) * g.wo + wo, g.cout, a.out_kind, a.e.act, a.y);
+        store_quad<ESZ>(acc[i][f], q, co, (n * g.ho + ho) * g.wo + wo, g.cout, a.out_kind, a.e.act, a.y, a.e.res);
     }
   }
 }

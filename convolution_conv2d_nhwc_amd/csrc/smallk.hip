@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void smallk_kernel(SkArgs a) {
   for (int i = 0; i < FCO; ++i) q[i] = load_quad_consts<ESZ>(a.e, co0 + 16 * i + 4 * kg, g.cout);
 
   const int hw_o = g.ho * g.wo;
-  const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1));
+  const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1), a.e.res);
   const int nwaves = gridDim.x * 4;
   for (int pt = blockIdx.x * 4 + (threadIdx.x >> 6); pt < a.npx_tiles; pt += nwaves) {
     const int pbase = pt * 64;
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void smallk_kernel(SkArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int px = pbase + 16 * j + lr;
-        if (px < g.m) store_quad<ESZ>(acc[i][j], q[i], co, px, g.cout, a.out_kind, a.e.act, a.y);
+        if (px < g.m) store_quad<ESZ>(acc[i][j], q[i], co, px, g.cout, a.out_kind, a.e.act, a.y, a.e.res);
       }
     }
   }

@@ -140,6 +140,22 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out);
 conv_status conv_run(const conv_plan* p, const void* x, const void* w,
                      const void* b, void* y, void* stream);
 
+/* conv_run with a residual added after the activation, written once (YOLOv4
+ * on Tenstorrent Wormhole, section 10 kernel table, K2: the ResBlock tail
+ * computes Mish and adds the skip tensor in one pass instead of storing and
+ * reloading the activation):
+ *   F32  : y = act(conv + b) + r                      (one fp32 add)
+ *   BF16 : y = bf16_rne(act(conv + b) + r)            (sum in fp32, one rounding)
+ *   I8   : y = clamp(round_half_even(act(v) + r), -127, 127)
+ *          with v as for conv_run and r an int8 value in the output's units
+ *          (computed exactly as round_half_even(act(v)) + r before the clamp)
+ *   r : device NHWC [n][ho][wo][c_out] of out_dtype, 16-byte aligned. It may
+ *       be y itself (in-place add) but must not otherwise overlap y.
+ * The int32 checkpoint output (I8 -> I32) gives CONV_E_UNSUPPORTED. Other
+ * arguments, errors and ordering rules as for conv_run. */
+conv_status conv_run_residual(const conv_plan* p, const void* x, const void* w,
+                              const void* b, const void* r, void* y, void* stream);
+
 /* Free a plan. NULL is a no-op. */
 conv_status conv_destroy(conv_plan* p);
 

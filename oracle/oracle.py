@@ -259,6 +259,25 @@ def upcat(s0, up0, s1, up1):
     return y
 
 
+def add_residual_float(r, a, res):
+    """Residual-add epilogue for float outputs (zerolat.eu YOLOv4 report,
+    section 10 kernel table, K2: the activation, then the skip tensor added,
+    the sum written once). r, a: the oracle's unrounded activation output and
+    absolute-value convolution; res: the residual's values (fp32, or bf16
+    widened exactly). Returns (r + res, a + |res|) in float64, unrounded."""
+    res = np.asarray(res, np.float64)
+    return np.asarray(r, np.float64) + res, np.asarray(a, np.float64) + np.abs(res)
+
+
+def add_residual_i8(m, res):
+    """Residual-add epilogue for int8 outputs: res is int8 in the output's
+    units, added to the activation's unrounded value m (float64) before the
+    rounding: Q = clamp(round_half_even(m + res), -127, 127). Returns
+    (Q int8, m + res)."""
+    t = np.asarray(m, np.float64) + np.asarray(res, np.float64)
+    return np.clip(np.rint(t), -127, 127).astype(np.int8), t
+
+
 def mish(x: float) -> float:
     return _load().oracle_mish(float(x))
 

@@ -28,7 +28,7 @@ def test_header_symbols_are_exported():
     names = header_functions()
     assert {"conv_prepare", "conv_run", "conv_destroy", "conv_out_shape", "conv_mosaic_pack",
             "conv_status_str", "conv_describe", "conv_algo_count", "conv_spp_maxpool",
-            "conv_upsample_concat"} <= set(names)
+            "conv_upsample_concat", "conv_run_residual"} <= set(names)
     L = ctypes.CDLL(_lib.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -171,6 +171,23 @@ def test_depthwise_forced_rows():
 
 def fake(addr):
     return ctypes.c_void_p(addr)
+
+
+def test_residual_argument_checks_before_launch():
+    """conv_run_residual refuses a NULL or misaligned residual, one that
+    partly overlaps y, and int32-checkpoint plans, before any launch."""
+    c = Conv2d(1, 8, 8, 16, 16, 3, 3, (1, 1), (1, 1), dtype="bf16")
+    L = _lib.lib()
+    P = c._plan
+    X, W, B, Y, R = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+    assert L.conv_run_residual(P, X, W, B, None, Y, None) == -1
+    assert L.conv_run_residual(None, X, W, B, R, Y, None) == -1
+    assert L.conv_run_residual(P, X, W, B, R + 8, Y, None) == -4
+    assert L.conv_run_residual(P, X, W, B, Y + 16, Y, None) == -5
+    c.close()
+    c32 = Conv2d(1, 8, 8, 16, 16, 3, 3, (1, 1), (1, 1), dtype="i8", out_dtype="i32")
+    assert L.conv_run_residual(c32._plan, X, W, B, R, Y, None) == -3
+    c32.close()
 
 
 def test_upcat_argument_checks_before_launch():

@@ -462,3 +462,34 @@ def test_upcat_matches_torch_interpolate_and_cat(dtype, up0, up1):
     assert np.array_equal(y.astype(np.float64), ref)
     rep = np.repeat(np.repeat(a, 2, axis=1), 2, axis=2) if up0 else a
     assert np.array_equal(y[..., :5], rep)
+
+
+# ------------------------------------------------------ residual epilogue --
+# Pinned to hand values: Mish(1) (the mpmath value above) plus a skip value,
+# an int8 tie that the residual moves (2.5 -> 2, 2.5 + 1 -> 4, half to
+# even), a negative Mish that rounds away once the skip is added, saturation,
+# and the identity with a zero residual.
+
+def test_residual_float_hand_values():
+    r, a = oracle.add_residual_float(np.array([0.86509838826731034612, -1.0]), np.array([1.0, 2.0]),
+                                     np.array([2.0, -0.5]))
+    assert r[0] == pytest.approx(2.86509838826731034612, abs=1e-15) and r[1] == -1.5
+    assert list(a) == [3.0, 2.5]
+
+
+@pytest.mark.parametrize("m,res,q", [(2.5, 0, 2), (2.5, 1, 4), (-0.3034014613741089, 5, 5), (100.0, 100, 127),
+                                     (-0.3, -127, -127), (0.4999999, 3, 3), (3.5, -1, 2), (-2.5, 0, -2)])
+def test_residual_i8_hand_values(m, res, q):
+    got, t = oracle.add_residual_i8(np.array([m]), np.array([res], np.int8))
+    assert int(got[0]) == q and t[0] == m + res
+
+
+def test_residual_zero_is_the_plain_epilogue():
+    rng = np.random.default_rng(5)
+    x = rng.integers(-127, 128, (1, 6, 5, 16)).astype(np.int8)
+    w = rng.integers(-127, 128, (8, 3, 3, 16)).astype(np.int8)
+    b = rng.integers(-16129, 16130, 8).astype(np.int32)
+    s = (rng.random(8) * 0.009 + 0.001).astype(np.float32)
+    q, m = oracle.conv_i8(x, w, b, s, (1, 1), (1, 1), 1, "relu6")
+    q2, _ = oracle.add_residual_i8(m, np.zeros(q.shape, np.int8))
+    assert np.array_equal(q, q2)

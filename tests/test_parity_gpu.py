@@ -469,3 +469,76 @@ def test_upsample_concat(a_shape, up0, b_shape, up1, dtype):
     y = _lib.upsample_concat(a.cuda(), up0, b.cuda(), up1)
     torch.cuda.synchronize()
     assert np.array_equal(to_np(y.cpu()), ref)
+
+
+# Residual-add epilogue (conv_run_residual): y = act(conv + b) + r written
+# once, against the oracle's unrounded activation plus r, on every kernel
+# path: implicit GEMM (tap, vec16 and element-wise loaders, Cout not a
+# multiple of 4), the large-layer kernel, the small-K stem kernel, the halo-
+# patch kernel, split K, the fp32 direct kernel and the three depthwise
+# kernels; in place (r is y) for a bf16 and an int8 layer.
+RES = [
+    L("res_bf16_tap", 1, 12, 13, 64, 64, 3, 3, (1, 1), (1, 1), act="mish"),
+    L("res_bf16_xl", 1, 11, 9, 128, 256, 3, 3, (1, 1), (1, 1), act="mish"),
+    L("res_bf16_vec", 1, 9, 10, 32, 48, 3, 3, (2, 2), (1, 1), act="relu6"),
+    L("res_bf16_cout6", 1, 9, 8, 24, 6, 3, 3, (1, 1), (1, 1), act="relu"),
+    L("res_bf16_stem", 1, 17, 15, 3, 32, 3, 3, (1, 1), (1, 1), act="mish"),
+    L("res_bf16_patch", 1, 14, 12, 64, 64, 3, 3, (1, 1), (1, 1), act="none"),
+    L("res_bf16_splitk", 1, 10, 10, 512, 256, 3, 3, (1, 1), (1, 1), act="mish"),
+    L("res_i8_tap", 1, 12, 11, 128, 64, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="mish"),
+    L("res_i8_xl", 1, 13, 9, 128, 256, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="relu6"),
+    L("res_i8_cout5", 1, 7, 9, 16, 5, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="none"),
+    L("res_f32", 1, 10, 10, 4, 8, 3, 3, (1, 1), (1, 1), dtype="f32", act="relu"),
+    L("res_dw_bf16", 2, 11, 13, 32, 32, 3, 3, (1, 1), (1, 1), groups=32, act="relu6"),
+    L("res_dw_bf16_s2", 1, 12, 11, 32, 32, 3, 3, (2, 2), (1, 1), groups=32, act="mish"),
+    L("res_dw_i8", 1, 9, 10, 64, 64, 3, 3, (1, 1), (1, 1), groups=64, dtype="i8", out="i8", act="mish"),
+    L("res_dw_i8_s2", 1, 12, 12, 32, 32, 3, 3, (2, 2), (1, 1), groups=32, dtype="i8", out="i8", act="relu"),
+    L("res_dw_f32", 1, 9, 9, 8, 8, 3, 3, (1, 1), (1, 1), groups=8, dtype="f32", act="mish"),
+]
+RES_KERNEL = {"res_bf16_xl": "igemm_xl", "res_i8_xl": "igemm_xl", "res_bf16_patch": "patch3x3",
+              "res_bf16_stem": "smallk", "res_bf16_splitk": "ksplit=", "res_dw_bf16": "dw3x3_rows_kernel",
+              "res_dw_bf16_s2": "dw3x3_kernel", "res_dw_i8": "dw3x3_i8_kernel", "res_dw_i8_s2": "dw3x3_kernel",
+              "res_f32": "direct_f32"}
+
+
+def _residual(layer, shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    if layer.dtype == "i8":
+        return torch.randint(-127, 128, shape, generator=g, dtype=torch.int8)
+    r = torch.randn(shape, generator=g)
+    return r.to(torch.bfloat16) if layer.dtype == "bf16" else r
+
+
+@pytest.mark.parametrize("layer", RES, ids=[l.name for l in RES])
+def test_residual_epilogue(layer):
+    t = random_layer_tensors(layer, LAW[layer.dtype], seed=23)
+    ref = H.oracle_full(layer, t["x"], t)
+    algo = 0
+    if layer.name.endswith("_xl"):
+        algo = next(a for a in forced_tiles(layer) if a in XL_ALGOS)
+    elif layer.name.endswith("_patch"):
+        algo = ALGO_PATCH
+    conv = _lib.Conv2d.from_layer(layer, algo=algo)
+    d = conv.describe()
+    want = RES_KERNEL.get(layer.name)
+    assert want is None or want in d, (layer.name, d)
+    if layer.name.endswith("splitk"):
+        assert "ksplit=1 " not in d, d
+    w = t["w"].cuda()
+    b = (_lib.pack_bias_scale(t["b"], t.get("s")) if layer.dtype == "i8" else t["b"]).cuda()
+    res = _residual(layer, conv.out_shape, seed=24)
+    for inplace in ((False, True) if layer.name in ("res_bf16_tap", "res_i8_tap") else (False,)):
+        rg = res.cuda()
+        y = rg if inplace else conv.empty_output()
+        conv.run(t["x"].cuda(), w, b, y, residual=rg)
+        torch.cuda.synchronize()
+        what = "%s inplace=%s [%s]" % (layer.name, inplace, d)
+        yc = y.cpu()
+        if layer.dtype == "i8":
+            q, m = oracle.add_residual_i8(ref[1], res.numpy())
+            H.check_int(yc.numpy(), (q, m), layer, what)
+        else:
+            rv = res.float().numpy()
+            r, a = oracle.add_residual_float(ref[0], ref[1], rv)
+            H.check_float(yc.float().numpy(), r, a, layer.dtype, what)
+    conv.close()
