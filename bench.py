@@ -363,7 +363,42 @@ def secondary_measurements():
                      "tflops": round(tot_flop / (tot_us * 1e-6) / 1e12, 2)}
     out["spp_bf16"] = spp_measurements(gen)
     out["upcat_bf16"] = upcat_measurements(gen)
+    out["residual_bf16"] = residual_measurements(gen)
     return out
+
+
+def residual_measurements(gen):
+    """The residual-add epilogue on a CSPDarknet ResBlock tail of the 640-pixel
+    network (3x3, 64 -> 64 channels, Mish, 320x320, N=1 and N=16): the same
+    layer through conv_run and through conv_run_residual. Cold buffer sets;
+    the residual adds one read of y's size."""
+    import torch
+
+    from convolution_conv2d_nhwc_amd import _lib
+    from convolution_conv2d_nhwc_amd.data import Layer
+
+    rows = []
+    for n in (1, 16):
+        layer = Layer("resblock_3x3_64", n, 320, 320, 64, 64, 3, 3, 1, 1, 1, 1, 1, "bf16", "bf16", "mish", 320, 320)
+        conv = _lib.Conv2d.from_layer(layer)
+        w = (torch.randn((64, 3, 3, 64), generator=gen, device="cuda") * (2.0 / 576) ** 0.5).to(torch.bfloat16)
+        b = (torch.rand(64, generator=gen, device="cuda") * 0.2 - 0.1).float()
+        xy = layer.bytes()
+        nsets = max(2, min(32, -(-768 * 2 ** 20 // (xy + 2 * n * 320 * 320 * 64))))
+        xs = [(torch.randn((n, 320, 320, 64), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+              for _ in range(nsets)]
+        rs = [(torch.randn((n, 320, 320, 64), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+              for _ in range(nsets)]
+        ys = [conv.empty_output() for _ in range(nsets)]
+        plain = _time_graph([lambda i=i: conv.run(xs[i], w, b, ys[i]) for i in range(nsets)])
+        fused = _time_graph([lambda i=i: conv.run(xs[i], w, b, ys[i], residual=rs[i]) for i in range(nsets)])
+        rows.append({"layer": "%dx320x320x64 3x3 -> 64, Mish" % n, "kernel": conv.describe().split("kernel=")[-1],
+                     "us_plain": round(plain, 2), "us_residual": round(fused, 2),
+                     "extra_mb": round(2 * n * 320 * 320 * 64 / 1e6, 2), "buffer_sets": nsets})
+        del xs, rs, ys
+        conv.close()
+        torch.cuda.empty_cache()
+    return {"layers": rows}
 
 
 def _time_graph(fn_list):
