@@ -142,3 +142,27 @@ def test_dw_probe_sampled(name):
         torch.cuda.synchronize()
         H.check_layer_sampled(layer, p["x"], p, y, count=3000, what="%s/%s [%s]" % (name, layer.name, conv.describe()))
         conv.close()
+
+
+@pytest.mark.gpu
+def test_residual_resblock_full_size():
+    """The residual epilogue at the size bench.py times it: a CSPDarknet
+    ResBlock tail of the 640-pixel network (3x3, 64 -> 64, Mish, 320x320,
+    N=1, bf16), every output against the oracle's activation plus the
+    residual, and in place."""
+    from convolution_conv2d_nhwc_amd.data import Layer, random_layer_tensors
+    layer = Layer("resblock_3x3_64", 1, 320, 320, 64, 64, 3, 3, 1, 1, 1, 1, 1, "bf16", "bf16", "mish", 320, 320)
+    t = random_layer_tensors(layer, "bf16", seed=7)
+    ref = H.oracle_full(layer, t["x"], t)
+    g = torch.Generator().manual_seed(8)
+    res = (torch.randn((1, 320, 320, 64), generator=g) * 0.5).to(torch.bfloat16)
+    r, a = oracle.add_residual_float(ref[0], ref[1], res.float().numpy())
+    conv = _lib.Conv2d.from_layer(layer)
+    x, w, b = t["x"].cuda(), t["w"].cuda(), t["b"].cuda()
+    for inplace in (False, True):
+        rg = res.cuda()
+        y = rg if inplace else conv.empty_output()
+        conv.run(x, w, b, y, residual=rg)
+        torch.cuda.synchronize()
+        H.check_float(y.cpu().float().numpy(), r, a, "bf16", "resblock inplace=%s [%s]" % (inplace, conv.describe()))
+    conv.close()
