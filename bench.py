@@ -248,6 +248,11 @@ def main():
     roof["avg_launch_us"] = avg_us
     roof["algorithmic_per_launch"] = {"flop": fl, "bytes": by}
     roof["event_gap_us"] = ev_gap_us
+    # the same fraction against what this GPU measurably sustains: a 1 GiB
+    # device-to-device copy (read + write) for HBM-bound work
+    copy_gbs = measured_copy_gbs()
+    roof["measured_peak"] = {"what": "1 GiB device copy, read+write", "value": round(copy_gbs, 1), "unit": "GB/s",
+                             "frac": (by / (avg_us * 1e-6) / 1e9) / copy_gbs}
 
     total_flop = wl.flops()
     value = total_flop / (ms_per_step * 1e-3) / 1e12
@@ -286,6 +291,31 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)
+
+
+def measured_copy_gbs() -> float:
+    """Bytes moved per second (read + write) by torch's device copy of a
+    1 GiB buffer, best of 5 timed runs after 2 warm-ups."""
+    import torch
+
+    n = 2 ** 30 // 4
+    x = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(2):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        y.copy_(x)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del x, y
+    torch.cuda.empty_cache()
+    return 2 * 2 ** 30 / (best * 1e-3) / 1e9
 
 
 def secondary_measurements():
@@ -364,6 +394,12 @@ def secondary_measurements():
     out["spp_bf16"] = spp_measurements(gen)
     out["upcat_bf16"] = upcat_measurements(gen)
     out["residual_bf16"] = residual_measurements(gen)
+    copy = measured_copy_gbs()
+    out["measured_copy_gbs"] = round(copy, 1)
+    for sec in out.values():
+        for row in sec.get("layers", []) if isinstance(sec, dict) else []:
+            if "gbs" in row:
+                row["frac_measured_copy"] = round(row["gbs"] / copy, 4)
     return out
 
 

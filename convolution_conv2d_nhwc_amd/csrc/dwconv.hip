@@ -30,6 +30,13 @@
 #ifndef DW_BF16_PW
 #define DW_BF16_PW 2
 #endif
+// Cache policy of the row-window kernels' output stores: non-temporal (the
+// output streams out; measured on the N=16 probe: 4 % faster for bf16,
+// 10 % for int8). A chained network that wants the next layer to find its
+// input in the caches can build with 0.
+#ifndef DW_ST_AUX
+#define DW_ST_AUX 2
+#endif
 #ifndef DW_MIN_LANES_PER_CU
 #define DW_MIN_LANES_PER_CU 256
 #endif
@@ -492,7 +499,7 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
           __builtin_amdgcn_raw_buffer_store_b128(
               i32x4{__builtin_bit_cast(int, v[4 * q]), __builtin_bit_cast(int, v[4 * q + 1]),
                     __builtin_bit_cast(int, v[4 * q + 2]), __builtin_bit_cast(int, v[4 * q + 3])},
-              ry, (int)(off + 16 * q), 0, 0);
+              ry, (int)(off + 16 * q), 0, DW_ST_AUX);
       } else {
         float v[VE];
 #pragma unroll
@@ -506,9 +513,9 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
 #pragma unroll
         for (int q = 0; q < VE / 2; ++q) wd[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
         if constexpr (VE == 8)
-          __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]}, ry, (int)off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]}, ry, (int)off, 0, DW_ST_AUX);
         else
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{wd[0], wd[1]}, ry, (int)off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{wd[0], wd[1]}, ry, (int)off, 0, DW_ST_AUX);
       }
     }
     yoff += yrow;
@@ -615,7 +622,7 @@ __global__ __launch_bounds__(256) void dw3x3_i8_kernel(DwArgs a) {
       if constexpr (OUT == OUT_I32) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = ACT == ACT_RELU ? max(acc[e], 0) : acc[e];
-        __builtin_amdgcn_raw_buffer_store_b128(i32x4{acc[0], acc[1], acc[2], acc[3]}, ry, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(i32x4{acc[0], acc[1], acc[2], acc[3]}, ry, (int)off, 0, DW_ST_AUX);
       } else {
         uint32_t q[4];
         if (has_res) {
@@ -629,7 +636,7 @@ __global__ __launch_bounds__(256) void dw3x3_i8_kernel(DwArgs a) {
         // low bytes of q0..q3 into one word
         const uint32_t lo = __builtin_amdgcn_perm(q[1], q[0], 0x0C0C0400u);
         const uint32_t hi = __builtin_amdgcn_perm(q[3], q[2], 0x0C0C0400u);
-        __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(hi, lo, 0x05040100u), ry, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32((int)__builtin_amdgcn_perm(hi, lo, 0x05040100u), ry, (int)off, 0, DW_ST_AUX);
       }
     }
     yoff += yrow;
