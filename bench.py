@@ -519,7 +519,7 @@ def spp_measurements(gen):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1000.0 / (reps * nsets)
         by = 5 * xb
-        rows.append({"shape": "x".join(map(str, shape)), "kernel": "spp_kernel<1>", "us": round(us, 2),
+        rows.append({"shape": "x".join(map(str, shape)), "kernel": "spp_kernel<1, %d>" % (2 if 4 * xb >= 8 << 20 else 0), "us": round(us, 2),
                      "gbs": round(by / (us * 1e-6) / 1e9, 1), "bound": "hbm",
                      "frac_hbm_peak": round(by / (us * 1e-6) / 1e9 / HBM_GBS, 4), "buffer_sets": nsets})
         del xs, ys, g

@@ -30,6 +30,9 @@ struct UpcatArgs {
 
 // Each lane moves CPT chunks of the row, 256 chunks apart: all loads are
 // issued before the first store, so CPT loads per lane are in flight.
+#ifndef UPCAT_ST_AUX
+#define UPCAT_ST_AUX 2  // non-temporal output stores
+#endif
 #ifndef UPCAT_CPT
 #define UPCAT_CPT 2
 #endif
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(256) void upcat_kernel(UpcatArgs a) {
   for (int c = 0; c < CPT; ++c) {
     const int t = (blockIdx.x * CPT + c) * 256 + threadIdx.x;
     const uint32_t dst = t < a.chunks_row ? ybase + (uint32_t)t * 16u : 0x80000000u;
-    __builtin_amdgcn_raw_buffer_store_b128(v[c], ry, (int)dst, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v[c], ry, (int)dst, 0, UPCAT_ST_AUX);
   }
 }
 
