@@ -1,6 +1,7 @@
-// igemm_xl.hip -- implicit-GEMM convolution for large layers: 256-wide
-// workgroup tiles, a 128x128 (or 128x64 / 64x128) output block per wave, and
-// a software pipeline that keeps the matrix cores fed from one wave per SIMD.
+// igemm_xl.hip -- implicit-GEMM convolution for large layers: 256- and
+// 128-channel by 128- to 256-pixel workgroup tiles, a 128x112 to 128x128
+// output block per wave (64x112 to 64x128 for 128-channel tiles), and a
+// software pipeline that keeps the matrix cores fed from one wave per SIMD.
 //
 // The GEMM view, operand layout, buffer loads and LDS swizzle are those of
 // igemm.hip; this kernel differs in how it spends LDS bandwidth and latency.
@@ -8,24 +9,24 @@
 // LDS bandwidth. Every MFMA operand is read from LDS once per wave, so the
 // bytes read per MFMA fall as the wave's output block grows: a 128x128 block
 // reads (128 + 128) rows per K-step for 64 MFMAs, a quarter of what a 32x32
-// block needs per MFMA. With 2x2 waves of 128x128 a K-tile of 128 bytes costs
-// 128 KiB of LDS reads and 64 KiB of LDS writes per workgroup against 128
-// MFMAs (2048 cycles) per SIMD, i.e. about 1536 cycles of the CU's 128
-// bytes/cycle: the matrix cores, not the LDS, set the pace.
+// block needs per MFMA.
 //
-// Latency. With one wave per SIMD nothing hides a stall, so each K-tile is
-// split at its single barrier into two halves that never wait on their own
-// loads:
-//   half 1: read the K-step-1 operands of tile t from LDS; run the K-step-0
-//           MFMAs of tile t (operands read during the previous half 2);
-//           between them, write tile t+1 from registers into the other LDS
-//           buffer and issue the global loads of tile t+2 into the freed
-//           registers;
-//   barrier (tile t+1 is visible; nobody reads the buffer of tile t-1);
-//   half 2: read the K-step-0 operands of tile t+1; run the K-step-1 MFMAs of
-//           tile t.
-// Global loads get a whole K-tile (about 2000 cycles) to land, LDS reads a
-// half.
+// Loads. Operands go from global memory straight into LDS (buffer loads with
+// the LDS as destination, 16 bytes per lane, no registers); each lane fetches
+// the chunk that lands its 16 bytes at the XOR-swizzled position. Measured on
+// MI355X these loads move about 61 bytes per clock per CU and do not overlap
+// the MFMAs, so a K-tile costs about its MFMA cycles plus 17 clocks per KiB
+// loaded; conv_api.cpp picks the tile shape from that model.
+//
+// Pipeline. Two LDS buffers, one barrier per K-tile, each K-tile split at the
+// barrier into two halves that never wait on their own operands:
+//   half 1: run the K-step-0 MFMAs of tile t (operands read during the
+//           previous half 2) while reading the K-step-1 operands of tile t;
+//   barrier (the loads of tile t+1 have landed; nobody reads tile t's
+//           buffer any more);
+//   half 2: issue the loads of tile t+2 into tile t's buffer; run the
+//           K-step-1 MFMAs of tile t while reading the K-step-0 operands of
+//           tile t+1.
 //
 // Only the tap and 1x1 loaders (Cin * elem_size a multiple of 128 bytes) are
 // offered, and Cout must be a multiple of the channel tile, so every weight
