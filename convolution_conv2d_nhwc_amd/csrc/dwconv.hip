@@ -28,7 +28,7 @@
 #define DW_PF 2
 #endif
 #ifndef DW_BF16_PW
-#define DW_BF16_PW 2
+#define DW_BF16_PW 4
 #endif
 // Cache policy of the row-window kernels' output stores: non-temporal (the
 // output streams out; measured on the N=16 probe: 4 % faster for bf16,
