@@ -92,34 +92,39 @@ int choose_xl(const Geometry& g, int esz, int loader) {
 // of the 256 CUs and each split still has >= 8 K-tiles of 128 bytes: aim at
 // ~512 workgroups, at most 8 splits. The splits' raw partial sums go to a device
 // workspace owned by the plan; a second kernel adds them in split order and
-// applies the epilogue. If the workspace cannot be allocated (no device, out
-// of memory) the plan runs unsplit, which is slower but the same arithmetic
-// up to the order of the fp32 additions.
-void plan_split_k(conv_plan* p) {
+// applies the epilogue. Returns false when the workspace allocation fails
+// (CONV_E_NOMEM). With no HIP device at all the plan stays unsplit: it can be
+// described but not run.
+bool plan_split_k(conv_plan* p) {
   const Geometry& g = p->g;
   const TileCfg& t = p->path == PATH_XL ? kXlTiles[p->tile] : kTiles[p->tile];
   const long nwg = (long)((g.cout + t.tco - 1) / t.tco) * ((g.m + t.tpx - 1) / t.tpx);
   const int nkt = p->kt_per;
-  if (nwg >= 128 || nkt < 16 || (g.cout & 3)) return;
+  if (nwg >= 128 || nkt < 16 || (g.cout & 3)) return true;
   int s = (int)((512 + nwg - 1) / nwg);
   s = s < 8 ? s : 8;
   s = s < nkt / 8 ? s : nkt / 8;
-  if (s < 2) return;
+  if (s < 2) return true;
   const int per = (nkt + s - 1) / s;
   s = (nkt + per - 1) / per;
-  if (s < 2) return;
+  if (s < 2) return true;
   const int64_t bytes = (int64_t)s * g.m * g.cout * 4;
-  int dev = 0;
+  int dev = 0, ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0 || hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();  // no device: an unsplit plan that cannot run anyway
+    return true;
+  }
   void* ws = nullptr;
-  if (hipGetDevice(&dev) != hipSuccess || hipMalloc(&ws, bytes) != hipSuccess) {
-    (void)hipGetLastError();  // clear the failure; run unsplit
-    return;
+  if (hipMalloc(&ws, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
   }
   p->ksplit = s;
   p->kt_per = per;
   p->ws = ws;
   p->ws_bytes = bytes;
   p->ws_device = dev;
+  return true;
 }
 
 bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
@@ -165,6 +170,9 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
   const int64_t w_bytes = d->c_out * (int64_t)d->kh * d->kw * cg * in_esz;
   const int64_t y_bytes = d->n * ho * wo * d->c_out * out_esz;
   if (x_bytes >= kMaxBytes || w_bytes >= kMaxBytes || y_bytes >= kMaxBytes) return CONV_E_UNSUPPORTED;
+  // The kernels split a reduction index into (tap, channel) with an fp32
+  // reciprocal, exact below 2^24.
+  if ((int64_t)d->kh * d->kw * cg * in_esz >= ((int64_t)1 << 24)) return CONV_E_UNSUPPORTED;
 
   int path;
   int loader = LOAD_GENERIC;
@@ -262,7 +270,10 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
   }
   p->ksplit = 1;
   p->kt_per = (int)((g.k * (int64_t)in_esz + 127) / 128);
-  if (path == PATH_IGEMM || path == PATH_XL) plan_split_k(p);
+  if ((path == PATH_IGEMM || path == PATH_XL) && !plan_split_k(p)) {
+    delete p;
+    return CONV_E_NOMEM;
+  }
   p->x_bytes = x_bytes;
   p->w_bytes = w_bytes;
   p->y_bytes = y_bytes;
@@ -480,7 +491,7 @@ const char* conv_status_str(int32_t status) {
     case CONV_E_UNSUPPORTED: return "CONV_E_UNSUPPORTED: layer kind, dtype, activation, algo or size not supported";
     case CONV_E_ALIGN: return "CONV_E_ALIGN: x, w, y need 16-byte and b 4-byte alignment";
     case CONV_E_ALIAS: return "CONV_E_ALIAS: output overlaps an input";
-    case CONV_E_NOMEM: return "CONV_E_NOMEM: plan allocation failed";
+    case CONV_E_NOMEM: return "CONV_E_NOMEM: plan or split-K workspace allocation failed";
     case CONV_E_HIP:
       std::snprintf(buf, sizeof(buf), "CONV_E_HIP: %s", g_last_hip_error);
       return buf;

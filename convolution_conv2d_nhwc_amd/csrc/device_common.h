@@ -40,21 +40,6 @@ __device__ __forceinline__ float mish_f32(float v) {
   return v * (n * __builtin_amdgcn_rcpf(n + 2.0f));
 }
 
-// Mish for outputs that are rounded to bf16 or to an integer afterwards, in
-// seven instructions (two of them transcendental) instead of nine: the same
-// function written as v - 2v / ((1 + e^v)^2 + 1), the section 9 form. No
-// clamp is needed: e^v = inf gives v, e^v = 0 gives 0. For v < 0 the
-// subtraction loses relative accuracy (the absolute error stays about
-// |v| * 2^-22), which is far below the rounding of a bf16 output at the scale
-// of its layer, and an int8 output never rounds near there (|Mish(v)| < 0.31
-// for v < 0). For v > 0 the quotient is at most 0.2 and there is no
-// cancellation.
-__device__ __forceinline__ float mish_lo(float v) {
-  const float u = __builtin_amdgcn_exp2f(v * 1.44269504088896341f) + 1.0f;
-  const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(u, u, 1.0f));
-  return __builtin_fmaf(-2.0f * v, r, v);
-}
-
 __device__ __forceinline__ float apply_act(float v, int act) {
   switch (act) {
     case ACT_RELU: return fmaxf(v, 0.0f);
@@ -74,12 +59,30 @@ __device__ __forceinline__ int requant_i8(int r, float s, int act) {
   return (int)q;
 }
 
-// With a residual rr added after the activation (see requant_i8_res_t).
+// Q = clamp(round_half_even(m + rr), -127, 127) for a float m and an
+// integer rr, with one rounding of the exact sum (a plain float add of m and
+// rr can round before the integer rounding does). With q0 = rne(m) and the
+// remainder d = m - q0 (exact: |d| <= 1/2, and m and q0 are within a factor
+// of two of each other unless q0 = 0), m + rr = (q0 + rr) + d. For |d| < 1/2
+// the nearest integer is q0 + rr. For d = +-1/2 the sum is a tie between
+// q0 + rr and q0 + rr + 2d; q0 is even (it is itself a tie broken to even),
+// so the even neighbour is q0 + rr when rr is even and q0 + rr + 2d when rr
+// is odd. m is first clamped to +-2^20, beyond which the result saturates
+// either way; adding 1.5 * 2^23 then rounds half to even in the adder.
+__device__ __forceinline__ int round_add_sat_i8(float m, int rr) {
+  const float c = __builtin_amdgcn_fmed3f(m, -1048576.0f, 1048576.0f);
+  const float t = c + 12582912.0f;
+  const int q0 = (int)(__builtin_bit_cast(uint32_t, t) - 0x4B400000u);
+  const float d = c - (t - 12582912.0f);
+  const int tie = (rr & 1) && __builtin_fabsf(d) == 0.5f ? (d > 0.0f ? 1 : -1) : 0;
+  return min(max(q0 + rr + tie, -127), 127);
+}
+
+// With a residual rr added after the activation: Q = clamp(rne(act(v) + rr),
+// -127, 127).
 __device__ __forceinline__ int requant_i8_res(int r, float s, int act, int rr) {
   const float v = __fmul_rn((float)r, s);
-  const float m = fminf(fmaxf(apply_act(v, act), -1048576.0f), 1048576.0f);
-  const int q = (int)__builtin_rintf(m);
-  return min(max(q + rr, -127), 127);
+  return round_add_sat_i8(apply_act(v, act), rr);
 }
 
 // Compile-time loop: f(std::integral_constant<int, i>) for i = I .. N-1.
@@ -113,15 +116,6 @@ __device__ __forceinline__ float act_t(float v) {
     return v;
 }
 
-// act_t with mish_lo: for bf16 and int8 outputs
-template <int ACT>
-__device__ __forceinline__ float act_lo_t(float v) {
-  if constexpr (ACT == ACT_MISH)
-    return mish_lo(v);
-  else
-    return act_t<ACT>(v);
-}
-
 // The int8 requantisation with the activation fixed at compile time. The
 // saturation comes first (the bounds are integers, so clamping before or
 // after rounding is the same); adding 1.5 * 2^23 then rounds half to even in
@@ -137,15 +131,12 @@ __device__ __forceinline__ uint32_t requant_i8_word_t(int r, float s) {
   else if constexpr (ACT == ACT_RELU6)
     c = __builtin_amdgcn_fmed3f(v, 0.0f, 6.0f);
   else
-    c = __builtin_amdgcn_fmed3f(act_lo_t<ACT>(v), -127.0f, 127.0f);
+    c = __builtin_amdgcn_fmed3f(act_t<ACT>(v), -127.0f, 127.0f);
   return __builtin_bit_cast(uint32_t, c + 12582912.0f);
 }
 // The same with a residual rr (an int8 value in the output's units) added
-// after the activation: Q = clamp(rne(act(v) + rr), -127, 127). rr is an
-// integer, so rne(m + rr) = rne(m) + rr exactly: the activation's value is
-// rounded first (clamped to +-2^20 so that the adder rounds it; beyond that
-// it saturates either way), then rr is added in integers before the
-// saturation.
+// after the activation: Q = clamp(rne(act(v) + rr), -127, 127), the sum
+// rounded once (round_add_sat_i8).
 template <int ACT>
 __device__ __forceinline__ int requant_i8_res_t(int r, float s, int rr) {
   const float v = __fmul_rn((float)r, s);
@@ -155,10 +146,8 @@ __device__ __forceinline__ int requant_i8_res_t(int r, float s, int rr) {
   else if constexpr (ACT == ACT_RELU6)
     m = __builtin_amdgcn_fmed3f(v, 0.0f, 6.0f);
   else
-    m = act_lo_t<ACT>(v);
-  const float c = __builtin_amdgcn_fmed3f(m, -1048576.0f, 1048576.0f);
-  const int q = (int)(__builtin_bit_cast(uint32_t, c + 12582912.0f) - 0x4B400000u);
-  return min(max(q + rr, -127), 127);
+    m = act_t<ACT>(v);
+  return round_add_sat_i8(m, rr);
 }
 
 template <int ACT>

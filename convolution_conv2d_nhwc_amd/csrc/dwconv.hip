@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void dw3x3_kernel(DwArgs a) {
 #pragma unroll
       for (int e = 0; e < VE; ++e)
         v[e] = (sizeof(T) == 4 ? act_t<ACT>(acc[p][e] + (a.e.bias ? a.e.bias[c0 + e] : 0.0f))
-                               : act_lo_t<ACT>(acc[p][e] + (a.e.bias ? a.e.bias[c0 + e] : 0.0f)));
+                               : act_t<ACT>(acc[p][e] + (a.e.bias ? a.e.bias[c0 + e] : 0.0f)));
       if (a.e.res) {
 #pragma unroll
         for (int e = 0; e < VE; ++e) v[e] += Elt<T>::get1(static_cast<const char*>(a.e.res) + (off + e) * sizeof(T));
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
       } else {
         float v[VE];
 #pragma unroll
-        for (int e = 0; e < VE; ++e) v[e] = act_lo_t<ACT>(acc[p][e]);
+        for (int e = 0; e < VE; ++e) v[e] = act_t<ACT>(acc[p][e]);
         if (has_res) {
           RawVec<T, VE> rv = load_raw<T, VE>(rr, off);
 #pragma unroll

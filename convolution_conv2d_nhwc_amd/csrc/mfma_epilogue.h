@@ -203,7 +203,7 @@ __device__ __forceinline__ void store_quad_t(const acc_t& v, const QuadConsts& q
   if constexpr (ESZ == 2) {
     float f[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) f[r] = act_lo_t<ACT>(v[r] + q.bsf[r]);
+    for (int r = 0; r < 4; ++r) f[r] = act_t<ACT>(v[r] + q.bsf[r]);
     if (o.has_res) {
       const u32x2 rv = __builtin_amdgcn_raw_buffer_load_b64(o.rr, in ? idx * 2u : kNowhere, 0, 0);
 #pragma unroll

@@ -1,6 +1,6 @@
 // spp.hip -- SPP max-pool block: the 13x13, 9x9 and 5x5 stride-1 max pools
 // of an NHWC map and the map itself, concatenated along channels (zerolat.eu
-// YOLOv4 report, section 10 kernel table, K3; section 3 names SPP as the
+// YOLOv4 report, section 9 "Four custom Tensix kernels", K3; section 3 names SPP as the
 // block that widens the context with those three windows).
 //
 // The larger windows come from cascaded 5x5 pools, the identity the report's

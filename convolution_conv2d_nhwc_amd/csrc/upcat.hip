@@ -1,6 +1,6 @@
 // upcat.hip -- nearest-neighbour 2x upsampling and channel concatenation of
 // two maps, written straight into the NHWC input of the next convolution
-// (zerolat.eu YOLOv4 report, section 10 kernel table, K4: the neck gathers
+// (zerolat.eu YOLOv4 report, section 9 "Four custom Tensix kernels", K4: the neck gathers
 // two feature maps, repeats one 2x in rows and columns and joins them along
 // channels in the layout the following convolution reads).
 //

@@ -1,0 +1,107 @@
+"""Stack executor: a chained workload as one sequence of launches on one
+stream, each layer writing straight into the next layer's preallocated NHWC
+input buffer, captured once into a HIP graph and replayed.
+
+This is the host-side runtime of the layer stacks (the 640x640 YOLO stack
+with its mosaic, the keyword-spotting and visual-wake-words stacks). It
+follows the pages' runtime lessons: record the model work once and replay
+it, and remove copies and moves between operations (zerolat.eu YOLOv4
+report, section 10 "Runtime and I/O changes on the card", and its note on
+why reducing the operation count matters); per-call host cost removed by
+graph replay (nanoinfer README, GPU section: back-to-back launches against a
+replayed graph). Every launch is a library call through the C ABI; the
+executor only owns buffers and the order of the calls.
+"""
+from __future__ import annotations
+
+from typing import Callable, List, Optional
+
+import torch
+
+from . import _lib
+from .data import Workload, layer_params, network_input
+
+
+class Stack:
+    """Plans, resident weights and buffers of a workload on the current
+    device. ``step()`` enqueues one pass on the current stream;
+    ``capture()`` records one pass into a graph that ``replay()`` runs."""
+
+    def __init__(self, wl: Workload, seed: int = 0, device: str = "cuda"):
+        if not wl.chained and len(wl.layers) != 1:
+            raise ValueError("%s is neither a chained stack nor a single layer" % wl.name)
+        self.wl = wl
+        self.convs: List[_lib.Conv2d] = []
+        self.params = []
+        self.bufs: List[torch.Tensor] = []
+        for i, layer in enumerate(wl.layers):
+            p = layer_params(wl, i, seed)
+            conv = _lib.Conv2d.from_layer(layer)
+            dev = {"w": p["w"].to(device)}
+            if layer.dtype == "i8":
+                dev["b"] = _lib.pack_bias_scale(p["b"], p.get("s") if layer.out == "i8" else None).to(device)
+            else:
+                dev["b"] = p["b"].to(device)
+            self.convs.append(conv)
+            self.params.append(dev)
+            self.bufs.append(conv.empty_output(device))
+        self.x0 = (network_input(wl, seed) if wl.chained else layer_params(wl, 0, seed)["x"]).to(device)
+        self.canvas: Optional[torch.Tensor] = None
+        if wl.mosaic is not None:
+            m, th, tw, c = wl.mosaic
+            self.canvas = torch.empty((m, 2 * th, 2 * tw, c), dtype=torch.bfloat16, device=device)
+        self.graph: Optional[torch.cuda.CUDAGraph] = None
+
+    # each layer's input: the canvas (or the network input), then the
+    # previous layer's output buffer
+    def layer_input(self, i: int) -> torch.Tensor:
+        if i > 0:
+            return self.bufs[i - 1]
+        return self.canvas if self.canvas is not None else self.x0
+
+    def launches(self) -> List[Callable[[], None]]:
+        """The pass as a list of single-kernel-call closures, in order."""
+        seq: List[Callable[[], None]] = []
+        if self.canvas is not None:
+            seq.append(lambda: _lib.mosaic_pack(self.x0, self.canvas, out_dtype=torch.bfloat16))
+        for i in range(len(self.convs)):
+            seq.append(lambda i=i: self.convs[i].run(self.layer_input(i), self.params[i]["w"], self.params[i]["b"],
+                                                     self.bufs[i]))
+        return seq
+
+    def step(self) -> torch.Tensor:
+        for f in self.launches():
+            f()
+        return self.bufs[-1]
+
+    def capture(self, warmup: int = 3) -> torch.cuda.CUDAGraph:
+        """Run `warmup` eager passes on a side stream, then record one pass."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(warmup):
+                self.step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
+
+    def replay(self) -> torch.Tensor:
+        if self.graph is None:
+            raise RuntimeError("capture() first")
+        self.graph.replay()
+        return self.bufs[-1]
+
+    @property
+    def output(self) -> torch.Tensor:
+        return self.bufs[-1]
+
+    def close(self):
+        self.graph = None
+        for c in self.convs:
+            c.close()
+        self.convs = []

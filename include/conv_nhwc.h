@@ -84,10 +84,12 @@ typedef enum conv_status {
   CONV_OK = 0,
   CONV_E_NULL = -1,        /* a required pointer is NULL */
   CONV_E_SHAPE = -2,       /* non-positive size, empty output, c_in or c_out not divisible by groups */
-  CONV_E_UNSUPPORTED = -3, /* groups not in {1, c_in==c_out}, depthwise not 3x3, dtype/out/act combination, size limit, bad algo */
+  CONV_E_UNSUPPORTED = -3, /* groups not in {1, c_in==c_out}, depthwise not 3x3, dtype/out/act combination, size limit
+                              (a tensor of 2^31 bytes or more, a reduction kh*kw*c_in/groups of 2^24 bytes or more),
+                              bad algo */
   CONV_E_ALIGN = -4,       /* x, w or y not 16-byte aligned, or b not 4-byte aligned */
   CONV_E_ALIAS = -5,       /* y overlaps x, w or b */
-  CONV_E_NOMEM = -6,       /* host allocation of the plan failed */
+  CONV_E_NOMEM = -6,       /* allocation of the plan, or of its split-K workspace, failed */
   CONV_E_HIP = -7          /* the HIP launch reported an error */
 } conv_status;
 
@@ -117,9 +119,17 @@ typedef struct conv_desc {
 typedef struct conv_plan conv_plan;
 
 /* Validate d and choose the kernel and its launch shape. On success *out
- * holds a new plan (free with conv_destroy). The only device call is the
- * allocation of a split-K workspace when the plan splits the reduction; if
- * that allocation fails the plan runs unsplit instead. */
+ * holds a new plan (free with conv_destroy); on failure *out is NULL and the
+ * return value names the reason. Every unsupported layer is refused here,
+ * before any buffer is bound, by a named code rather than a wrong result
+ * later (nanoinfer README, the bug list: op/dtype pairs are validated at load
+ * so that an unsupported pair is a named load failure; SiMa box-decode page,
+ * the YOLO profile: preparation validates the profile and returns a plan that
+ * states what execution needs). The only device call is the allocation of the
+ * split-K workspace when the plan splits the reduction (conv_describe shows
+ * ksplit > 1), on the device current at this call: if that allocation fails,
+ * CONV_E_NOMEM. With no HIP device present at all the plan is made unsplit
+ * (it can be inspected but not run). */
 conv_status conv_prepare(const conv_desc* d, conv_plan** out);
 
 /* Enqueue the layer on `stream` (a hipStream_t; NULL = the default stream).
@@ -141,14 +151,17 @@ conv_status conv_run(const conv_plan* p, const void* x, const void* w,
                      const void* b, void* y, void* stream);
 
 /* conv_run with a residual added after the activation, written once (YOLOv4
- * on Tenstorrent Wormhole, section 10 kernel table, K2: the ResBlock tail
+ * on Tenstorrent Wormhole, section 9 "Four custom Tensix kernels", K2: the ResBlock tail
  * computes Mish and adds the skip tensor in one pass instead of storing and
  * reloading the activation):
  *   F32  : y = act(conv + b) + r                      (one fp32 add)
  *   BF16 : y = bf16_rne(act(conv + b) + r)            (sum in fp32, one rounding)
  *   I8   : y = clamp(round_half_even(act(v) + r), -127, 127)
- *          with v as for conv_run and r an int8 value in the output's units
- *          (computed exactly as round_half_even(act(v)) + r before the clamp)
+ *          with v as for conv_run and r an int8 value in the output's units:
+ *          the exact sum act(v) + r is rounded once (at a half-integer the
+ *          even neighbour of the sum wins, e.g. act(v) = 2.5, r = 1 gives 4),
+ *          so no intermediate rounding of the activation comes before the
+ *          add, as in K2
  *   r : device NHWC [n][ho][wo][c_out] of out_dtype, 16-byte aligned. It may
  *       be y itself (in-place add) but must not otherwise overlap y.
  * The int32 checkpoint output (I8 -> I32) gives CONV_E_UNSUPPORTED. Other
@@ -156,10 +169,17 @@ conv_status conv_run(const conv_plan* p, const void* x, const void* w,
 conv_status conv_run_residual(const conv_plan* p, const void* x, const void* w,
                               const void* b, const void* r, void* y, void* stream);
 
-/* Free a plan. NULL is a no-op. */
+/* Free a plan and the workspace conv_prepare allocated for it; all device
+ * memory a plan holds is taken at preparation and given back here, none in
+ * between (nanoinfer README, memory planner: no allocations in the forward
+ * pass after load). NULL is a no-op. Always CONV_OK. */
 conv_status conv_destroy(conv_plan* p);
 
-/* Output shape {n, ho, wo, c_out} of a plan. */
+/* Output shape {n, ho, wo, c_out} of a plan: ho = (h + 2*pad_h - kh) /
+ * stride_h + 1 and wo likewise, the floor rule of PyTorch from which the
+ * nanoinfer engine takes its shapes (nanoinfer README, the bug list:
+ * asymmetric padding collapsed to one axis; the output shapes came from
+ * PyTorch). CONV_E_NULL if p or nhwc is NULL. */
 conv_status conv_out_shape(const conv_plan* p, int64_t nhwc[4]);
 
 /* Human-readable description of the chosen kernel path and tile, written
@@ -183,8 +203,8 @@ conv_status conv_mosaic_pack(const void* tiles, int32_t in_dtype, void* canvas,
                              int32_t tw, int32_t c, int32_t c_pad,
                              void* stream);
 
-/* SPP max-pool block (YOLOv4 on Tenstorrent Wormhole, section 10 kernel
- * table, K3; section 3 for the block's role): for each pixel, the maximum over
+/* SPP max-pool block (YOLOv4 on Tenstorrent Wormhole, section 9 "Four custom
+ * Tensix kernels", K3; section 3 for the block's role): for each pixel, the maximum over
  * the 13x13, 9x9 and 5x5 windows centred on it (stride 1, output the size of
  * the input, positions outside the map ignored, i.e. padding with -infinity),
  * concatenated with the map itself:
@@ -198,8 +218,8 @@ conv_status conv_mosaic_pack(const void* tiles, int32_t in_dtype, void* canvas,
 conv_status conv_spp_maxpool(const void* x, int32_t dtype, void* y, int32_t n,
                              int32_t h, int32_t w, int32_t c, void* stream);
 
-/* Upsample x2 + concat (YOLOv4 on Tenstorrent Wormhole, section 10 kernel
- * table, K4): two maps joined along channels in the NHWC layout the next
+/* Upsample x2 + concat (YOLOv4 on Tenstorrent Wormhole, section 9 "Four custom
+ * Tensix kernels", K4): two maps joined along channels in the NHWC layout the next
  * convolution reads, each repeated 2x in rows and columns (nearest
  * neighbour) when its up flag is 1:
  *   y[n][i][j][k]      = s0[n][i >> up0][j >> up0][k]       k < c0
@@ -217,8 +237,11 @@ conv_status conv_upsample_concat(const void* s0, int32_t c0, int32_t up0,
                                  int32_t dtype, void* y, int32_t n, int32_t ho,
                                  int32_t wo, void* stream);
 
-/* Name of a status code ("CONV_OK", "CONV_E_SHAPE", ...). For CONV_E_HIP
- * the text of the last HIP error seen by this thread is appended. */
+/* Name and meaning of a status code ("CONV_OK", "CONV_E_SHAPE: ..."), so a
+ * refusal reads as a named failure rather than quiet garbage (nanoinfer
+ * README, the bug list). For CONV_E_HIP the text of the last HIP error seen
+ * by this thread is appended. The string is static or thread-local: valid
+ * until the next call on the same thread. */
 const char* conv_status_str(int32_t status);
 
 #ifdef __cplusplus

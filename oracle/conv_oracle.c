@@ -367,8 +367,8 @@ int oracle_mosaic(const float *tiles, int64_t m, int64_t th, int64_t tw,
 }
 
 /*
- * SPP max-pool block (zerolat.eu YOLOv4 report, section 10 kernel table, row
- * K3: the 5, 9 and 13 spatial max-pool windows of the SPP block; section 3
+ * SPP max-pool block (zerolat.eu YOLOv4 report, section 9 "Four custom Tensix
+ * kernels", K3: the 5, 9 and 13 spatial max-pool windows of the SPP block; section 3
  * names SPP as the block that combines local and wider context with those
  * three windows). Written from the definition of a stride-1 max pool whose
  * output has the input's size, NOT from the cascade identity the report's
@@ -434,8 +434,8 @@ int oracle_spp(const void *x, int dtype, int64_t n, int64_t h, int64_t w, int64_
 }
 
 /*
- * Upsample x2 + concat (zerolat.eu YOLOv4 report, section 10 kernel table,
- * row K4: two neck feature maps, one repeated 2x in rows and columns, joined
+ * Upsample x2 + concat (zerolat.eu YOLOv4 report, section 9 "Four custom Tensix
+ * kernels", K4: two neck feature maps, one repeated 2x in rows and columns, joined
  * along channels into the next convolution's input). Two sources s = 0, 1,
  * each [n][ho >> up_s][wo >> up_s][c_s] (up_s = 1: nearest-neighbour 2x
  * upsampling, every source pixel feeds a 2x2 block; up_s = 0: same size),

@@ -261,7 +261,7 @@ def upcat(s0, up0, s1, up1):
 
 def add_residual_float(r, a, res):
     """Residual-add epilogue for float outputs (zerolat.eu YOLOv4 report,
-    section 10 kernel table, K2: the activation, then the skip tensor added,
+    section 9 "Four custom Tensix kernels", K2: the activation, then the skip tensor added,
     the sum written once). r, a: the oracle's unrounded activation output and
     absolute-value convolution; res: the residual's values (fp32, or bf16
     widened exactly). Returns (r + res, a + |res|) in float64, unrounded."""

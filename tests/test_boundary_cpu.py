@@ -68,6 +68,10 @@ def prepare(d):
     (dict(algo=99), -3),
     (dict(dtype=0, out_dtype=0, algo=1), -3),      # algo only for the MFMA path
     (dict(n=1, h=1 << 15, w=1 << 15, c_in=8), -3),  # x over 2^31 bytes
+    # a reduction of 2^24 bytes per output (kh*kw*c_in*esz): the kernels'
+    # (tap, channel) split of a reduction index is exact only below that
+    (dict(n=1, h=1, w=1, c_in=1 << 23, c_out=1, kh=1, kw=1, pad_h=0, pad_w=0), -3),
+    (dict(n=1, h=1, w=1, c_in=1 << 24, c_out=1, kh=1, kw=1, pad_h=0, pad_w=0, dtype=2, out_dtype=2), -3),
 ])
 def test_prepare_rejects(kw, code):
     st, p = prepare(desc(**kw))

@@ -81,6 +81,11 @@ def test_float_matches_torch_float64(case):
     assert r.shape == ref.shape
     # double sums in another order: agree to rounding of the abs sum.
     assert np.all(np.abs(r - ref) <= 1e-12 * (a + 1.0))
+    # A, the absolute-value convolution that sets every float tolerance
+    # floor, is the same library conv on |x|, |w| and |b| (signed inputs, so
+    # a sum of |x*w| cannot pass as |sum x*w|).
+    ref_a = torch_conv_nhwc(np.abs(x), np.abs(w), np.abs(b), stride, pad, case["groups"])
+    assert np.all(np.abs(a - ref_a) <= 1e-12 * (ref_a + 1.0))
 
 
 @settings(max_examples=100, deadline=None)
@@ -279,7 +284,7 @@ def test_relu_relu6():
     (-40, 0.1, "relu", 0),      # ReLU before rounding
     (90, 0.1, "relu6", 6),      # 9.0 clamps to 6
     (55, 0.1, "relu6", 6),      # 5.5 -> 6 (tie to even)
-    (45, 0.1, "relu6", 4),      # fl32(45*0.1f) = 4.5000000... -> check below
+    (45, 0.1, "relu6", 4),      # 45*0.1f = 4.50000006..., which rounds to the float 4.5 -> 4 (tie to even)
     (0, 0.37, "mish", 0),
     (100, 0.05, "mish", 5),     # Mish(5.0) = 4.99954... -> 5
     (-100, 0.05, "mish", 0),    # Mish(-5) = -0.0336 -> 0
@@ -287,9 +292,9 @@ def test_relu_relu6():
 def test_requant_hand_values(r32, s, act, q):
     got, m = oracle.requant(r32, s, act)
     if (r32, s) == (45, 0.1):
-        # 0.1f is slightly above 0.1, so 45*0.1f rounds to a float just above
-        # 4.5 or exactly 4.5; either way the answer follows from m.
-        q = 5 if m > 4.5 else 4
+        # 0.1f = 0.100000001490116..., so the exact product is 4.5 + 6.7e-8,
+        # less than half a float32 ulp (2.4e-7) above 4.5: fl32 gives 4.5.
+        assert m == 4.5
     assert got == q
 
 

@@ -107,6 +107,52 @@ def test_yolo640_mosaic_and_chain():
         print(layer.name, s)
 
 
+@pytest.mark.parametrize("name", ["yolo640_bf16", "kws_int8", "vww_bf16", "mnist_f32"])
+def test_stack_graph_replay_matches_oracle(name):
+    """The exact graph bench.py times (the Stack executor: mosaic + every
+    layer captured once, replayed): after the first replay every layer's
+    output buffer is checked against the oracle chain (int8 bit-exact, bf16
+    under the chain rule, the single fp32 layer under the strict rule);
+    two more replays, with every buffer overwritten by eager fills in
+    between, and one eager pass must reproduce it bit for bit."""
+    from convolution_conv2d_nhwc_amd.stack import Stack
+    wl = workload(name)
+    st = Stack(wl)
+    st.capture()
+    st.replay()
+    torch.cuda.synchronize()
+    first = [b.clone() for b in st.bufs]
+    descs = [c.describe() for c in st.convs]
+    if wl.mosaic is not None:
+        bits = oracle.mosaic(network_input(wl).numpy(), out="bf16")
+        assert np.array_equal(st.canvas.cpu().view(torch.int16).numpy().view(np.uint16), bits), "mosaic"
+        x0 = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    elif wl.chained:
+        x0 = network_input(wl)
+    else:
+        x0 = None
+    if x0 is None:
+        p = layer_params(wl, 0)
+        H.check_layer_full(wl.layers[0], p["x"], p, first[0], "%s graph [%s]" % (name, descs[0]))
+    else:
+        stats = _oracle_chain_check(wl, x0, list(zip(first, descs)))
+        print(name, stats[-1])
+    for rep in range(2):
+        for b in st.bufs:
+            b.fill_(-77 if b.dtype == torch.int8 else float("nan") if b.dtype.is_floating_point else -(2 ** 30))
+        if st.canvas is not None:
+            st.canvas.zero_()
+        st.replay()
+        torch.cuda.synchronize()
+        for i, (b, f0) in enumerate(zip(st.bufs, first)):
+            assert torch.equal(b.view(torch.uint8), f0.view(torch.uint8)), (name, "replay", rep, i)
+    st.step()
+    torch.cuda.synchronize()
+    for i, (b, f0) in enumerate(zip(st.bufs, first)):
+        assert torch.equal(b.view(torch.uint8), f0.view(torch.uint8)), (name, "eager", i)
+    st.close()
+
+
 @pytest.mark.parametrize("name", ["yolo_sweep_int8", "yolo_sweep_bf16"])
 def test_yolo_sweep_sampled(name):
     wl = workload(name)
@@ -116,6 +162,23 @@ def test_yolo_sweep_sampled(name):
         torch.cuda.synchronize()
         s = H.check_layer_sampled(layer, p["x"], p, y, count=3000, what="%s/%s [%s]" % (name, layer.name, conv.describe()))
         print(name, layer.name, conv.describe(), s)
+        conv.close()
+        del y
+
+
+@pytest.mark.parametrize("name", ["yolo_sweep_int8", "yolo_sweep_bf16"])
+def test_yolo_sweep_full_elementwise(name):
+    """Every output of every N=16 sweep layer (each shipped kernel instance at
+    its real shape: the 128x128 implicit-GEMM tile on 160x160x128, the
+    large-layer tiles on the 80x80, 40x40 and 20x20 3x3 layers, the 1x1
+    loaders) against the oracle under the strict rules."""
+    wl = workload(name)
+    for i, layer in enumerate(wl.layers):
+        p = layer_params(wl, i)
+        y, conv = H.gpu_run(layer, p["x"], p)
+        torch.cuda.synchronize()
+        s = H.check_layer_full(layer, p["x"], p, y, "%s/%s full [%s]" % (name, layer.name, conv.describe()))
+        print(name, layer.name, conv.describe(), s, flush=True)
         conv.close()
         del y
 
