@@ -1,6 +1,6 @@
 """Build ``libconv_nhwc.so`` (the HIP library) in-tree for gfx950.
 
-Usage:  python -m convolution_conv2d_nhwc_amd.build [-v]
+Usage:  python -m convolution_conv2d_nhwc_amd.build [-v] [--incremental]
 
 Each source under ``csrc/`` is compiled with hipcc in parallel, then linked
 into ``convolution_conv2d_nhwc_amd/libconv_nhwc.so``. The flags disable the
@@ -33,8 +33,26 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _deps(path: str, seen=None) -> set:
+    """The file and every quoted #include it pulls in, recursively."""
+    seen = set() if seen is None else seen
+    if path in seen or not os.path.exists(path):
+        return seen
+    seen.add(path)
+    for line in open(path, errors="replace"):
+        line = line.strip()
+        if line.startswith("#include \""):
+            inc = line.split('"')[1]
+            _deps(os.path.normpath(os.path.join(os.path.dirname(path), inc)), seen)
+    return seen
+
+
+def _compile(src: str, verbose: bool, incremental: bool = False) -> str:
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
+    if incremental and os.path.exists(obj):
+        newest = max(os.path.getmtime(d) for d in _deps(src))
+        if os.path.getmtime(obj) >= newest:
+            return obj
     cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -47,12 +65,16 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link the shared library. Always rebuilds."""
+def build(verbose: bool = False, jobs: int = 8, incremental: bool = False) -> str:
+    """Compile every source and link the shared library. Rebuilds every
+    object unless `incremental`, which recompiles only objects older than
+    their source or a header it includes."""
     os.makedirs(OUT_DIR, exist_ok=True)
     srcs = sources()
+    # the longest compiles first
+    srcs.sort(key=lambda p: -os.path.getsize(p))
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        objs = list(ex.map(lambda s: _compile(s, verbose, incremental), srcs))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
@@ -63,5 +85,5 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
 
 if __name__ == "__main__":
-    t = build(verbose="-v" in sys.argv)
+    t = build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv)
     print(t)

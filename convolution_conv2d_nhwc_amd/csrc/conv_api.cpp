@@ -49,7 +49,7 @@ int choose_tile(const Geometry& g, int esz) {
   // at least 384 workgroups (1.5 per CU); below that the 64x64 tile keeps
   // the CUs busy.
   (void)kbytes;
-  const int t128x128 = 3, t64x64 = 5;
+  const int t128x128 = 1, t64x64 = 0;
   if (g.cout >= 128 && nwg(t128x128) >= 384) return t128x128;
   return t64x64;
 }
@@ -98,17 +98,19 @@ int choose_xl(const Geometry& g, int esz, int loader) {
 bool plan_split_k(conv_plan* p) {
   const Geometry& g = p->g;
   const TileCfg& t = p->path == PATH_XL ? kXlTiles[p->tile] : kTiles[p->tile];
-  const long nwg = (long)((g.cout + t.tco - 1) / t.tco) * ((g.m + t.tpx - 1) / t.tpx);
+  const int tco = t.tco, tpx = t.tpx, target = 512, min_per = 8;
+  const long nwg = (long)((g.cout + tco - 1) / tco) * ((g.m + tpx - 1) / tpx);
   const int nkt = p->kt_per;
-  if (nwg >= 128 || nkt < 16 || (g.cout & 3)) return true;
-  int s = (int)((512 + nwg - 1) / nwg);
+  if (2 * nwg >= target || nkt < 16 || (g.cout & 3)) return true;
+  int s = (int)((target + nwg - 1) / nwg);
   s = s < 8 ? s : 8;
-  s = s < nkt / 8 ? s : nkt / 8;
+  s = s < nkt / min_per ? s : nkt / min_per;
   if (s < 2) return true;
   const int per = (nkt + s - 1) / s;
   s = (nkt + per - 1) / per;
   if (s < 2) return true;
-  const int64_t bytes = (int64_t)s * g.m * g.cout * 4;
+  const int64_t part_bytes = (int64_t)s * g.m * g.cout * 4;
+  const int64_t bytes = part_bytes;
   int dev = 0, ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0 || hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();  // no device: an unsplit plan that cannot run anyway
@@ -123,6 +125,7 @@ bool plan_split_k(conv_plan* p) {
   p->kt_per = per;
   p->ws = ws;
   p->ws_bytes = bytes;
+
   p->ws_device = dev;
   return true;
 }
@@ -203,6 +206,7 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
   } else if (d->algo != 0 && (path != PATH_IGEMM || d->algo < 1 || d->algo > kAlgoLast)) {
     return CONV_E_UNSUPPORTED;
   }
+
   // A short reduction over an odd channel count (the 3-channel and 1-channel
   // stems) goes to the LDS-free small-K kernel unless a tile is forced.
   if (path == PATH_IGEMM && loader == LOAD_GENERIC && d->algo == 0 &&
@@ -234,15 +238,13 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
   p->in_esz = in_esz;
   p->out_esz = out_esz;
   p->out_kind = ot == CONV_F32 ? OUT_F32 : ot == CONV_BF16 ? OUT_BF16 : ot == CONV_I8 ? OUT_I8 : OUT_I32;
-  // 3x3 layers with 64-byte channel blocks can be forced onto the halo-patch
-  // kernel (algo kAlgoPatch). It is not chosen automatically: on MI355X the
-  // implicit GEMM measured faster on every workload layer.
-  if (path == PATH_IGEMM && patch_eligible(g, in_esz, d->groups)) {
-    if (d->algo == kAlgoPatch) path = PATH_PATCH;
-  } else if (d->algo == kAlgoPatch) {
-    delete p;
-    *out = nullptr;
-    return CONV_E_UNSUPPORTED;
+  p->cus = 256;
+  {
+    int dev = 0, ndev = 0, cus = 0;
+    if (hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0 && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      p->cus = cus;
+    (void)hipGetLastError();
   }
   if (d->algo >= kAlgoXl) {
     if (!xl_eligible(g, in_esz, loader, d->algo - kAlgoXl)) {
@@ -317,7 +319,6 @@ conv_status run_common(const conv_plan* p, const void* x, const void* w, const v
     case PATH_IGEMM: err = launch_igemm(p, x, w, e, y, s); break;
     case PATH_DW: err = launch_dw(p, x, w, e, y, s); break;
     case PATH_SMALLK: err = launch_smallk(p, x, w, e, y, s); break;
-    case PATH_PATCH: err = launch_patch(p, x, w, e, y, s); break;
     case PATH_XL: err = launch_xl(p, x, w, e, y, s); break;
     default: err = launch_f32(p, x, w, e, y, s); break;
   }
@@ -383,11 +384,6 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
                   "kernel=igemm_xl_kernel<%d, %d, %d, %d>",
                   kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], kAlgoXl + p->tile, t.tco, t.tpx, nwg,
                   p->g.m, p->g.k, p->ksplit, p->in_esz, t.tco, t.tpx, p->loader);
-  } else if (p->path == PATH_PATCH) {
-    const int s = p->g.sh, bh = s == 1 ? 16 : 8, cb = patch_cb(p->g, p->in_esz);
-    std::snprintf(buf, len, "patch3x3 dtype=%s out=%s tile=%d stride=%d block=%dx16 cb=%d m=%d k=%d "
-                  "kernel=patch3x3_kernel<%d, %d, %d, %d>", kDt[p->d.dtype], kDt[p->d.out_dtype], kAlgoPatch, s, bh,
-                  cb, p->g.m, p->g.k, p->in_esz, s, bh, cb);
   } else if (p->path == PATH_SMALLK) {
     int fco, ks;
     smallk_shape(p->g, p->in_esz, &fco, &ks);

@@ -40,16 +40,10 @@
 namespace convnhwc {
 
 const TileCfg kTiles[kNumTiles] = {
-    {32, 256, 1, 4},   // 1: narrow layers (Cout <= 32)
-    {64, 128, 2, 2},   // 2
-    {64, 256, 1, 4},   // 3: Cout = 64, many pixels
-    {128, 128, 2, 2},  // 4
-    {128, 64, 2, 2},   // 5
-    {64, 64, 2, 2},    // 6: few pixels
-    {256, 128, 2, 2},  // 7
-    {128, 256, 2, 2},  // 8
-    {256, 256, 2, 2},  // 9: 128x128 per wave, long reductions
-    {128, 512, 1, 4},  // 10: 128x128 per wave, Cout = 128
+    {64, 64, 2, 2},    // 1: few pixels or short reductions
+    {128, 128, 2, 2},  // 2: 128 channels and enough tiles to fill the CUs
+    {64, 128, 2, 2},   // 3
+    {128, 64, 2, 2},   // 4
 };
 
 namespace {
@@ -504,16 +498,10 @@ hipError_t launch_tile(int loader, const IgArgs& args, dim3 nwg, hipStream_t s) 
 template <int ESZ>
 hipError_t launch_esz(int tile, int loader, const IgArgs& args, dim3 nwg, hipStream_t s) {
   switch (tile) {
-    case 0: return launch_tile<ESZ, 32, 256, 1, 4>(loader, args, nwg, s);
-    case 1: return launch_tile<ESZ, 64, 128, 2, 2>(loader, args, nwg, s);
-    case 2: return launch_tile<ESZ, 64, 256, 1, 4>(loader, args, nwg, s);
-    case 3: return launch_tile<ESZ, 128, 128, 2, 2>(loader, args, nwg, s);
-    case 4: return launch_tile<ESZ, 128, 64, 2, 2>(loader, args, nwg, s);
-    case 5: return launch_tile<ESZ, 64, 64, 2, 2>(loader, args, nwg, s);
-    case 6: return launch_tile<ESZ, 256, 128, 2, 2>(loader, args, nwg, s);
-    case 7: return launch_tile<ESZ, 128, 256, 2, 2>(loader, args, nwg, s);
-    case 8: return launch_tile<ESZ, 256, 256, 2, 2>(loader, args, nwg, s);
-    default: return launch_tile<ESZ, 128, 512, 1, 4>(loader, args, nwg, s);
+    case 0: return launch_tile<ESZ, 64, 64, 2, 2>(loader, args, nwg, s);
+    case 1: return launch_tile<ESZ, 128, 128, 2, 2>(loader, args, nwg, s);
+    case 2: return launch_tile<ESZ, 64, 128, 2, 2>(loader, args, nwg, s);
+    default: return launch_tile<ESZ, 128, 64, 2, 2>(loader, args, nwg, s);
   }
 }
 

@@ -14,8 +14,7 @@ enum Path {
   PATH_DW = 2,     // depthwise 3x3, VALU stencil
   PATH_F32 = 3,    // true-fp32 direct convolution, VALU
   PATH_SMALLK = 4, // MFMA, operands straight from global memory: short K, odd Cin
-  PATH_PATCH = 5,  // MFMA 3x3 with the input halo patch staged in LDS
-  PATH_XL = 6      // MFMA, 256-wide tiles, software-pipelined (large layers)
+  PATH_XL = 6      // MFMA, direct-to-LDS loads, software-pipelined
 };
 
 // How the implicit-GEMM kernel gathers its activation operand.
@@ -34,14 +33,13 @@ struct TileCfg {
   int tco, tpx, wco, wpx;
 };
 
-constexpr int kNumTiles = 10;
-constexpr int kAlgoPatch = kNumTiles + 1;  // desc.algo value forcing PATH_PATCH
+constexpr int kNumTiles = 4;
 extern const TileCfg kTiles[kNumTiles];  // index = algo - 1
 
 // Tile configurations of the large-layer kernel; desc.algo kAlgoXl + i forces
 // configuration i.
 constexpr int kNumXlTiles = 6;
-constexpr int kAlgoXl = kAlgoPatch + 1;
+constexpr int kAlgoXl = kNumTiles + 1;
 constexpr int kAlgoLast = kAlgoXl + kNumXlTiles - 1;
 extern const TileCfg kXlTiles[kNumXlTiles];
 
@@ -64,11 +62,12 @@ struct conv_plan {
   int out_kind; // convnhwc::OutKind
   int in_esz, out_esz;
   int64_t x_bytes, w_bytes, y_bytes, b_bytes;
-  int ksplit;       // PATH_IGEMM: K-splits (1 = none)
+  int ksplit;       // PATH_IGEMM / PATH_XL: K-splits (1 = none)
   int kt_per;       // K-tiles per split
   void* ws;         // split-K partial sums [ksplit][m][cout] (fp32/int32), device
   int64_t ws_bytes;
   int ws_device;    // device the workspace lives on
+  int cus;          // compute units of the device current at prepare (256 without one)
 };
 
 namespace convnhwc {
@@ -81,10 +80,6 @@ hipError_t launch_xl(const conv_plan* p, const void* x, const void* w, const Epi
 hipError_t launch_smallk(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                          hipStream_t s);
 void smallk_shape(const Geometry& g, int esz, int* fco, int* ks);
-hipError_t launch_patch(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
-                        hipStream_t s);
-bool patch_eligible(const Geometry& g, int esz, int groups);
-int patch_cb(const Geometry& g, int esz);
 void dw_shape(const conv_plan* p, int* ve, int* pw, int* th);
 int dw_prefetch_rows();  // input rows in flight per lane in the row-window kernels
 hipError_t launch_dw(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,

@@ -98,7 +98,8 @@ double oracle_act(double x, int act) {
 }
 
 /* One output element of the float convolution: returns pre-activation in
- * double and the absolute-value sum through *abs_out. */
+ * double and, when abs_out is not NULL, the absolute-value sum through it
+ * (the pre-activation's sum is the same either way). */
 static double conv_point_float(const geom_t *g, const float *x, const float *wt,
                                const float *b, int64_t n, int64_t ho,
                                int64_t wo, int64_t co, double *abs_out) {
@@ -118,14 +119,18 @@ static double conv_point_float(const geom_t *g, const float *x, const float *wt,
       if (wi < 0 || wi >= g->w) continue;
       const float *xp = x + ((n * g->h + hi) * g->w + wi) * g->cin + grp * cg;
       const float *wp = wt + ((co * g->kh + kh) * g->kw + kw) * cg;
-      for (int64_t ci = 0; ci < cg; ++ci) {
-        double p = (double)xp[ci] * (double)wp[ci];
-        acc += p;
-        aacc += fabs(p);
+      if (abs_out) {
+        for (int64_t ci = 0; ci < cg; ++ci) {
+          double p = (double)xp[ci] * (double)wp[ci];
+          acc += p;
+          aacc += fabs(p);
+        }
+      } else {
+        for (int64_t ci = 0; ci < cg; ++ci) acc += (double)xp[ci] * (double)wp[ci];
       }
     }
   }
-  *abs_out = aacc;
+  if (abs_out) *abs_out = aacc;
   return acc;
 }
 
@@ -156,8 +161,8 @@ int oracle_conv_float(const float *x, const float *wt, const float *b,
     int64_t nn = row / g.ho, ho = row % g.ho;
     for (int64_t wo = 0; wo < g.wo; ++wo)
       for (int64_t co = 0; co < g.cout; ++co) {
-        double ab;
-        double pre = conv_point_float(&g, x, wt, b, nn, ho, wo, co, &ab);
+        double ab = 0.0;
+        double pre = conv_point_float(&g, x, wt, b, nn, ho, wo, co, a ? &ab : NULL);
         int64_t o = ((nn * g.ho + ho) * g.wo + wo) * g.cout + co;
         r[o] = oracle_act(pre, act);
         if (a) a[o] = ab;
@@ -187,8 +192,8 @@ int oracle_conv_float_at(const float *x, const float *wt, const float *b,
     int64_t wo = t % g.wo;
     t /= g.wo;
     int64_t ho = t % g.ho, nn = t / g.ho;
-    double ab;
-    double pre = conv_point_float(&g, x, wt, b, nn, ho, wo, co, &ab);
+    double ab = 0.0;
+    double pre = conv_point_float(&g, x, wt, b, nn, ho, wo, co, a ? &ab : NULL);
     r[i] = oracle_act(pre, act);
     if (a) a[i] = ab;
   }

@@ -106,12 +106,12 @@ def test_prepare_null():
     (dict(c_in=4, c_out=4, groups=4, dtype="f32", stride=(2, 2)), "dw3x3 dtype=f32 out=f32 loader=vec16"),
     (dict(c_in=6, c_out=6, groups=6, dtype="bf16"), "dw3x3 dtype=bf16 out=bf16 loader=generic"),
     # long reductions over 128-byte channel blocks: the large-layer kernel
-    (dict(n=16, h=40, w=40, c_in=512, c_out=512, dtype="bf16"), "igemm_xl dtype=bf16 out=bf16 loader=tap tile=15"),
-    (dict(n=16, h=20, w=20, c_in=512, c_out=1024, dtype="bf16"), "igemm_xl dtype=bf16 out=bf16 loader=tap tile=16"),
-    (dict(n=16, h=40, w=40, c_in=512, c_out=512, dtype="i8"), "igemm_xl dtype=i8 out=i8 loader=tap tile=15"),
-    (dict(n=16, h=80, w=80, c_in=256, c_out=256, dtype="i8"), "igemm_xl dtype=i8 out=i8 loader=tap tile=15"),
+    (dict(n=16, h=40, w=40, c_in=512, c_out=512, dtype="bf16"), "igemm_xl dtype=bf16 out=bf16 loader=tap tile=8"),
+    (dict(n=16, h=20, w=20, c_in=512, c_out=1024, dtype="bf16"), "igemm_xl dtype=bf16 out=bf16 loader=tap tile=9"),
+    (dict(n=16, h=40, w=40, c_in=512, c_out=512, dtype="i8"), "igemm_xl dtype=i8 out=i8 loader=tap tile=8"),
+    (dict(n=16, h=80, w=80, c_in=256, c_out=256, dtype="i8"), "igemm_xl dtype=i8 out=i8 loader=tap tile=8"),
     (dict(n=16, h=80, w=80, c_in=128, c_out=128, dtype="i8"), "igemm dtype=i8 out=i8 loader=tap"),  # short K, 128 channels
-    (dict(n=16, h=160, w=160, c_in=128, c_out=128, dtype="bf16"), "loader=tap tile=4 co128xpx128"),
+    (dict(n=16, h=160, w=160, c_in=128, c_out=128, dtype="bf16"), "loader=tap tile=2 co128xpx128"),
     (dict(n=16, h=40, w=40, c_in=512, c_out=320, dtype="bf16"), "igemm dtype=bf16"),  # Cout % 128
 ])
 def test_path_selection(layer, expect):
@@ -146,7 +146,7 @@ def test_forced_algo_and_count():
         assert "tile=%d " % a in d
         kinds.add(d.split()[0])
         c.close()
-    assert kinds == {"igemm", "igemm_xl", "patch3x3"}
+    assert kinds == {"igemm", "igemm_xl"}
     xl = [a for a in range(1, n + 1)
           if Conv2d(1, 20, 20, 64, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=a).describe().startswith("igemm_xl")]
     for a in xl:

@@ -20,7 +20,7 @@ import torch
 from convolution_conv2d_nhwc_amd import _lib
 from oracle import oracle
 from tests import helpers as H
-from tests.test_parity_gpu import ALGO_PATCH, L, XL_ALGOS, forced_tiles
+from tests.test_parity_gpu import L, XL_ALGOS, forced_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -30,11 +30,12 @@ TIE_LAYERS = [
     (L("tie_i8_tap", 1, 12, 11, 128, 64, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="none"), "loader=tap"),
     (L("tie_i8_vec_s2", 1, 13, 12, 32, 48, 3, 3, (2, 2), (1, 1), dtype="i8", out="i8", act="relu"), "loader=vec16"),
     (L("tie_i8_1x1", 2, 9, 7, 64, 96, 1, 1, dtype="i8", out="i8", act="none"), "loader=1x1"),
-    (L("tie_i8_cout5", 1, 7, 9, 16, 5, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="relu6"), "igemm"),
+    (L("tie_i8_cout5", 1, 15, 17, 16, 5, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="none"), "igemm"),
     (L("tie_i8_xl", 1, 13, 9, 128, 256, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="none"), "igemm_xl"),
     (L("tie_i8_smallk", 1, 17, 15, 3, 32, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="relu"), "smallk"),
     (L("tie_i8_splitk", 1, 8, 8, 512, 256, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="none"), "ksplit="),
-    (L("tie_i8_patch", 1, 14, 12, 64, 64, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="none"), "patch3x3"),
+    (L("tie_i8_xl_1x1", 1, 12, 12, 128, 128, 1, 1, dtype="i8", out="i8", act="none"), "igemm_xl"),
+    (L("tie_i8_xl_splitk", 1, 8, 8, 512, 256, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="none"), "igemm_xl"),
     (L("tie_dw_i8_rows", 1, 9, 10, 64, 64, 3, 3, (1, 1), (1, 1), groups=64, dtype="i8", out="i8", act="none"),
      "dw3x3_i8_kernel"),
     (L("tie_dw_i8_s2", 1, 12, 12, 32, 32, 3, 3, (2, 2), (1, 1), groups=32, dtype="i8", out="i8", act="relu"),
@@ -56,8 +57,8 @@ def _tie_tensors(layer, seed):
 def _forced_algo(layer):
     if layer.name.endswith("_xl"):
         return next(a for a in forced_tiles(layer) if a in XL_ALGOS)
-    if layer.name.endswith("_patch"):
-        return ALGO_PATCH
+    if "_xl_" in layer.name:
+        return next(a for a in forced_tiles(layer) if a in XL_ALGOS)
     return 0
 
 
@@ -67,7 +68,7 @@ def test_residual_i8_ties(layer, path):
     conv = _lib.Conv2d.from_layer(layer, algo=_forced_algo(layer))
     d = conv.describe()
     assert path in d, (layer.name, d)
-    if layer.name.endswith("splitk"):
+    if layer.name.endswith("splitk") and torch.cuda.is_available():
         assert "ksplit=1 " not in d, d
     q_plain, m = H.oracle_full(layer, t["x"], t)
     g = np.random.default_rng(78)
@@ -104,7 +105,7 @@ NEG_LAYERS = [
     (L("neg_bf16_xl", 1, 11, 9, 128, 256, 3, 3, (1, 1), (1, 1)), "igemm_xl"),
     (L("neg_bf16_smallk", 1, 13, 11, 3, 32, 3, 3, (1, 1), (1, 1)), "smallk"),
     (L("neg_bf16_splitk", 1, 8, 8, 512, 256, 3, 3, (1, 1), (1, 1)), "ksplit="),
-    (L("neg_bf16_patch", 1, 14, 12, 64, 64, 3, 3, (1, 1), (1, 1)), "patch3x3"),
+    (L("neg_bf16_xl_splitk", 1, 8, 8, 512, 256, 3, 3, (1, 1), (1, 1)), "igemm_xl"),
     (L("neg_dw_bf16_rows", 1, 9, 10, 64, 64, 3, 3, (1, 1), (1, 1), groups=64), "dw3x3_rows_kernel"),
     (L("neg_dw_bf16_s2", 1, 12, 12, 32, 32, 3, 3, (2, 2), (1, 1), groups=32), "dw3x3_kernel"),
     (L("neg_f32", 1, 10, 10, 4, 8, 3, 3, (1, 1), (1, 1), dtype="f32"), "direct_f32"),

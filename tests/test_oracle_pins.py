@@ -498,3 +498,16 @@ def test_residual_zero_is_the_plain_epilogue():
     q, m = oracle.conv_i8(x, w, b, s, (1, 1), (1, 1), 1, "relu6")
     q2, _ = oracle.add_residual_i8(m, np.zeros(q.shape, np.int8))
     assert np.array_equal(q, q2)
+
+
+def test_abs_sum_is_optional_and_leaves_r_unchanged():
+    # the CPU baseline times the oracle without the absolute-value sum; the
+    # pre-activation sum must be the same bits either way
+    rng = np.random.default_rng(11)
+    x = rng.normal(0, 0.5, (1, 9, 8, 16)).astype(np.float32)
+    w = rng.normal(0, 0.3, (12, 3, 3, 16)).astype(np.float32)
+    b = rng.uniform(-0.1, 0.1, 12).astype(np.float32)
+    r1, a1 = oracle.conv_float(x, w, b, (2, 1), (1, 1), 1, "mish", want_abs=True)
+    r2, a2 = oracle.conv_float(x, w, b, (2, 1), (1, 1), 1, "mish", want_abs=False)
+    assert a2 is None and a1 is not None
+    assert np.array_equal(r1.view(np.int64), r2.view(np.int64))

@@ -28,8 +28,7 @@ def _algo_describe(algo):
 ALGO_DESC = {a: _algo_describe(a) for a in range(1, ALGO_COUNT + 1)}
 TILE_ALGOS = [a for a, d in ALGO_DESC.items() if d.startswith("igemm ")]
 XL_ALGOS = [a for a, d in ALGO_DESC.items() if d.startswith("igemm_xl ")]
-ALGO_PATCH = next(a for a, d in ALGO_DESC.items() if d.startswith("patch3x3 "))
-assert len(TILE_ALGOS) + len(XL_ALGOS) + 1 == ALGO_COUNT
+assert len(TILE_ALGOS) + len(XL_ALGOS) == ALGO_COUNT
 
 # Tiles wider than 256 rows on either side need a 16-byte-vector loader; the
 # element-wise gather refuses them at prepare time.
@@ -38,7 +37,7 @@ BIG_TILES = {a for a in TILE_ALGOS if max(map(int, re.search(r"co(\d+)xpx(\d+)",
 
 def forced_tiles(layer):
     """Every forced MFMA tile the layer accepts. Only the generic loader may
-    refuse a tile wider than 256; the large-layer kernel refuses layers
+    refuse a tile wider than 256; the direct-to-LDS kernel refuses layers
     without 128-byte channel blocks or with Cout not a multiple of its tile."""
     out = []
     for a in TILE_ALGOS + XL_ALGOS:
@@ -248,35 +247,6 @@ def test_zero_bias_pointer():
     H.check_float(y.cpu().float().numpy(), r, a, "bf16", "null bias")
 
 
-# 3x3 layers through the halo-patch kernel (forced with algo 9): strides 1 and
-# 2, 64- and 128-byte channel blocks, several blocks, ragged edges and Cout.
-PATCH = [
-    L("patch_bf16_s1_c64", 2, 35, 37, 64, 72, 3, 3, (1, 1), (1, 1)),
-    L("patch_bf16_s1_c32", 1, 33, 18, 32, 64, 3, 3, (1, 1), (1, 1), act="relu"),
-    L("patch_bf16_s1_c256", 1, 20, 21, 256, 130, 3, 3, (1, 1), (1, 1), act="relu6"),
-    L("patch_bf16_s2_c32", 1, 41, 39, 32, 64, 3, 3, (2, 2), (1, 1)),
-    L("patch_bf16_s2_c128", 2, 17, 35, 128, 64, 3, 3, (2, 2), (1, 1), act="none"),
-    L("patch_bf16_s1_pad0", 1, 19, 20, 64, 16, 3, 3, (1, 1), (0, 0)),
-    L("patch_i8_s1_c128", 1, 34, 33, 128, 64, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="mish"),
-    L("patch_i8_s1_c64_i32", 2, 17, 19, 64, 72, 3, 3, (1, 1), (1, 1), dtype="i8", out="i32", act="none"),
-    L("patch_i8_s2_c256", 1, 23, 40, 256, 64, 3, 3, (2, 2), (1, 1), dtype="i8", out="i8", act="relu"),
-]
-
-
-@pytest.mark.parametrize("layer", PATCH, ids=[l.name for l in PATCH])
-def test_patch3x3(layer):
-    t = random_layer_tensors(layer, LAW[layer.dtype], seed=20)
-    ref = H.oracle_full(layer, t["x"], t)
-    y, conv = H.gpu_run(layer, t["x"], t, algo=ALGO_PATCH)
-    desc = conv.describe()
-    assert desc.startswith("patch3x3"), desc
-    what = "%s [%s]" % (layer.name, desc)
-    if layer.dtype == "i8":
-        H.check_int(y.cpu().numpy(), ref, layer, what)
-    else:
-        H.check_float(y.cpu().float().numpy(), ref[0], ref[1], layer.dtype, what)
-
-
 # Few output tiles, long reduction: the plan splits K over workgroups and a
 # second kernel sums the partials in split order.
 SPLITK = [
@@ -365,13 +335,11 @@ def _guarded_run(layer, t, algo=0):
 
 
 @pytest.mark.parametrize("layer", [DENSE[0], DENSE[5], DENSE[8], DENSE[14], DW[0], DW[3], F32[1], SMALLK[2],
-                                   SMALLK[6], PATCH[0], PATCH[3]],
+                                   SMALLK[6], XL[0], XL[8]],
                          ids=lambda l: l.name)
 def test_guard_bands_and_determinism(layer):
     t = random_layer_tensors(layer, LAW[layer.dtype], seed=16)
     algos = [0] + (forced_tiles(layer) if layer.groups == 1 and layer.dtype != "f32" else [])
-    if layer.name.startswith("patch_"):
-        algos = [ALGO_PATCH]
     for algo in algos:
         y1 = _guarded_run(layer, t, algo).clone()
         y2 = _guarded_run(layer, t, algo)
@@ -475,7 +443,7 @@ def test_upsample_concat(a_shape, up0, b_shape, up1, dtype):
 # once, against the oracle's unrounded activation plus r, on every kernel
 # path: implicit GEMM (tap, vec16 and element-wise loaders, Cout not a
 # multiple of 4), the large-layer kernel, the small-K stem kernel, the halo-
-# patch kernel, split K, the fp32 direct kernel and the three depthwise
+# persistent kernel, split K, the fp32 direct kernel and the three depthwise
 # kernels; in place (r is y) for a bf16 and an int8 layer.
 RES = [
     L("res_bf16_tap", 1, 12, 13, 64, 64, 3, 3, (1, 1), (1, 1), act="mish"),
@@ -483,7 +451,8 @@ RES = [
     L("res_bf16_vec", 1, 9, 10, 32, 48, 3, 3, (2, 2), (1, 1), act="relu6"),
     L("res_bf16_cout6", 1, 9, 8, 24, 6, 3, 3, (1, 1), (1, 1), act="relu"),
     L("res_bf16_stem", 1, 17, 15, 3, 32, 3, 3, (1, 1), (1, 1), act="mish"),
-    L("res_bf16_patch", 1, 14, 12, 64, 64, 3, 3, (1, 1), (1, 1), act="none"),
+    L("res_bf16_xl_c128", 1, 14, 12, 64, 128, 3, 3, (1, 1), (1, 1), act="none"),
+    L("res_i8_xl_splitk", 1, 9, 9, 512, 256, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="relu"),
     L("res_bf16_splitk", 1, 10, 10, 512, 256, 3, 3, (1, 1), (1, 1), act="mish"),
     L("res_i8_tap", 1, 12, 11, 128, 64, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="mish"),
     L("res_i8_xl", 1, 13, 9, 128, 256, 3, 3, (1, 1), (1, 1), dtype="i8", out="i8", act="relu6"),
@@ -495,7 +464,8 @@ RES = [
     L("res_dw_i8_s2", 1, 12, 12, 32, 32, 3, 3, (2, 2), (1, 1), groups=32, dtype="i8", out="i8", act="relu"),
     L("res_dw_f32", 1, 9, 9, 8, 8, 3, 3, (1, 1), (1, 1), groups=8, dtype="f32", act="mish"),
 ]
-RES_KERNEL = {"res_bf16_xl": "igemm_xl", "res_i8_xl": "igemm_xl", "res_bf16_patch": "patch3x3",
+RES_KERNEL = {"res_bf16_xl": "igemm_xl", "res_i8_xl": "igemm_xl", "res_bf16_xl_c128": "igemm_xl",
+              "res_i8_xl_splitk": "ksplit=",
               "res_bf16_stem": "smallk", "res_bf16_splitk": "ksplit=", "res_dw_bf16": "dw3x3_rows_kernel",
               "res_dw_bf16_s2": "dw3x3_kernel", "res_dw_i8": "dw3x3_i8_kernel", "res_dw_i8_s2": "dw3x3_kernel",
               "res_f32": "direct_f32"}
@@ -516,8 +486,8 @@ def test_residual_epilogue(layer):
     algo = 0
     if layer.name.endswith("_xl"):
         algo = next(a for a in forced_tiles(layer) if a in XL_ALGOS)
-    elif layer.name.endswith("_patch"):
-        algo = ALGO_PATCH
+    elif "_xl_c128" in layer.name or "_xl_splitk" in layer.name:
+        algo = next(a for a in forced_tiles(layer) if a in XL_ALGOS)
     conv = _lib.Conv2d.from_layer(layer, algo=algo)
     d = conv.describe()
     want = RES_KERNEL.get(layer.name)
