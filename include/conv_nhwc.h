@@ -106,10 +106,9 @@ typedef struct conv_desc {
   int32_t algo;           /* 0 = the library chooses the kernel and tile.
                              k > 0 forces one kernel configuration of a
                              dense bf16/int8 layer (for tests and tuning):
-                             1..10 the implicit-GEMM tiles, 11 the 3x3
-                             halo-patch kernel, 12 and up the large-layer
-                             kernel's tiles (conv_describe names the one
-                             chosen). For a depthwise layer with stride 1 and
+                             1..4 the implicit-GEMM tiles, 5 up to
+                             conv_algo_count() the large-layer kernel's
+                             tiles (conv_describe names the one chosen). For a depthwise layer with stride 1 and
                              c_in % 4 == 0, k = 1..4 forces 1, 2, 4 or 8
                              output rows per lane of the row-window kernel.
                              A configuration that cannot run the layer gives
