@@ -19,7 +19,8 @@ DTYPES = {"f32": 0, "bf16": 1, "i8": 2, "i32": 3}
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "i32": torch.int32}
 ACTS = {"none": 0, "relu": 1, "relu6": 2, "mish": 3}
 STATUS = {0: "CONV_OK", -1: "CONV_E_NULL", -2: "CONV_E_SHAPE", -3: "CONV_E_UNSUPPORTED",
-          -4: "CONV_E_ALIGN", -5: "CONV_E_ALIAS", -6: "CONV_E_NOMEM", -7: "CONV_E_HIP"}
+          -4: "CONV_E_ALIGN", -5: "CONV_E_ALIAS", -6: "CONV_E_NOMEM", -7: "CONV_E_HIP",
+          -8: "CONV_E_SCRATCH"}
 
 
 class ConvError(RuntimeError):
@@ -65,6 +66,8 @@ def lib():
     L.conv_run.restype = ctypes.c_int
     L.conv_run_residual.argtypes = [P, P, P, P, P, P, P]
     L.conv_run_residual.restype = ctypes.c_int
+    L.conv_run_noalloc.argtypes = [ctypes.POINTER(_Desc), P, P, P, P, P, P]
+    L.conv_run_noalloc.restype = ctypes.c_int
     L.conv_destroy.argtypes = [P]
     L.conv_destroy.restype = ctypes.c_int
     L.conv_out_shape.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
@@ -130,6 +133,7 @@ class Conv2d:
         self.groups = groups
         d = _Desc(n, h, w, c_in, c_out, kh, kw, stride[0], stride[1], pad[0], pad[1], groups,
                   DTYPES[dtype], DTYPES[out_dtype], ACTS[act], algo)
+        self._desc = d
         self._plan = ctypes.c_void_p()
         _check(lib().conv_prepare(ctypes.byref(d), ctypes.byref(self._plan)), "conv_prepare")
         shp = (ctypes.c_int64 * 4)()
@@ -185,6 +189,25 @@ class Conv2d:
             st = lib().conv_run_residual(self._plan, x.data_ptr(), w.data_ptr(), bp, residual.data_ptr(),
                                          y.data_ptr(), _stream_handle(stream))
             _check(st, "conv_run_residual")
+        return y
+
+    def run_noalloc(self, x: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor], y: torch.Tensor,
+                    stream=None, residual: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """The same layer through conv_run_noalloc (this object's description,
+        not its plan): nothing is allocated, y must be given, and a split
+        reduction uses the library's static scratch."""
+        self._chk(x, "x", TORCH_DT[self.dtype], self.in_shape)
+        self._chk(w, "w", TORCH_DT[self.dtype], self.w_shape)
+        if b is not None:
+            self._chk(b, "b", torch.int32 if self.dtype == "i8" else torch.float32, None)
+        self._chk(y, "y", TORCH_DT[self.out_dtype], self.out_shape)
+        if residual is not None:
+            self._chk(residual, "residual", TORCH_DT[self.out_dtype], self.out_shape)
+        st = lib().conv_run_noalloc(ctypes.byref(self._desc), x.data_ptr(), w.data_ptr(),
+                                    None if b is None else b.data_ptr(),
+                                    None if residual is None else residual.data_ptr(), y.data_ptr(),
+                                    _stream_handle(stream))
+        _check(st, "conv_run_noalloc")
         return y
 
     def run_ptrs(self, x: int, w: int, b: Optional[int], y: int, stream=None) -> int:

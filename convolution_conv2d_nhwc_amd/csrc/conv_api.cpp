@@ -9,8 +9,10 @@
 // only enqueues one kernel on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "device_common.h"
@@ -18,9 +20,21 @@
 
 using namespace convnhwc;
 
+// The split-K workspace of conv_run_noalloc, one copy per device, held until
+// the process ends. Host code never passes the name itself to a kernel or a
+// copy: it stands for a host-side shadow, so only the per-device address from
+// hipGetSymbolAddress is used.
+static __device__ __align__(256) unsigned char scratch[CONV_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_last_hip_error[256] = "";
+
+// Device address of `scratch` per device, looked up at the first
+// conv_run_noalloc call on that device (with it current).
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
 
 constexpr int64_t kMaxBytes = (int64_t)1 << 31;  // per tensor, see header
 constexpr int32_t kMaxSmall = 1 << 16;           // kernel, stride, pad limit
@@ -90,44 +104,51 @@ int choose_xl(const Geometry& g, int esz, int loader) {
 
 // Split the reduction when the output tiles alone would fill fewer than half
 // of the 256 CUs and each split still has >= 8 K-tiles of 128 bytes: aim at
-// ~512 workgroups, at most 8 splits. The splits' raw partial sums go to a device
-// workspace owned by the plan; a second kernel adds them in split order and
-// applies the epilogue. Returns false when the workspace allocation fails
-// (CONV_E_NOMEM). With no HIP device at all the plan stays unsplit: it can be
-// described but not run.
-bool plan_split_k(conv_plan* p) {
+// ~512 workgroups, at most 8 splits. The splits' raw partial sums go to a
+// device workspace; a second kernel adds them in split order and applies the
+// epilogue. Every split writes its whole [m][cout] slice before the second
+// kernel reads it, so the workspace never needs clearing.
+//   scratch == nullptr: the workspace is allocated here and owned by the plan
+//     (CONV_E_NOMEM if that fails). With no HIP device at all the plan stays
+//     unsplit: it can be described but not run.
+//   scratch != nullptr: the workspace is `scratch` (scratch_bytes long) and
+//     nothing is allocated; CONV_E_SCRATCH if the partials do not fit.
+conv_status plan_split_k(conv_plan* p, void* scratch, int64_t scratch_bytes) {
   const Geometry& g = p->g;
   const TileCfg& t = p->path == PATH_XL ? kXlTiles[p->tile] : kTiles[p->tile];
   const int tco = t.tco, tpx = t.tpx, target = 512, min_per = 8;
   const long nwg = (long)((g.cout + tco - 1) / tco) * ((g.m + tpx - 1) / tpx);
   const int nkt = p->kt_per;
-  if (2 * nwg >= target || nkt < 16 || (g.cout & 3)) return true;
+  if (2 * nwg >= target || nkt < 16 || (g.cout & 3)) return CONV_OK;
   int s = (int)((target + nwg - 1) / nwg);
   s = s < 8 ? s : 8;
   s = s < nkt / min_per ? s : nkt / min_per;
-  if (s < 2) return true;
+  if (s < 2) return CONV_OK;
   const int per = (nkt + s - 1) / s;
   s = (nkt + per - 1) / per;
-  if (s < 2) return true;
-  const int64_t part_bytes = (int64_t)s * g.m * g.cout * 4;
-  const int64_t bytes = part_bytes;
-  int dev = 0, ndev = 0;
-  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0 || hipGetDevice(&dev) != hipSuccess) {
-    (void)hipGetLastError();  // no device: an unsplit plan that cannot run anyway
-    return true;
-  }
-  void* ws = nullptr;
-  if (hipMalloc(&ws, bytes) != hipSuccess) {
-    (void)hipGetLastError();
-    return false;
+  if (s < 2) return CONV_OK;
+  const int64_t bytes = (int64_t)s * g.m * g.cout * 4;
+  void* ws = scratch;
+  if (scratch) {
+    if (bytes > scratch_bytes) return CONV_E_SCRATCH;
+  } else {
+    int dev = 0, ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0 || hipGetDevice(&dev) != hipSuccess) {
+      (void)hipGetLastError();  // no device: an unsplit plan that cannot run anyway
+      return CONV_OK;
+    }
+    if (hipMalloc(&ws, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return CONV_E_NOMEM;
+    }
+    p->ws_device = dev;
+    p->ws_owned = 1;
   }
   p->ksplit = s;
   p->kt_per = per;
   p->ws = ws;
   p->ws_bytes = bytes;
-
-  p->ws_device = dev;
-  return true;
+  return CONV_OK;
 }
 
 bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
@@ -138,11 +159,11 @@ bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
-  if (!d || !out) return CONV_E_NULL;
-  *out = nullptr;
+// Validate d and fill *p (memory the caller owns) with its plan. The split-K
+// workspace comes from plan_split_k(p, scratch, scratch_bytes).
+conv_status build_plan(const conv_desc* d, conv_plan* p, void* scratch, int64_t scratch_bytes) {
   if (d->n <= 0 || d->h <= 0 || d->w <= 0 || d->c_in <= 0 || d->c_out <= 0 || d->kh <= 0 ||
       d->kw <= 0 || d->stride_h <= 0 || d->stride_w <= 0 || d->pad_h < 0 || d->pad_w < 0 ||
       d->groups <= 0)
@@ -213,8 +234,6 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
       (int64_t)d->kh * d->kw * cg * in_esz <= 128)
     path = PATH_SMALLK;
 
-  conv_plan* p = new (std::nothrow) conv_plan;
-  if (!p) return CONV_E_NOMEM;
   std::memset(p, 0, sizeof(*p));
   p->d = *d;
   Geometry& g = p->g;
@@ -247,10 +266,7 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
     (void)hipGetLastError();
   }
   if (d->algo >= kAlgoXl) {
-    if (!xl_eligible(g, in_esz, loader, d->algo - kAlgoXl)) {
-      delete p;
-      return CONV_E_UNSUPPORTED;
-    }
+    if (!xl_eligible(g, in_esz, loader, d->algo - kAlgoXl)) return CONV_E_UNSUPPORTED;
     path = PATH_XL;
   }
   if (path == PATH_IGEMM && d->algo == 0) {
@@ -266,20 +282,32 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
             : path == PATH_XL  ? d->algo - kAlgoXl
             : path == PATH_DW && d->algo ? 1 << (d->algo - 1)
                                : 0;
-  if (path == PATH_IGEMM && loader == LOAD_GENERIC && (kTiles[p->tile].tco > 256 || kTiles[p->tile].tpx > 256)) {
-    delete p;  // the element-wise gather needs a thread per tile row
-    return CONV_E_UNSUPPORTED;
-  }
+  if (path == PATH_IGEMM && loader == LOAD_GENERIC && (kTiles[p->tile].tco > 256 || kTiles[p->tile].tpx > 256))
+    return CONV_E_UNSUPPORTED;  // the element-wise gather needs a thread per tile row
   p->ksplit = 1;
   p->kt_per = (int)((g.k * (int64_t)in_esz + 127) / 128);
-  if ((path == PATH_IGEMM || path == PATH_XL) && !plan_split_k(p)) {
-    delete p;
-    return CONV_E_NOMEM;
-  }
   p->x_bytes = x_bytes;
   p->w_bytes = w_bytes;
   p->y_bytes = y_bytes;
   p->b_bytes = dt == CONV_I8 ? (ot == CONV_I8 ? 8 * d->c_out : 4 * d->c_out) : 4 * d->c_out;
+  if (path == PATH_IGEMM || path == PATH_XL) return plan_split_k(p, scratch, scratch_bytes);
+  return CONV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+conv_status conv_prepare(const conv_desc* d, conv_plan** out) {
+  if (!d || !out) return CONV_E_NULL;
+  *out = nullptr;
+  conv_plan* p = new (std::nothrow) conv_plan;
+  if (!p) return CONV_E_NOMEM;
+  const conv_status st = build_plan(d, p, nullptr, 0);
+  if (st != CONV_OK) {
+    delete p;  // build_plan allocates nothing on a failing return
+    return st;
+  }
   *out = p;
   return CONV_OK;
 }
@@ -342,8 +370,39 @@ conv_status conv_run_residual(const conv_plan* p, const void* x, const void* w, 
   return run_common(p, x, w, b, r, y, stream);
 }
 
+conv_status conv_run_noalloc(const conv_desc* d, const void* x, const void* w, const void* b, const void* r,
+                             void* y, void* stream) {
+  if (!d) return CONV_E_NULL;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(hipGetLastError()));
+    return CONV_E_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return CONV_E_UNSUPPORTED;
+  void* ws = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ws) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ws = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ws) {
+      const hipError_t err = hipGetSymbolAddress(&ws, HIP_SYMBOL(scratch));
+      if (err != hipSuccess || !ws) {
+        std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "hipGetSymbolAddress(scratch): %s",
+                      hipGetErrorString(err));
+        (void)hipGetLastError();
+        return CONV_E_HIP;
+      }
+      g_scratch_ptr[dev].store(ws, std::memory_order_release);
+    }
+  }
+  conv_plan p;  // on this call's stack: no allocation
+  const conv_status st = build_plan(d, &p, ws, CONV_NOALLOC_SCRATCH_BYTES);
+  if (st != CONV_OK) return st;
+  if (r && p.out_kind == OUT_I32) return CONV_E_UNSUPPORTED;
+  return run_common(&p, x, w, b, r, y, stream);
+}
+
 conv_status conv_destroy(conv_plan* p) {
-  if (p && p->ws) {
+  if (p && p->ws && p->ws_owned) {
     int cur = 0;
     const bool have = hipGetDevice(&cur) == hipSuccess;
     if (have && cur != p->ws_device) (void)hipSetDevice(p->ws_device);
@@ -488,6 +547,9 @@ const char* conv_status_str(int32_t status) {
     case CONV_E_ALIGN: return "CONV_E_ALIGN: x, w, y need 16-byte and b 4-byte alignment";
     case CONV_E_ALIAS: return "CONV_E_ALIAS: output overlaps an input";
     case CONV_E_NOMEM: return "CONV_E_NOMEM: plan or split-K workspace allocation failed";
+    case CONV_E_SCRATCH:
+      return "CONV_E_SCRATCH: the layer's split-K partial sums exceed the static scratch of conv_run_noalloc "
+             "(CONV_NOALLOC_SCRATCH_BYTES)";
     case CONV_E_HIP:
       std::snprintf(buf, sizeof(buf), "CONV_E_HIP: %s", g_last_hip_error);
       return buf;

@@ -67,6 +67,7 @@ struct conv_plan {
   void* ws;         // split-K partial sums [ksplit][m][cout] (fp32/int32), device
   int64_t ws_bytes;
   int ws_device;    // device the workspace lives on
+  int ws_owned;     // ws was allocated for this plan (conv_destroy frees it)
   int cus;          // compute units of the device current at prepare (256 without one)
 };
 

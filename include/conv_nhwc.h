@@ -90,7 +90,9 @@ typedef enum conv_status {
   CONV_E_ALIGN = -4,       /* x, w or y not 16-byte aligned, or b not 4-byte aligned */
   CONV_E_ALIAS = -5,       /* y overlaps x, w or b */
   CONV_E_NOMEM = -6,       /* allocation of the plan, or of its split-K workspace, failed */
-  CONV_E_HIP = -7          /* the HIP launch reported an error */
+  CONV_E_HIP = -7,         /* the HIP launch reported an error */
+  CONV_E_SCRATCH = -8      /* conv_run_noalloc: the split-K partial sums need more than
+                              CONV_NOALLOC_SCRATCH_BYTES */
 } conv_status;
 
 /* Description of one layer. All sizes in elements. */
@@ -167,6 +169,33 @@ conv_status conv_run(const conv_plan* p, const void* x, const void* w,
  * arguments, errors and ordering rules as for conv_run. */
 conv_status conv_run_residual(const conv_plan* p, const void* x, const void* w,
                               const void* b, const void* r, void* y, void* stream);
+
+/* Bytes of the static device array behind conv_run_noalloc (16 MiB, one copy
+ * on each device the library runs on, held until the process ends). */
+#define CONV_NOALLOC_SCRATCH_BYTES (16 << 20)
+
+/* conv_prepare + conv_run (r == NULL) or conv_run_residual (r != NULL) +
+ * conv_destroy in one call that allocates nothing, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. The plan lives on this call's stack and a split reduction
+ * keeps its partial sums in the library's static device array of
+ * CONV_NOALLOC_SCRATCH_BYTES instead of a per-plan workspace; no hipMalloc,
+ * hipFree or host heap allocation is made (the first call on a device looks
+ * up that device's address of the array once). The kernels, the split and so
+ * the results are the same as conv_prepare + conv_run with the same d.
+ *   d : layer description as for conv_prepare (host pointer, read only).
+ *   x, w, b, r, y, stream : as for conv_run / conv_run_residual.
+ * Errors: those of conv_prepare and conv_run / conv_run_residual, except that
+ * CONV_E_NOMEM cannot occur; CONV_E_SCRATCH when the split-K partial sums
+ * (ksplit * m * c_out * 4 bytes, m = n * ho * wo) exceed
+ * CONV_NOALLOC_SCRATCH_BYTES; CONV_E_UNSUPPORTED for a device index of 64 or
+ * more; CONV_E_HIP if the array's address cannot be found.
+ * Every call on one device shares that device's array and leaves its partial
+ * sums there (nothing in it needs clearing: a split call writes every partial
+ * it reads). Calls that split and overlap on one device (different streams,
+ * host threads on one stream without ordering) race on the array: order them. */
+conv_status conv_run_noalloc(const conv_desc* d, const void* x, const void* w, const void* b,
+                             const void* r, void* y, void* stream);
 
 /* Free a plan and the workspace conv_prepare allocated for it; all device
  * memory a plan holds is taken at preparation and given back here, none in

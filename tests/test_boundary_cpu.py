@@ -2,6 +2,7 @@
 header declares, and rejects every malformed call with a named error before
 anything would be enqueued (no GPU is touched by these tests)."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -19,7 +20,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.library_path()),
 
 
 def header_functions():
-    src = open(HEADER).read()
+    src = "".join(open(h).read() for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(conv_[a-z_0-9]+)\s*\(", src)))
 
@@ -28,7 +29,8 @@ def test_header_symbols_are_exported():
     names = header_functions()
     assert {"conv_prepare", "conv_run", "conv_destroy", "conv_out_shape", "conv_mosaic_pack",
             "conv_status_str", "conv_describe", "conv_algo_count", "conv_spp_maxpool",
-            "conv_upsample_concat", "conv_run_residual"} <= set(names)
+            "conv_upsample_concat", "conv_run_residual", "conv_run_noalloc", "conv_probe_mfma",
+            "conv_probe_copy"} <= set(names)
     L = ctypes.CDLL(_lib.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -265,6 +267,13 @@ def test_mosaic_argument_checks():
     assert L.conv_mosaic_pack(T, 2, C, 1, 1, 4, 4, 3, 3, None) == -3   # int8 tiles
     assert L.conv_mosaic_pack(T + 4, 0, C, 1, 1, 4, 4, 3, 3, None) == -4
     assert L.conv_mosaic_pack(T, 0, T + 64, 1, 1, 4, 4, 3, 3, None) == -5
+
+
+def test_noalloc_null_desc_and_status_text():
+    # a NULL description is refused before any device call
+    assert _lib.lib().conv_run_noalloc(None, 16, 16, None, None, 16, None) == -1
+    assert _lib.lib().conv_status_str(-8).decode().startswith("CONV_E_SCRATCH")
+    assert _lib.STATUS[-8] == "CONV_E_SCRATCH"
 
 
 def test_destroy_null_is_noop():
