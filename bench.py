@@ -12,12 +12,17 @@ Prints ONE JSON line:
   ms_per_step   ms per 640x640 layer stack
   roofline      the dominant kernel (largest share of the step), timed with
                 HIP events on the stream it runs on, against MI355X peaks
-  cpu_baseline  the CPU oracle on the same stack (all host threads)
+  cpu_baseline  the CPU oracle on the same stack: all host threads (median
+                of 5 passes), with a 1-thread rung (median of 3)
   layers        per-layer time and roofline fraction
 
   secondary     per-layer rates of the depthwise probe (vs the HBM peak) and
                 of the N=16 YOLO sweep (vs the MFMA peak), measured after the
-                step, each launch on its own buffer set (Infinity-Cache cold)
+                step, each launch on its own buffer set (Infinity-Cache cold);
+                the SPP, upsample+concat and residual kernels; the small
+                stacks (digit classifier, keyword spotting, wake words) as
+                microseconds per stack and per layer; the measured peaks
+                (matrix-core probe, 1 GiB read+write stream)
 
 Options: --gpus N (only 1 is supported), --steps K, --warmup W,
 --workload NAME (another stack, for information), --no-cpu-baseline,
@@ -95,66 +100,31 @@ def main():
     torch.cuda.set_device(0)
 
     if args.calib_copy:
+        from convolution_conv2d_nhwc_amd import _lib
+
         n = args.calib_copy * (1 << 20) // 4
         a = torch.ones(n, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
         for _ in range(5):
-            b.copy_(a)
+            _lib.probe_copy(a, b)
         torch.cuda.synchronize()
-        print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4, "launches": 5}))
+        print(json.dumps({"calib_copy_kernel": "stream_copy_kernel", "calib_copy_bytes_read": n * 4,
+                          "calib_copy_bytes_written": n * 4, "launches": 5}))
         return
 
     from convolution_conv2d_nhwc_amd import _lib
-    from convolution_conv2d_nhwc_amd.data import layer_params, network_input, workload
+    from convolution_conv2d_nhwc_amd.data import workload
+    from convolution_conv2d_nhwc_amd.stack import Stack
 
     wl = workload(args.workload)
     if not wl.chained:
         print("bench.py: the step is a chained stack; %s is not one" % wl.name, file=sys.stderr)
         sys.exit(2)
 
-    # ---- resident inputs, weights and buffers --------------------------------
-    convs, params, bufs = [], [], []
-    for i, layer in enumerate(wl.layers):
-        p = layer_params(wl, i)
-        conv = _lib.Conv2d.from_layer(layer)
-        dev = {"w": p["w"].cuda()}
-        if layer.dtype == "i8":
-            dev["b"] = _lib.pack_bias_scale(p["b"], p.get("s") if layer.out == "i8" else None).cuda()
-        else:
-            dev["b"] = p["b"].cuda()
-        convs.append(conv)
-        params.append(dev)
-        bufs.append(conv.empty_output())
-    x0 = network_input(wl).cuda()
-    canvas = None
-    if wl.mosaic is not None:
-        m, th, tw, c = wl.mosaic
-        canvas = torch.empty((m, 2 * th, 2 * tw, c), dtype=torch.bfloat16, device="cuda")
-
-    def launch(i, x):
-        convs[i].run(x, params[i]["w"], params[i]["b"], bufs[i])
-        return bufs[i]
-
-    def step():
-        x = x0
-        if canvas is not None:
-            _lib.mosaic_pack(x0, canvas, out_dtype=torch.bfloat16)
-            x = canvas
-        for i in range(len(convs)):
-            x = launch(i, x)
-
-    # warm up on a side stream, then capture one step into a graph
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for _ in range(3):
-            step()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    torch.cuda.synchronize()
+    # ---- resident inputs, weights and buffers; one step captured as a graph --
+    stack = Stack(wl)
+    convs, canvas = stack.convs, stack.canvas
+    graph = stack.capture()
 
     for _ in range(args.warmup):
         graph.replay()
@@ -173,36 +143,10 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
+    progress("%s: %.5f ms per step over %d graph replays" % (wl.name, ms_per_step, args.steps))
+
     # ---- per-kernel durations, inside the stack ----------------------------------
-    # The step runs eagerly T more times with a timing event after every
-    # kernel. A spin kernel first holds the stream while the host enqueues all
-    # of it, so the kernels run back to back as in the graph, each reading what
-    # the previous one just wrote, and the interval between consecutive events
-    # is one kernel's duration (plus the event's own sub-microsecond cost). The
-    # profiler's per-dispatch average of the same command covers these
-    # launches and the graph replays alike.
-    ins = [canvas if canvas is not None else x0] + bufs[:-1]
-    seq = []
-    if canvas is not None:
-        seq.append(lambda: _lib.mosaic_pack(x0, canvas, out_dtype=torch.bfloat16))
-    seq += [lambda i=i: launch(i, ins[i]) for i in range(len(convs))]
-    # An event between two kernels delays the second by a few microseconds;
-    # a pair of events with nothing between them measures that delay, which
-    # is taken off every interval.
-    T = 20
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 2)] for _ in range(T)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(50_000_000)
-    for t in range(T):
-        evs[t][0].record()
-        evs[t][1].record()
-        for k, fn in enumerate(seq):
-            fn()
-            evs[t][k + 2].record()
-    torch.cuda.synchronize()
-    ev_gap_us = sum(evs[t][0].elapsed_time(evs[t][1]) for t in range(T)) * 1000.0 / T
-    dur_us = [sum(evs[t][k + 1].elapsed_time(evs[t][k + 2]) for t in range(T)) * 1000.0 / T - ev_gap_us
-              for k in range(len(seq))]
+    dur_us, ev_gap_us = per_launch_us(stack.launches())
 
     layers = []
     j = 0
@@ -248,20 +192,22 @@ def main():
     roof["avg_launch_us"] = avg_us
     roof["algorithmic_per_launch"] = {"flop": fl, "bytes": by}
     roof["event_gap_us"] = ev_gap_us
-    # the same fraction against what this GPU measurably sustains: a 1 GiB
-    # device-to-device copy (read + write) for HBM-bound work
-    copy_gbs = measured_copy_gbs()
-    roof["measured_peak"] = {"what": "1 GiB device copy, read+write", "value": round(copy_gbs, 1), "unit": "GB/s",
-                             "frac": (by / (avg_us * 1e-6) / 1e9) / copy_gbs}
+    # the same fraction against what this GPU measurably sustains (the
+    # library's matrix-core probe and 1 GiB read+write stream)
+    progress("measured peaks")
+    peaks = measured_peaks()
+    mp = peaks["copy"] if roof["bound"] == "hbm" else peaks["mfma_" + wl.layers[0].dtype]
+    roof["measured_peak"] = dict(peaks, frac=roof["achieved"] / mp["value"])
 
     total_flop = wl.flops()
     value = total_flop / (ms_per_step * 1e-3) / 1e12
 
     cpu = None
     if not args.no_cpu_baseline:
+        progress("CPU oracle ladder")
         cpu = cpu_baseline(wl)
 
-    secondary = None if args.no_secondary else secondary_measurements()
+    secondary = None if args.no_secondary else secondary_measurements(peaks)
 
     dt = wl.layers[0].dtype
     out = {
@@ -293,32 +239,156 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measured_copy_gbs() -> float:
-    """Bytes moved per second (read + write) by torch's device copy of a
-    1 GiB buffer, best of 5 timed runs after 2 warm-ups."""
+def per_launch_us(seq, T=20):
+    """Average duration of each launch of `seq` (single-kernel closures run in
+    order), over T eager passes with a timing event after every launch. A spin
+    kernel first holds the stream while the host enqueues all of it, so the
+    kernels run back to back as in the graph, each reading what the previous
+    one just wrote, and the interval between consecutive events is one
+    kernel's duration. An event between two kernels delays the second by a
+    little; a pair of events with nothing between them measures that delay,
+    which is taken off every interval. Returns (durations in us, that delay)."""
     import torch
 
-    n = 2 ** 30 // 4
-    x = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
-    y = torch.empty_like(x)
-    for _ in range(2):
-        y.copy_(x)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 2)] for _ in range(T)]
     torch.cuda.synchronize()
-    best = None
-    for _ in range(5):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(50_000_000)
+    for t in range(T):
+        evs[t][0].record()
+        evs[t][1].record()
+        for k, fn in enumerate(seq):
+            fn()
+            evs[t][k + 2].record()
+    torch.cuda.synchronize()
+    ev_gap_us = sum(evs[t][0].elapsed_time(evs[t][1]) for t in range(T)) * 1000.0 / T
+    dur_us = [sum(evs[t][k + 1].elapsed_time(evs[t][k + 2]) for t in range(T)) * 1000.0 / T - ev_gap_us
+              for k in range(len(seq))]
+    return dur_us, ev_gap_us
+
+
+def graph_median_us(fn_list, reps=200, warmup=20):
+    """Microseconds of one replay of `fn_list` captured as one graph, after
+    `warmup` replays: the median over `reps` replays each between its own pair
+    of events (one stack's latency), and the mean over `reps` replays back to
+    back (its rate when the host keeps the queue full)."""
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fn_list:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fn_list:
+            f()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
         e0.record()
-        y.copy_(x)
+        g.replay()
         e1.record()
+    torch.cuda.synchronize()
+    ts = sorted(e0.elapsed_time(e1) * 1000.0 for e0, e1 in evs)
+    # the same replays back to back with no events between them
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return ts[len(ts) // 2], a.elapsed_time(b) * 1000.0 / reps
+
+
+def stack_measurements():
+    """The small stacks (single fp32 layer of the 28x28 digit classifier,
+    keyword-spotting int8 DS-CNN, visual-wake-words bf16 MobileNet) and the
+    640x640 stack with and without its mosaic: microseconds per stack as the
+    median of 200 graph replays after 20 warm-ups, and per layer. Their ideal
+    work is far below a microsecond, so launch latency bounds them and a
+    roofline fraction says nothing about them."""
+    import torch
+
+    from convolution_conv2d_nhwc_amd.data import workload
+    from convolution_conv2d_nhwc_amd.stack import Stack
+
+    out = {}
+    for name in ("mnist_f32", "kws_int8", "vww_bf16", "yolo640_bf16"):
+        wl = workload(name)
+        st = Stack(wl)
+        seq = st.launches()
+        st.step()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        best = ms if best is None else min(best, ms)
-    del x, y
+        med, thr = graph_median_us(seq)
+        durs, _ = per_launch_us(seq)
+        names = (["mosaic_pack"] if st.canvas is not None else []) + [l.name for l in wl.layers]
+        kern = (["mosaic_vec8_kernel"] if st.canvas is not None else []) + [
+            c.describe().split("kernel=")[-1] for c in st.convs]
+        row = {"us_per_stack_median": round(med, 2), "us_per_stack_back_to_back": round(thr, 2),
+               "replays": 200, "warmup": 20, "nodes": len(seq),
+               "gflop": round(wl.flops() / 1e9, 5),
+               "layers": [{"name": n, "kernel": k, "us": round(u, 2)} for n, k, u in zip(names, kern, durs)],
+               "roofline": "not meaningful: launch-latency bound" if name != "yolo640_bf16" else "see the main line"}
+        if st.canvas is not None:
+            med1, thr1 = graph_median_us(seq[1:])
+            row["us_per_stack_median_without_mosaic"] = round(med1, 2)
+            row["us_per_stack_back_to_back_without_mosaic"] = round(thr1, 2)
+        out[name] = row
+        st.close()
+        del st
+        torch.cuda.empty_cache()
+    return out
+
+
+def measured_peaks():
+    """What this GPU measurably sustains, beside the spec peaks: the library's
+    matrix-core probe (bf16 and int8, back-to-back independent MFMAs on every
+    SIMD) and its read+write stream over 1 GiB. Best of 5 timed launches after
+    2 warm-ups each."""
+    import torch
+
+    from convolution_conv2d_nhwc_amd import _lib
+
+    def best_us(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0
+            best = us if best is None else min(best, us)
+        return best
+
+    out = {}
+    buf = torch.empty(4 * _lib.PROBE_MFMA_WORKGROUPS, dtype=torch.float32, device="cuda")
+    for dt, unit in (("bf16", "TFLOP/s"), ("i8", "TOPS")):
+        ops = _lib.probe_mfma(dt, 4000, buf)
+        us = best_us(lambda dt=dt: _lib.probe_mfma(dt, 4000, buf))
+        out["mfma_" + dt] = {"value": round(ops / (us * 1e-6) / 1e12, 1), "unit": unit,
+                             "spec": PEAK[dt], "what": "conv_probe_mfma, %d workgroups x 4 waves" %
+                             _lib.PROBE_MFMA_WORKGROUPS}
+    n = 2 ** 30 // 16
+    src = torch.ones(n * 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    moved = _lib.probe_copy(src, dst)
+    us = best_us(lambda: _lib.probe_copy(src, dst))
+    out["copy"] = {"value": round(moved / (us * 1e-6) / 1e9, 1), "unit": "GB/s", "spec": HBM_GBS,
+                   "what": "conv_probe_copy over 1 GiB, read + write"}
+    del src, dst
     torch.cuda.empty_cache()
-    return 2 * 2 ** 30 / (best * 1e-3) / 1e9
+    return out
 
 
-def secondary_measurements():
+def secondary_measurements(peaks):
     """Per-layer rates of the depthwise probe (against the HBM peak) and of the
     N=16 YOLO sweep (against the MFMA peak), outside the step's timed region.
     Inputs are seeded device tensors of each layer's shape and value law;
@@ -346,6 +416,7 @@ def secondary_measurements():
 
     out = {}
     for name in ("dw_probe_bf16", "dw_probe_int8", "yolo_sweep_bf16", "yolo_sweep_int8"):
+        progress(name)
         rows = []
         tot_flop = tot_us = 0.0
         for layer in workload(name).layers:
@@ -384,22 +455,28 @@ def secondary_measurements():
                          "bound": "mfma" if fl / (peak * 1e12) >= by / (HBM_GBS * 1e9) else "hbm",
                          "roof_frac": round(t_roof / (us * 1e-6), 4),
                          "frac_mfma_peak": round(fl / (us * 1e-6) / 1e12 / peak, 4),
-                         "frac_hbm_peak": round(by / (us * 1e-6) / 1e9 / HBM_GBS, 4), "buffer_sets": nsets})
+                         "frac_hbm_peak": round(by / (us * 1e-6) / 1e9 / HBM_GBS, 4),
+                         "frac_measured_mfma": round(fl / (us * 1e-6) / 1e12 / peaks["mfma_" + layer.dtype]["value"],
+                                                     4),
+                         "dtype": layer.dtype, "buffer_sets": nsets})
             tot_flop += fl
             tot_us += us
             del xs, ys, g
             torch.cuda.empty_cache()
         out[name] = {"layers": rows, "total_us": round(tot_us, 2),
                      "tflops": round(tot_flop / (tot_us * 1e-6) / 1e12, 2)}
+    progress("spp, upsample+concat, residual")
     out["spp_bf16"] = spp_measurements(gen)
     out["upcat_bf16"] = upcat_measurements(gen)
     out["residual_bf16"] = residual_measurements(gen)
-    copy = measured_copy_gbs()
-    out["measured_copy_gbs"] = round(copy, 1)
+    copy = peaks["copy"]["value"]
     for sec in out.values():
         for row in sec.get("layers", []) if isinstance(sec, dict) else []:
             if "gbs" in row:
                 row["frac_measured_copy"] = round(row["gbs"] / copy, 4)
+    progress("small stacks")
+    out["stacks"] = stack_measurements()
+    out["measured_peaks"] = peaks
     return out
 
 
@@ -527,34 +604,55 @@ def spp_measurements(gen):
     return {"layers": rows}
 
 
-def cpu_baseline(wl):
-    """The oracle, untuned, on the same stack: mosaic + every layer, all host
-    threads, one pass (the whole 640x640 stack is ~13 GMAC)."""
+def progress(msg: str):
+    """A progress line on stderr (the JSON line alone goes to stdout)."""
+    print("bench: " + msg, file=sys.stderr, flush=True)
+
+
+def _oracle_stack_seconds(wl, threads):
+    """One pass of the oracle over the stack (mosaic + every layer, each
+    output rounded to the layer's output type as the next layer reads it)."""
     import numpy as np
     import torch
 
     from convolution_conv2d_nhwc_amd.data import layer_params, network_input
     from oracle import oracle
 
-    threads = oracle.num_threads(0)
     x0 = network_input(wl)
+    ps = [layer_params(wl, i) for i in range(len(wl.layers))]
     t = time.perf_counter()
     if wl.mosaic is not None:
         bits = oracle.mosaic(x0.numpy(), out="bf16")
         x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
     else:
         x = x0.float().numpy()
-    for i, layer in enumerate(wl.layers):
-        p = layer_params(wl, i)
+    for layer, p in zip(wl.layers, ps):
         r, _ = oracle.conv_float(x, p["w"].float().numpy(), p["b"].numpy(), (layer.sh, layer.sw),
                                  (layer.ph, layer.pw), layer.groups, layer.act, want_abs=False, threads=threads)
         x = torch.from_numpy(r.astype(np.float32)).to(torch.bfloat16).float().numpy() if layer.out == "bf16" \
             else r.astype(np.float32)
-    sec = time.perf_counter() - t
-    return {"value": round(wl.flops() / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "the whole %s stack, one pass (%.2f GFLOP), %.2f s" % (wl.name, wl.flops() / 1e9, sec),
-            "ms_per_step": round(sec * 1e3, 1),
-            "cpu": _cpu_name()}
+    return time.perf_counter() - t
+
+
+def cpu_baseline(wl):
+    """The oracle, untuned, on the same stack, as a ladder: every host thread
+    (median of 5 passes; the reported value) and one thread (median of 3
+    passes, ~10 s each)."""
+    from oracle import oracle
+
+    threads = oracle.num_threads(0)
+    all_t = sorted(_oracle_stack_seconds(wl, threads) for _ in range(5))[2]
+    one_t = sorted(_oracle_stack_seconds(wl, 1) for _ in range(3))[1]
+    gf = wl.flops() / 1e9
+    return {"value": round(gf / all_t / 1e3, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole %s stack (%.2f GFLOP): median of 5 passes on %d threads (%.3f s); "
+                      "ladder also at 1 thread, median of 3" % (wl.name, gf, threads, all_t),
+            "ms_per_step": round(all_t * 1e3, 1),
+            "ladder": [{"threads": 1, "ms_per_step": round(one_t * 1e3, 1), "runs": 3,
+                        "value": round(gf / one_t / 1e3, 6)},
+                       {"threads": threads, "ms_per_step": round(all_t * 1e3, 1), "runs": 5,
+                        "value": round(gf / all_t / 1e3, 6)}],
+            "host_cpus": os.cpu_count(), "cpu": _cpu_name()}
 
 
 def _cpu_name():

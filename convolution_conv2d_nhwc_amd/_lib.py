@@ -83,6 +83,10 @@ def lib():
     I32 = ctypes.c_int32
     L.conv_upsample_concat.argtypes = [P, I32, I32, P, I32, I32, I32, P, I32, I32, I32, P]
     L.conv_upsample_concat.restype = ctypes.c_int
+    L.conv_probe_mfma.argtypes = [I32, I32, P, ctypes.POINTER(ctypes.c_double), P]
+    L.conv_probe_mfma.restype = ctypes.c_int
+    L.conv_probe_copy.argtypes = [P, P, ctypes.c_int64, P]
+    L.conv_probe_copy.restype = ctypes.c_int
     L.conv_status_str.argtypes = [ctypes.c_int32]
     L.conv_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -289,3 +293,33 @@ def upsample_concat(s0: torch.Tensor, up0: int, s1: torch.Tensor, up1: int, y: O
                                     n, ho, wo, _stream_handle(stream))
     _check(st, "conv_upsample_concat")
     return y
+
+
+# ---- measurement probes (include/conv_probe.h) ---------------------------------
+PROBE_MFMA_WORKGROUPS = 1024  # kProbeMfmaWorkgroups
+
+
+def probe_mfma(dtype: str, iters: int, out: Optional[torch.Tensor] = None, stream=None) -> float:
+    """Enqueue the matrix-core probe (bf16 or i8) and return the operations
+    (2 x multiply-adds) it performs; time it with events on the same stream."""
+    if out is None:
+        out = torch.empty(4 * PROBE_MFMA_WORKGROUPS, dtype=torch.float32, device="cuda")
+    if not out.is_cuda or out.dtype != torch.float32 or out.numel() < 4 * PROBE_MFMA_WORKGROUPS:
+        raise ValueError("out must be a device float32 tensor of at least %d values" % (4 * PROBE_MFMA_WORKGROUPS))
+    ops = ctypes.c_double()
+    _check(lib().conv_probe_mfma(DTYPES[dtype], iters, out.data_ptr(), ctypes.byref(ops), _stream_handle(stream)),
+           "conv_probe_mfma")
+    return ops.value
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> int:
+    """Enqueue the read+write stream dst <- src (same byte size, contiguous
+    device tensors); returns the bytes moved through memory (read + write)."""
+    for t, n in ((src, "src"), (dst, "dst")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous device tensor" % n)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    _check(lib().conv_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream_handle(stream)), "conv_probe_copy")
+    return 2 * nbytes

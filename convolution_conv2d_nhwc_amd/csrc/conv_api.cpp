@@ -103,8 +103,11 @@ int choose_xl(const Geometry& g, int esz, int loader) {
 }
 
 // Split the reduction when the output tiles alone would fill fewer than half
-// of the 256 CUs and each split still has >= 8 K-tiles of 128 bytes: aim at
-// ~512 workgroups, at most 8 splits. The splits' raw partial sums go to a
+// of the 256 CUs (under 128 workgroups) and each split still has >= 8 K-tiles
+// of 128 bytes: aim at ~512 workgroups, at most 8 splits. (Splitting layers
+// of 128..255 tiles measured slower on MI355X: the partial sums' extra write
+// and read outweigh the occupancy gained, e.g. 177 against 120 us for the
+// 16x40x40x512 3x3 layer on the large-layer kernel.) The splits' raw partial sums go to a
 // device workspace; a second kernel adds them in split order and applies the
 // epilogue. Every split writes its whole [m][cout] slice before the second
 // kernel reads it, so the workspace never needs clearing.
@@ -119,7 +122,7 @@ conv_status plan_split_k(conv_plan* p, void* scratch, int64_t scratch_bytes) {
   const int tco = t.tco, tpx = t.tpx, target = 512, min_per = 8;
   const long nwg = (long)((g.cout + tco - 1) / tco) * ((g.m + tpx - 1) / tpx);
   const int nkt = p->kt_per;
-  if (2 * nwg >= target || nkt < 16 || (g.cout & 3)) return CONV_OK;
+  if (nwg >= 128 || nkt < 16 || (g.cout & 3)) return CONV_OK;
   int s = (int)((target + nwg - 1) / nwg);
   s = s < 8 ? s : 8;
   s = s < nkt / min_per ? s : nkt / min_per;
