@@ -15,7 +15,14 @@
 //     done once; each element is a buffer load whose offset is forced out of
 //     range (reads 0) outside the image or past K. All loads of a tile are
 //     issued before any is used.
-//   * Waves walk the 64-pixel tiles with a grid stride.
+//   * Waves walk the 64-pixel tiles with a grid stride, at most four
+//     workgroups per CU, so that the set-up above serves several tiles.
+//   * Such a layer is bound by instruction issue, not by memory: on the
+//     640x640x3 -> 32 stem (bf16, Mish) the wave-level VALU instructions
+//     alone (about 7 M, four cycles each on a 16-lane SIMD: ~12 us) are
+//     more than half of the kernel's time, most of them in the epilogue.
+//     Staging the input rows in LDS with 16-byte loads, tried in place of
+//     the element gathers, measured no faster (20.3 against 19.8 us).
 // The output quads go through the same fused epilogue as the implicit GEMM.
 #include <algorithm>
 
@@ -39,6 +46,8 @@ struct SkArgs {
   int w_bytes;
   float rcp_c;
   float rcp_kw;
+  float rcp_wo;
+  float rcp_ho;
   int npx_tiles;  // ceil(m / 64)
 };
 
@@ -147,18 +156,24 @@ __global__ __launch_bounds__(256) void smallk_kernel(SkArgs a) {
   const int hw_o = g.ho * g.wo;
   const OutRef o = out_ref(a.y, g.m, g.cout, ESZ == 2 ? 2 : (a.out_kind == OUT_I32 ? 4 : 1), a.e.res);
   const int nwaves = gridDim.x * 4;
-  for (int pt = blockIdx.x * 4 + (threadIdx.x >> 6); pt < a.npx_tiles; pt += nwaves) {
-    const int pbase = pt * 64;
-    uint32_t v[4][KS][VE];
+  // The K elements of the four 16-pixel fragments of 64-pixel tile pt. The
+  // tile's first pixel is decomposed once (wave-uniform); the pixels of the
+  // fragments follow by small divisions, exact here (< 2^24).
+  auto gather = [&](int pt, uint32_t (&v)[4][KS][VE]) __attribute__((always_inline)) {
+    const int pbase = __builtin_amdgcn_readfirstlane(pt) * 64;
+    const int nb = pbase / hw_o;
+    const int rb = pbase - nb * hw_o;
+    const int hob = rb / g.wo;
+    const int wob = rb - hob * g.wo;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int p = pbase + 16 * j + lr;
       int base = 0, hi0 = -0x40000000, wi0 = 0;
       if (p < g.m) {
-        const int n = p / hw_o;
-        const int r = p - n * hw_o;
-        const int ho = r / g.wo;
-        const int wo = r - ho * g.wo;
+        int q, wo, q2, ho;
+        divmod_small(wob + 16 * j + lr, g.wo, a.rcp_wo, q, wo);
+        divmod_small(hob + q, g.ho, a.rcp_ho, q2, ho);
+        const int n = nb + q2;
         hi0 = ho * g.sh - g.ph;
         wi0 = wo * g.sw - g.pw;
         base = ((n * g.h + hi0) * g.w + wi0) * g.c;
@@ -171,6 +186,15 @@ __global__ __launch_bounds__(256) void smallk_kernel(SkArgs a) {
           v[j][ks][e] = bload_elem<ESZ>(rx, ok ? (uint32_t)(base + kofs[ks][e]) * ESZ : kOOB);
         }
     }
+  };
+  // Each wave walks its tiles. (Loading the next tile's elements while the
+  // current one is multiplied and stored measured slower on the 640x640
+  // stem, 19.4 against 18.5 us: the second set of registers costs waves.)
+  int pt = blockIdx.x * 4 + (threadIdx.x >> 6);
+  uint32_t v[4][KS][VE];
+  for (; pt < a.npx_tiles; pt += nwaves) {
+    const int pbase = pt * 64;
+    gather(pt, v);
     acc_t acc[FCO][4];
 #pragma unroll
     for (int i = 0; i < FCO; ++i)
@@ -248,12 +272,16 @@ hipError_t launch_smallk(const conv_plan* p, const void* x, const void* w, const
   a.w_bytes = (int)p->w_bytes;
   a.rcp_c = 1.0f / (float)p->g.c;
   a.rcp_kw = 1.0f / (float)p->g.kw;
+  a.rcp_wo = 1.0f / (float)p->g.wo;
+  a.rcp_ho = 1.0f / (float)p->g.ho;
   a.npx_tiles = (p->g.m + 63) / 64;
   int fco, ks;
   smallk_shape(p->g, p->in_esz, &fco, &ks);
   const int nco = (p->g.cout + 16 * fco - 1) / (16 * fco);
-  // one wave per 64-pixel tile, at most 8 workgroups (32 waves) per CU
-  const int wgs = std::min((a.npx_tiles + 3) / 4, 256 * 8);
+  // at most four workgroups (16 waves) per CU, each wave walking several
+  // 64-pixel tiles (measured on the 640x640 stem: 18.9 us at four per CU
+  // against 21.4 us at one tile per wave)
+  const int wgs = std::min((a.npx_tiles + 3) / 4, 4 * p->cus);
   const dim3 grid(wgs, nco);
   if (p->in_esz == 2) return launch_esz<2>(fco, ks, a, grid, s);
   return launch_esz<1>(fco, ks, a, grid, s);

@@ -102,6 +102,14 @@ SMALLK = [
     L("sk_i8_stem10x4", 1, 49, 10, 1, 64, 10, 4, (2, 2), (5, 1), dtype="i8", out="i8", act="relu"),
     L("sk_i8_c3_i32", 2, 15, 17, 3, 24, 3, 3, (1, 1), (1, 1), dtype="i8", out="i32", act="none"),
     L("sk_i8_c8_mish", 1, 21, 19, 8, 130, 3, 3, (2, 1), (0, 1), dtype="i8", out="i8", act="mish"),
+    # wide images: several 64-pixel tiles per output row with a ragged last
+    # one, image rows whose byte length is not a multiple of 16, stride 2,
+    # and a pad wider than the kernel
+    L("sk_bf16_w300", 1, 9, 300, 3, 32, 3, 3, (1, 1), (1, 1)),
+    L("sk_bf16_w530_s2", 1, 11, 530, 3, 32, 3, 3, (2, 2), (1, 1), act="relu6"),
+    L("sk_bf16_w100_n2", 2, 7, 100, 3, 16, 3, 3, (1, 1), (1, 1), act="relu"),
+    L("sk_i8_w277_pad4", 1, 6, 277, 3, 48, 3, 3, (1, 1), (4, 4), dtype="i8", out="i8", act="mish"),
+    L("sk_bf16_c2_w131_cout20", 1, 5, 131, 2, 20, 3, 5, (1, 2), (1, 2), act="none"),
 ]
 
 
