@@ -40,7 +40,10 @@ class _Desc(ctypes.Structure):
                 ("pad_h", ctypes.c_int32), ("pad_w", ctypes.c_int32),
                 ("groups", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("act", ctypes.c_int32),
-                ("algo", ctypes.c_int32)]
+                ("algo", ctypes.c_int32), ("w_format", ctypes.c_int32)]
+
+
+W_FORMATS = {"plain": 0, "bfp8": 1}
 
 
 _lib = None
@@ -83,6 +86,10 @@ def lib():
     I32 = ctypes.c_int32
     L.conv_upsample_concat.argtypes = [P, I32, I32, P, I32, I32, I32, P, I32, I32, I32, P]
     L.conv_upsample_concat.restype = ctypes.c_int
+    L.conv_bfp8_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    L.conv_bfp8_bytes.restype = ctypes.c_int64
+    L.conv_pack_bfp8.argtypes = [P, I32, ctypes.c_int64, ctypes.c_int64, P, P]
+    L.conv_pack_bfp8.restype = ctypes.c_int
     L.conv_probe_mfma.argtypes = [I32, I32, P, ctypes.POINTER(ctypes.c_double), P]
     L.conv_probe_mfma.restype = ctypes.c_int
     L.conv_probe_copy.argtypes = [P, P, ctypes.c_int64, P]
@@ -131,12 +138,13 @@ class Conv2d:
     def __init__(self, n: int, h: int, w: int, c_in: int, c_out: int, kh: int, kw: int,
                  stride: Sequence[int] = (1, 1), pad: Sequence[int] = (0, 0), groups: int = 1,
                  dtype: str = "bf16", out_dtype: Optional[str] = None, act: str = "none",
-                 algo: int = 0):
+                 algo: int = 0, w_format: str = "plain"):
         out_dtype = out_dtype or dtype
         self.dtype, self.out_dtype, self.act = dtype, out_dtype, act
         self.groups = groups
+        self.w_format = w_format
         d = _Desc(n, h, w, c_in, c_out, kh, kw, stride[0], stride[1], pad[0], pad[1], groups,
-                  DTYPES[dtype], DTYPES[out_dtype], ACTS[act], algo)
+                  DTYPES[dtype], DTYPES[out_dtype], ACTS[act], algo, W_FORMATS[w_format])
         self._desc = d
         self._plan = ctypes.c_void_p()
         _check(lib().conv_prepare(ctypes.byref(d), ctypes.byref(self._plan)), "conv_prepare")
@@ -145,12 +153,17 @@ class Conv2d:
         self.out_shape = tuple(int(v) for v in shp)
         self.in_shape = (n, h, w, c_in)
         self.w_shape = (c_out, kh, kw, c_in // groups)
+        if w_format == "bfp8":
+            self.w_shape = (int(lib().conv_bfp8_bytes(c_out, kh * kw * (c_in // groups))),)
 
     @classmethod
-    def from_layer(cls, layer, algo: int = 0) -> "Conv2d":
+    def from_layer(cls, layer, algo: int = 0, w_format: str = "plain") -> "Conv2d":
         return cls(layer.n, layer.h, layer.w, layer.cin, layer.cout, layer.kh, layer.kw,
                    (layer.sh, layer.sw), (layer.ph, layer.pw), layer.groups, layer.dtype,
-                   layer.out, layer.act, algo)
+                   layer.out, layer.act, algo, w_format)
+
+    def _w_dtype(self):
+        return torch.uint8 if self.w_format == "bfp8" else TORCH_DT[self.dtype]
 
     def describe(self) -> str:
         buf = ctypes.create_string_buffer(256)
@@ -177,7 +190,7 @@ class Conv2d:
         `residual` (y's dtype and shape; may be y itself) the layer computes
         act(conv + b) + residual through conv_run_residual."""
         self._chk(x, "x", TORCH_DT[self.dtype], self.in_shape)
-        self._chk(w, "w", TORCH_DT[self.dtype], self.w_shape)
+        self._chk(w, "w", self._w_dtype(), self.w_shape)
         if b is not None:
             want = torch.int32 if self.dtype == "i8" else torch.float32
             self._chk(b, "b", want, None)
@@ -201,7 +214,7 @@ class Conv2d:
         not its plan): nothing is allocated, y must be given, and a split
         reduction uses the library's static scratch."""
         self._chk(x, "x", TORCH_DT[self.dtype], self.in_shape)
-        self._chk(w, "w", TORCH_DT[self.dtype], self.w_shape)
+        self._chk(w, "w", self._w_dtype(), self.w_shape)
         if b is not None:
             self._chk(b, "b", torch.int32 if self.dtype == "i8" else torch.float32, None)
         self._chk(y, "y", TORCH_DT[self.out_dtype], self.out_shape)
@@ -323,3 +336,24 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> int:
         raise ValueError("src and dst differ in size")
     _check(lib().conv_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream_handle(stream)), "conv_probe_copy")
     return 2 * nbytes
+
+
+def bfp8_bytes(c_out: int, k: int) -> int:
+    return int(lib().conv_bfp8_bytes(c_out, k))
+
+
+def pack_bfp8(w: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Encode OHWI weights (device, bf16 or fp32, contiguous) into the bfp8
+    image conv_run takes for w_format "bfp8" (uint8, conv_bfp8_bytes)."""
+    if not w.is_cuda or not w.is_contiguous() or w.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("w must be a contiguous device bf16 or float32 tensor")
+    c_out = w.shape[0]
+    k = w.numel() // c_out
+    nbytes = bfp8_bytes(c_out, k)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    if out.dtype != torch.uint8 or out.numel() != nbytes or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 tensor of %d bytes" % nbytes)
+    _check(lib().conv_pack_bfp8(w.data_ptr(), DTYPES["f32" if w.dtype == torch.float32 else "bf16"], c_out, k,
+                                out.data_ptr(), _stream_handle(stream)), "conv_pack_bfp8")
+    return out

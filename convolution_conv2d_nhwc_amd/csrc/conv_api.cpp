@@ -194,7 +194,11 @@ conv_status build_plan(const conv_desc* d, conv_plan* p, void* scratch, int64_t 
   const int in_esz = esz_of(dt), out_esz = esz_of(ot);
   const int64_t cg = d->c_in / d->groups;
   const int64_t x_bytes = d->n * d->h * d->w * d->c_in * in_esz;
-  const int64_t w_bytes = d->c_out * (int64_t)d->kh * d->kw * cg * in_esz;
+  // bfp8 weights: int8 mantissas [c_out][Kp] and one exponent byte per 16
+  const bool wq = d->w_format == CONV_W_BFP8;
+  if (d->w_format != CONV_W_PLAIN && !wq) return CONV_E_UNSUPPORTED;
+  const int64_t kp = ((int64_t)d->kh * d->kw * cg + 15) / 16 * 16;
+  const int64_t w_bytes = wq ? d->c_out * kp + d->c_out * (kp / 16) : d->c_out * (int64_t)d->kh * d->kw * cg * in_esz;
   const int64_t y_bytes = d->n * ho * wo * d->c_out * out_esz;
   if (x_bytes >= kMaxBytes || w_bytes >= kMaxBytes || y_bytes >= kMaxBytes) return CONV_E_UNSUPPORTED;
   // The kernels split a reduction index into (tap, channel) with an fp32
@@ -230,6 +234,12 @@ conv_status build_plan(const conv_desc* d, conv_plan* p, void* scratch, int64_t 
   } else if (d->algo != 0 && (path != PATH_IGEMM || d->algo < 1 || d->algo > kAlgoLast)) {
     return CONV_E_UNSUPPORTED;
   }
+
+  // bfp8 weights are decoded by the implicit-GEMM kernel's 16-byte weight
+  // loaders: dense bf16 layers with c_in * 2 % 16 == 0, implicit-GEMM tiles
+  // only (the first, 3-channel convolution stays bf16, as on the pages).
+  if (wq && !(dt == CONV_BF16 && path == PATH_IGEMM && loader != LOAD_GENERIC && d->algo < kAlgoXl))
+    return CONV_E_UNSUPPORTED;
 
   // A short reduction over an odd channel count (the 3-channel and 1-channel
   // stems) goes to the LDS-free small-K kernel unless a tile is forced.
@@ -272,7 +282,7 @@ conv_status build_plan(const conv_desc* d, conv_plan* p, void* scratch, int64_t 
     if (!xl_eligible(g, in_esz, loader, d->algo - kAlgoXl)) return CONV_E_UNSUPPORTED;
     path = PATH_XL;
   }
-  if (path == PATH_IGEMM && d->algo == 0) {
+  if (path == PATH_IGEMM && d->algo == 0 && !wq) {
     const int xt = choose_xl(g, in_esz, loader);
     if (xt >= 0) {
       path = PATH_XL;
@@ -291,6 +301,9 @@ conv_status build_plan(const conv_desc* d, conv_plan* p, void* scratch, int64_t 
   p->kt_per = (int)((g.k * (int64_t)in_esz + 127) / 128);
   p->x_bytes = x_bytes;
   p->w_bytes = w_bytes;
+  p->wq = wq;
+  p->kp = (int)kp;
+  p->w_exp_off = wq ? d->c_out * kp : 0;
   p->y_bytes = y_bytes;
   p->b_bytes = dt == CONV_I8 ? (ot == CONV_I8 ? 8 * d->c_out : 4 * d->c_out) : 4 * d->c_out;
   if (path == PATH_IGEMM || path == PATH_XL) return plan_split_k(p, scratch, scratch_bytes);
@@ -433,11 +446,11 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
     const TileCfg& t = kTiles[p->tile];
     const long nwg = (long)((p->g.cout + t.tco - 1) / t.tco) * ((p->g.m + t.tpx - 1) / t.tpx);
     std::snprintf(buf, len,
-                  "igemm dtype=%s out=%s loader=%s tile=%d co%dxpx%d waves=%dx%d wgs=%ld m=%d k=%d "
-                  "ksplit=%d kernel=igemm_kernel<%d, %d, %d, %d, %d, %d, %d>",
-                  kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], p->tile + 1, t.tco, t.tpx, t.wco,
-                  t.wpx, nwg, p->g.m, p->g.k, p->ksplit, p->in_esz, t.tco, t.tpx, t.wco, t.wpx, p->loader,
-                  igemm_stages(p->loader, p->tile));
+                  "igemm dtype=%s out=%s%s loader=%s tile=%d co%dxpx%d waves=%dx%d wgs=%ld m=%d k=%d "
+                  "ksplit=%d kernel=igemm_kernel<%d, %d, %d, %d, %d, %d, %d, %d>",
+                  kDt[p->d.dtype], kDt[p->d.out_dtype], p->wq ? " w=bfp8" : "", kLoader[p->loader], p->tile + 1,
+                  t.tco, t.tpx, t.wco, t.wpx, nwg, p->g.m, p->g.k, p->ksplit, p->in_esz, t.tco, t.tpx, t.wco, t.wpx,
+                  p->loader, igemm_stages(p->loader, p->tile), p->wq);
   } else if (p->path == PATH_XL) {
     const TileCfg& t = kXlTiles[p->tile];
     const long nwg = (long)(p->g.cout / t.tco) * ((p->g.m + t.tpx - 1) / t.tpx);
@@ -493,6 +506,29 @@ conv_status conv_mosaic_pack(const void* tiles, int32_t in_dtype, void* canvas, 
   if (ranges_overlap(tiles, in_bytes, canvas, out_bytes)) return CONV_E_ALIAS;
   hipError_t err = launch_mosaic(tiles, in_dtype == CONV_F32, canvas, out_dtype == CONV_F32, m, th, tw, c, c_pad,
                                  static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(err));
+    return CONV_E_HIP;
+  }
+  return CONV_OK;
+}
+
+int64_t conv_bfp8_bytes(int64_t c_out, int64_t k) {
+  if (c_out <= 0 || k <= 0) return 0;
+  const int64_t kp = (k + 15) / 16 * 16;
+  return c_out * kp + c_out * (kp / 16);
+}
+
+conv_status conv_pack_bfp8(const void* w, int32_t w_dtype, int64_t c_out, int64_t k, void* packed, void* stream) {
+  if (!w || !packed) return CONV_E_NULL;
+  if (c_out <= 0 || k <= 0) return CONV_E_SHAPE;
+  if (w_dtype != CONV_F32 && w_dtype != CONV_BF16) return CONV_E_UNSUPPORTED;
+  const int64_t in_bytes = c_out * k * esz_of(w_dtype);
+  const int64_t out_bytes = conv_bfp8_bytes(c_out, k);
+  if (in_bytes >= kMaxBytes || out_bytes >= kMaxBytes) return CONV_E_UNSUPPORTED;
+  if ((uintptr_t)packed & 15 || (uintptr_t)w & (esz_of(w_dtype) - 1)) return CONV_E_ALIGN;
+  if (ranges_overlap(w, in_bytes, packed, out_bytes)) return CONV_E_ALIAS;
+  hipError_t err = launch_bfp8_pack(w, w_dtype == CONV_F32, (int)c_out, (int)k, packed, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) {
     std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(err));
     return CONV_E_HIP;

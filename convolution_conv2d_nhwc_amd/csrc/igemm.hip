@@ -65,7 +65,28 @@ struct IgArgs {
   int ksplit;    // K-splits (gridDim.y); > 1 writes raw partial sums to ws
   int kt_per;    // K-tiles per split
   void* ws;      // [ksplit][m][cout] fp32 / int32 partial sums
+  int kp;        // bfp8 weights: K padded to a multiple of 16 (mantissa row length)
+  int w_exp_off; // bfp8 weights: byte offset of the exponent bytes in w
 };
+
+// bfp8 weights (WQ): eight consecutive mantissas of one block (two dwords)
+// and the block's exponent byte E -> the 8 bf16 values m * 2^(E - 133). Each
+// is exact: (float)m has at most 7 significant bits, the power-of-two
+// scaling is exact (fp32 keeps denormals), and the top half of such a float
+// is its bf16 value.
+__device__ __forceinline__ i32x4 bfp8_to_bf16x8(const i32x4& q) {
+  const int sh = (int)((uint32_t)q[2] & 0xffu) - 133;
+  uint32_t out[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t wd = (uint32_t)q[p >> 1];
+    const int s0 = 16 * (p & 1);
+    const float f0 = __builtin_ldexpf((float)(int)(int8_t)(wd >> s0), sh);
+    const float f1 = __builtin_ldexpf((float)(int)(int8_t)(wd >> (s0 + 8)), sh);
+    out[p] = (__builtin_bit_cast(uint32_t, f0) >> 16) | (__builtin_bit_cast(uint32_t, f1) & 0xffff0000u);
+  }
+  return i32x4{(int)out[0], (int)out[1], (int)out[2], (int)out[3]};
+}
 
 
 // ---------------------------------------------------------------- kernel
@@ -77,7 +98,7 @@ struct IgArgs {
 #define IGEMM_WPE 2
 #endif
 
-template <int ESZ, int TCO, int TPX, int WCO, int WPX, int LOADER, int D>
+template <int ESZ, int TCO, int TPX, int WCO, int WPX, int LOADER, int D, int WQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))) void igemm_kernel(IgArgs a) {
   constexpr int VE = 16 / ESZ;      // elements per 16-byte chunk
   constexpr int BKE = kBKB / ESZ;   // elements per K-tile row
@@ -87,6 +108,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
   constexpr int BCH = TPX / 32;     // 16-byte B chunks per thread per tile
   static_assert(FCO >= 1 && FPX >= 1 && WCO * WPX == 4, "bad tile");
   static_assert(LOADER != LOAD_GENERIC || D == 1, "generic loader is single-stage");
+  static_assert(WQ == 0 || (ESZ == 2 && LOADER != LOAD_GENERIC), "bfp8 weights: bf16, 16-byte loaders");
   typedef typename Mfma<ESZ>::acc_t acc_t;
 
   __shared__ __attribute__((aligned(16))) char smem[2 * (TCO + TPX) * kBKB];
@@ -195,6 +217,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
     }
   }
 
+  // bfp8 weights: chunk j of this thread covers elements kt*64 + e8 .. +7 of
+  // row co (one block); its 8 mantissa bytes and its block's exponent byte
+  // sit at these offsets plus kt*64 and kt*4.
+  uint32_t voff_am[ACH], voff_ae[ACH];
+  if constexpr (WQ) {
+    const int e8 = (tid & 7) * 8;
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) {
+      const int co = co0 + (tid >> 3) + 32 * j;
+      voff_am[j] = co < g.cout ? (uint32_t)(co * a.kp + e8) : kOOB;
+      voff_ae[j] = co < g.cout ? (uint32_t)(a.w_exp_off + co * (a.kp >> 4) + (e8 >> 4)) : kOOB;
+    }
+  }
+  // The raw bfp8 bytes of K-tile kt: {mantissas 0-3, 4-7, exponent, 0}.
+  auto fetch_aq = [&](int kt, i32x4 (&ra)[ACH]) {
+    const bool kin = kt * 64 + (tid & 7) * 8 < g.k;
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) {
+      const u32x2 mm = __builtin_amdgcn_raw_buffer_load_b64(rw, kin ? voff_am[j] : kOOB, kin ? kt * 64 : 0, 0);
+      const uint32_t ee = __builtin_amdgcn_raw_buffer_load_b8(rw, kin ? voff_ae[j] : kOOB, kin ? kt * 4 : 0, 0);
+      ra[j] = i32x4{(int)mm[0], (int)mm[1], (int)ee, 0};
+    }
+  };
+
   // Issue the global loads of K-tile kt into one register stage (tiles are
   // fetched in increasing order).
   auto fetch = [&](int kt, i32x4 (&ra)[ACH], i32x4 (&rb)[BCH]) {
@@ -268,8 +314,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
       const int tap = t_kh * g.kw + t_kw;
       const int soff_b = (t_kh * g.w + t_kw) * cbytes + t_cb;
       const int soff_a = kt * kBKB;
+      if constexpr (WQ)
+        fetch_aq(kt, ra);
+      else
 #pragma unroll
-      for (int j = 0; j < ACH; ++j) ra[j] = bload16s(rw, live ? voff_a[j] : kOOB, live ? soff_a : 0);
+        for (int j = 0; j < ACH; ++j) ra[j] = bload16s(rw, live ? voff_a[j] : kOOB, live ? soff_a : 0);
 #pragma unroll
       for (int j = 0; j < BCH; ++j) {
         const bool ok = live && ((tmask[j] >> (tap & 31)) & 1u);
@@ -287,17 +336,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
       // K = Cin: chunk c of tile kt is valid while kt*128 + 16c < Cin*ESZ.
       const int soff = kt * kBKB;
       const bool cin_ok = (tid & 7) * 16 < cbytes - soff;
+      if constexpr (WQ)
+        fetch_aq(kt, ra);
+      else
 #pragma unroll
-      for (int j = 0; j < ACH; ++j) ra[j] = bload16s(rw, cin_ok ? voff_a[j] : kOOB, cin_ok ? soff : 0);
+        for (int j = 0; j < ACH; ++j) ra[j] = bload16s(rw, cin_ok ? voff_a[j] : kOOB, cin_ok ? soff : 0);
 #pragma unroll
       for (int j = 0; j < BCH; ++j) rb[j] = bload16s(rx, cin_ok ? voff_b[j] : kOOB, cin_ok ? soff : 0);
     } else {
       const int kc = kb + (tid & 7) * VE;  // first element of this thread's chunk
       const bool kin = kc < g.k;
+      if constexpr (WQ) {
+        fetch_aq(kt, ra);
+      } else {
 #pragma unroll
-      for (int j = 0; j < ACH; ++j) {
-        const int co = co0 + (tid >> 3) + 32 * j;
-        ra[j] = bload16(rw, (co < g.cout && kin) ? (uint32_t)(co * g.k + kc) * ESZ : kOOB);
+        for (int j = 0; j < ACH; ++j) {
+          const int co = co0 + (tid >> 3) + 32 * j;
+          ra[j] = bload16(rw, (co < g.cout && kin) ? (uint32_t)(co * g.k + kc) * ESZ : kOOB);
+        }
       }
       {
         // this thread's chunk starts at element kc = (kh, kw, ci) of the
@@ -339,7 +395,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
     } else {
       const int col = tid & 7;
 #pragma unroll
-      for (int j = 0; j < ACH; ++j) *reinterpret_cast<i32x4*>(A + lds_off((tid >> 3) + 32 * j, col)) = ra[j];
+      for (int j = 0; j < ACH; ++j)
+        *reinterpret_cast<i32x4*>(A + lds_off((tid >> 3) + 32 * j, col)) = WQ ? bfp8_to_bf16x8(ra[j]) : ra[j];
 #pragma unroll
       for (int j = 0; j < BCH; ++j) *reinterpret_cast<i32x4*>(B + lds_off((tid >> 3) + 32 * j, col)) = rb[j];
     }
@@ -468,40 +525,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
 template <int LOADER, int TCO, int TPX>
 constexpr int kStages = (LOADER == LOAD_GENERIC || TCO + TPX >= 512) ? 1 : IGEMM_STAGES;
 
-template <int ESZ, int TCO, int TPX, int WCO, int WPX>
+template <int ESZ, int TCO, int TPX, int WCO, int WPX, int WQ>
 hipError_t launch_tile(int loader, const IgArgs& args, dim3 nwg, hipStream_t s) {
   switch (loader) {
     case LOAD_GENERIC:
       // the element-wise gather maps at least one thread to each tile row
-      if constexpr (TCO <= 256 && TPX <= 256)
-        hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_GENERIC, kStages<LOAD_GENERIC, TCO, TPX>>),
+      if constexpr (TCO <= 256 && TPX <= 256 && WQ == 0)
+        hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_GENERIC, kStages<LOAD_GENERIC, TCO, TPX>, 0>),
                            dim3(nwg), dim3(256), 0, s, args);
       else
         return hipErrorInvalidValue;  // refused by conv_prepare
       break;
     case LOAD_VEC:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_VEC, kStages<LOAD_VEC, TCO, TPX>>), dim3(nwg), dim3(256),
-                         0, s, args);
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_VEC, kStages<LOAD_VEC, TCO, TPX>, WQ>), dim3(nwg),
+                         dim3(256), 0, s, args);
       break;
     case LOAD_1X1:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_1X1, kStages<LOAD_1X1, TCO, TPX>>), dim3(nwg), dim3(256),
-                         0, s, args);
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_1X1, kStages<LOAD_1X1, TCO, TPX>, WQ>), dim3(nwg),
+                         dim3(256), 0, s, args);
       break;
     default:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_TAP, kStages<LOAD_TAP, TCO, TPX>>), dim3(nwg), dim3(256),
-                         0, s, args);
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_TAP, kStages<LOAD_TAP, TCO, TPX>, WQ>), dim3(nwg),
+                         dim3(256), 0, s, args);
       break;
   }
   return hipGetLastError();
 }
 
-template <int ESZ>
+template <int ESZ, int WQ>
 hipError_t launch_esz(int tile, int loader, const IgArgs& args, dim3 nwg, hipStream_t s) {
   switch (tile) {
-    case 0: return launch_tile<ESZ, 64, 64, 2, 2>(loader, args, nwg, s);
-    case 1: return launch_tile<ESZ, 128, 128, 2, 2>(loader, args, nwg, s);
-    case 2: return launch_tile<ESZ, 64, 128, 2, 2>(loader, args, nwg, s);
-    default: return launch_tile<ESZ, 128, 64, 2, 2>(loader, args, nwg, s);
+    case 0: return launch_tile<ESZ, 64, 64, 2, 2, WQ>(loader, args, nwg, s);
+    case 1: return launch_tile<ESZ, 128, 128, 2, 2, WQ>(loader, args, nwg, s);
+    case 2: return launch_tile<ESZ, 64, 128, 2, 2, WQ>(loader, args, nwg, s);
+    default: return launch_tile<ESZ, 128, 64, 2, 2, WQ>(loader, args, nwg, s);
   }
 }
 
@@ -533,9 +590,12 @@ hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const 
   args.ksplit = p->ksplit;
   args.kt_per = p->kt_per;
   args.ws = p->ws;
+  args.kp = p->kp;
+  args.w_exp_off = (int)p->w_exp_off;
   const dim3 grid(npx * args.nco_tiles, p->ksplit);
-  hipError_t err = p->in_esz == 2 ? launch_esz<2>(p->tile, p->loader, args, grid, s)
-                                  : launch_esz<1>(p->tile, p->loader, args, grid, s);
+  hipError_t err = p->in_esz == 1 ? launch_esz<1, 0>(p->tile, p->loader, args, grid, s)
+                   : p->wq        ? launch_esz<2, 1>(p->tile, p->loader, args, grid, s)
+                                  : launch_esz<2, 0>(p->tile, p->loader, args, grid, s);
   if (err != hipSuccess || p->ksplit == 1) return err;
   return launch_splitk_reduce(p, e, y, s);
 }

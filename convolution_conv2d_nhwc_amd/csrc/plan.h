@@ -69,6 +69,9 @@ struct conv_plan {
   int ws_device;    // device the workspace lives on
   int ws_owned;     // ws was allocated for this plan (conv_destroy frees it)
   int cus;          // compute units of the device current at prepare (256 without one)
+  int wq;           // weights as bfp8 blocks (conv_desc.w_format == CONV_W_BFP8)
+  int kp;           // wq: K padded to a multiple of 16
+  int64_t w_exp_off;  // wq: byte offset of the exponents in the weight image
 };
 
 namespace convnhwc {
@@ -92,6 +95,7 @@ hipError_t launch_spp(const void* x, int dtype, void* y, int64_t n, int64_t h, i
                       hipStream_t s);
 hipError_t launch_upcat(const void* s0, int64_t c0_bytes, int up0, const void* s1, int64_t c1_bytes, int up1, void* y,
                         int64_t n, int64_t ho, int64_t wo, hipStream_t s);
+hipError_t launch_bfp8_pack(const void* w, int w_f32, int rows, int k, void* packed, hipStream_t s);
 hipError_t launch_mosaic(const void* tiles, int in_f32, void* canvas, int out_f32, int m, int th,
                          int tw, int c, int c_pad, hipStream_t s);
 

@@ -80,6 +80,12 @@ typedef enum conv_act {
   CONV_ACT_MISH = 3
 } conv_act;
 
+/* Storage of the weights (conv_desc.w_format). */
+typedef enum conv_wformat {
+  CONV_W_PLAIN = 0, /* OHWI in the layer's dtype */
+  CONV_W_BFP8 = 1   /* bfp8 blocks of 16 along K (conv_pack_bfp8) */
+} conv_wformat;
+
 typedef enum conv_status {
   CONV_OK = 0,
   CONV_E_NULL = -1,        /* a required pointer is NULL */
@@ -115,6 +121,11 @@ typedef struct conv_desc {
                              output rows per lane of the row-window kernel.
                              A configuration that cannot run the layer gives
                              CONV_E_UNSUPPORTED. */
+  int32_t w_format;       /* conv_wformat: how w is stored. CONV_W_PLAIN:
+                             OHWI of dtype. CONV_W_BFP8: block floating
+                             point as conv_pack_bfp8 writes it (BF16 layers
+                             with groups == 1 and c_in * 2 a multiple of 16
+                             only; others give CONV_E_UNSUPPORTED). */
 } conv_desc;
 
 typedef struct conv_plan conv_plan;
@@ -135,7 +146,8 @@ conv_status conv_prepare(const conv_desc* d, conv_plan** out);
 
 /* Enqueue the layer on `stream` (a hipStream_t; NULL = the default stream).
  *   x : device pointer, NHWC of dtype, 16-byte aligned.
- *   w : device pointer, OHWI of dtype, 16-byte aligned.
+ *   w : device pointer, OHWI of dtype, 16-byte aligned (for w_format
+ *       CONV_W_BFP8: the conv_pack_bfp8 image of those weights).
  *   b : F32/BF16 layers: device float[c_out] bias, or NULL for zero bias.
  *       I8 layers: device block of int32 bias[c_out] immediately followed by
  *       float scale[c_out] (one allocation, 4-byte aligned). The scales are
@@ -169,6 +181,34 @@ conv_status conv_run(const conv_plan* p, const void* x, const void* w,
  * arguments, errors and ordering rules as for conv_run. */
 conv_status conv_run_residual(const conv_plan* p, const void* x, const void* w,
                               const void* b, const void* r, void* y, void* stream);
+
+/* Block-floating-point weights (the pages' bfp8: weights stored in groups
+ * of 16 that share one exponent; YOLOv4 on Tenstorrent Wormhole, the table
+ * "Precision in the selected m640 graph" and the glossary; zerolat.eu
+ * technology page, "Spend precision selectively"). The pages fix no more
+ * than that; the library's format:
+ *   * Kp = 16 * ceil(K / 16), K = kh * kw * c_in; each output channel's K
+ *     weights, zero-padded to Kp, form Kp / 16 blocks of 16 consecutive
+ *     values along K;
+ *   * a value is m * 2^(E - 133): m a signed byte in [-127, 127], E the
+ *     block's exponent byte. With A the block's largest magnitude,
+ *     e = max(floor(log2 A), -126), m = round_half_even(w / 2^(e - 6)), and
+ *     e is raised by one if a mantissa would round to 128; E = e + 127 (an
+ *     all-zero block has E = 0);
+ *   * layout: int8 mantissas [c_out][Kp], then uint8 exponents
+ *     [c_out][Kp / 16]; conv_bfp8_bytes(c_out, k) bytes in all.
+ * Every decoded value is exactly a bf16 value, so a layer with bfp8 weights
+ * computes the bf16 convolution of the decoded weights (fp32 accumulation).
+ *
+ * conv_pack_bfp8 encodes device weights w (OHWI, c_out rows of k values,
+ * dtype CONV_F32 or CONV_BF16, finite, magnitudes below 2^126) into
+ * `packed` (device, 16-byte aligned, conv_bfp8_bytes(c_out, k) bytes, not
+ * overlapping w), on `stream`. CONV_E_NULL, CONV_E_SHAPE (c_out or k <= 0),
+ * CONV_E_UNSUPPORTED (dtype, or more than 2^31 bytes), CONV_E_ALIGN,
+ * CONV_E_ALIAS, CONV_E_HIP. conv_bfp8_bytes returns 0 for sizes <= 0. */
+int64_t conv_bfp8_bytes(int64_t c_out, int64_t k);
+conv_status conv_pack_bfp8(const void* w, int32_t w_dtype, int64_t c_out, int64_t k, void* packed,
+                           void* stream);
 
 /* Bytes of the static device array behind conv_run_noalloc (16 MiB, one copy
  * on each device the library runs on, held until the process ends). */

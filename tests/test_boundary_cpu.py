@@ -276,6 +276,35 @@ def test_noalloc_null_desc_and_status_text():
     assert _lib.STATUS[-8] == "CONV_E_SCRATCH"
 
 
+def test_bfp8_sizes_and_plan_checks():
+    L = _lib.lib()
+    assert L.conv_bfp8_bytes(64, 576) == 64 * 576 + 64 * 36
+    assert L.conv_bfp8_bytes(5, 20) == 5 * 32 + 5 * 2
+    assert L.conv_bfp8_bytes(0, 5) == 0 and L.conv_bfp8_bytes(3, -1) == 0
+    st, p = prepare(desc(c_in=64, c_out=64, w_format=1))
+    assert st == 0
+    buf = ctypes.create_string_buffer(256)
+    L.conv_describe(p, buf, 256)
+    assert b"w=bfp8" in buf.value and buf.value.startswith(b"igemm "), buf.value
+    L.conv_destroy(p)
+    for kw in (dict(c_in=3, c_out=32, w_format=1),                       # stem: generic loader
+               dict(c_in=64, c_out=64, dtype=2, out_dtype=2, w_format=1),  # int8
+               dict(c_in=64, c_out=64, groups=64, w_format=1),             # depthwise
+               dict(c_in=64, c_out=256, algo=5, w_format=1),               # a large-layer tile
+               dict(c_in=64, c_out=64, w_format=2)):                       # no such format
+        st, p = prepare(desc(**kw))
+        assert st == -3 and not p.value, kw
+
+
+def test_bfp8_pack_argument_checks_before_launch():
+    L = _lib.lib()
+    assert L.conv_pack_bfp8(None, 1, 4, 16, 4096, None) == -1
+    assert L.conv_pack_bfp8(4096, 1, 0, 16, 8192, None) == -2
+    assert L.conv_pack_bfp8(4096, 2, 4, 16, 8192, None) == -3      # int8 weights
+    assert L.conv_pack_bfp8(4096, 1, 4, 16, 8200, None) == -4      # packed not 16-byte aligned
+    assert L.conv_pack_bfp8(4096, 1, 4, 16, 4096 + 64, None) == -5  # overlapping
+
+
 def test_destroy_null_is_noop():
     assert _lib.lib().conv_destroy(None) == 0
 
