@@ -415,18 +415,26 @@ def secondary_measurements(peaks):
         return (torch.randn(shape, generator=gen, device="cuda") * sd).to(torch.bfloat16)
 
     out = {}
-    for name in ("dw_probe_bf16", "dw_probe_int8", "yolo_sweep_bf16", "yolo_sweep_int8"):
-        progress(name)
+    # (label, workload, weight format): the bf16 sweep once more with its
+    # weights in bfp8 blocks (16 values per shared exponent)
+    for label, name, wfmt in (("dw_probe_bf16", "dw_probe_bf16", "plain"), ("dw_probe_int8", "dw_probe_int8", "plain"),
+                              ("yolo_sweep_bf16", "yolo_sweep_bf16", "plain"),
+                              ("yolo_sweep_int8", "yolo_sweep_int8", "plain"),
+                              ("yolo_sweep_bf16_bfp8w", "yolo_sweep_bf16", "bfp8")):
+        progress(label)
         rows = []
         tot_flop = tot_us = 0.0
         for layer in workload(name).layers:
-            conv = _lib.Conv2d.from_layer(layer)
+            conv = _lib.Conv2d.from_layer(layer, w_format=wfmt)
             w = draw(layer, (layer.cout, layer.kh, layer.kw, layer.cin // layer.groups), "w")
+            wbytes_plain = w.numel() * w.element_size()
+            if wfmt == "bfp8":
+                w = _lib.pack_bfp8(w)
             b = draw(layer, (layer.cout,), "b")
             if layer.dtype == "i8":
                 s_ = torch.rand(layer.cout, generator=gen, device="cuda") * 0.009 + 0.001
                 b = _lib.pack_bias_scale(b, s_)
-            xy_bytes = layer.bytes()
+            xy_bytes = layer.bytes() - wbytes_plain + w.numel() * w.element_size()
             nsets = max(2, min(32, -(-768 * 2 ** 20 // xy_bytes)))
             xs = [draw(layer, (layer.n, layer.h, layer.w, layer.cin), "x") for _ in range(nsets)]
             ys = [conv.empty_output() for _ in range(nsets)]
@@ -447,7 +455,7 @@ def secondary_measurements(peaks):
             e1.record()
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1000.0 / (reps * nsets)
-            fl, by = layer.flops(), layer.bytes()
+            fl, by = layer.flops(), xy_bytes
             peak = PEAK[layer.dtype]
             t_roof = max(fl / (peak * 1e12), by / (HBM_GBS * 1e9))
             rows.append({"layer": layer.name, "kernel": conv.describe().split("kernel=")[-1], "us": round(us, 2),
@@ -463,7 +471,7 @@ def secondary_measurements(peaks):
             tot_us += us
             del xs, ys, g
             torch.cuda.empty_cache()
-        out[name] = {"layers": rows, "total_us": round(tot_us, 2),
+        out[label] = {"layers": rows, "total_us": round(tot_us, 2),
                      "tflops": round(tot_flop / (tot_us * 1e-6) / 1e12, 2)}
     progress("spp, upsample+concat, residual")
     out["spp_bf16"] = spp_measurements(gen)
