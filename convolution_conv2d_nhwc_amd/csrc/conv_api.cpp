@@ -234,6 +234,9 @@ conv_status build_plan(const conv_desc* d, conv_plan* p, void* scratch, int64_t 
   } else if (d->algo != 0 && (path != PATH_IGEMM || d->algo < 1 || d->algo > kAlgoLast)) {
     return CONV_E_UNSUPPORTED;
   }
+  const bool ws_ok = path == PATH_IGEMM && !wq && loader != LOAD_GENERIC &&
+                     (int64_t)d->kh * d->kw * cg * in_esz <= 256;
+  if (d->algo == kAlgoWs && !ws_ok) return CONV_E_UNSUPPORTED;
 
   // bfp8 weights are decoded by the implicit-GEMM kernel's 16-byte weight
   // loaders: dense bf16 layers with c_in * 2 % 16 == 0, implicit-GEMM tiles
@@ -278,7 +281,7 @@ conv_status build_plan(const conv_desc* d, conv_plan* p, void* scratch, int64_t 
       p->cus = cus;
     (void)hipGetLastError();
   }
-  if (d->algo >= kAlgoXl) {
+  if (d->algo >= kAlgoXl && d->algo < kAlgoWs) {
     if (!xl_eligible(g, in_esz, loader, d->algo - kAlgoXl)) return CONV_E_UNSUPPORTED;
     path = PATH_XL;
   }
@@ -289,6 +292,10 @@ conv_status build_plan(const conv_desc* d, conv_plan* p, void* scratch, int64_t 
       p->tile = xt;
     }
   }
+  // A reduction of at most 256 bytes on the 64x64 tile goes to the
+  // weight-stationary kernel.
+  if (path == PATH_IGEMM && ws_ok && (d->algo == kAlgoWs || (d->algo == 0 && choose_tile(g, in_esz) == 0)))
+    path = PATH_WS;
   p->path = path;
   p->tile = path == PATH_IGEMM ? (d->algo ? d->algo - 1 : choose_tile(g, in_esz))
             : path == PATH_XL && d->algo == 0 ? p->tile
@@ -364,6 +371,7 @@ conv_status run_common(const conv_plan* p, const void* x, const void* w, const v
     case PATH_DW: err = launch_dw(p, x, w, e, y, s); break;
     case PATH_SMALLK: err = launch_smallk(p, x, w, e, y, s); break;
     case PATH_XL: err = launch_xl(p, x, w, e, y, s); break;
+    case PATH_WS: err = launch_ws(p, x, w, e, y, s); break;
     default: err = launch_f32(p, x, w, e, y, s); break;
   }
   if (err != hipSuccess) {
@@ -459,6 +467,12 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
                   "kernel=igemm_xl_kernel<%d, %d, %d, %d>",
                   kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], kAlgoXl + p->tile, t.tco, t.tpx, nwg,
                   p->g.m, p->g.k, p->ksplit, p->in_esz, t.tco, t.tpx, p->loader);
+  } else if (p->path == PATH_WS) {
+    std::snprintf(buf, len,
+                  "igemm_ws dtype=%s out=%s loader=%s tile=%d co64xpx64 waves=2x2 grid=%dx%d m=%d k=%d "
+                  "kernel=igemm_ws_kernel<%d, %d, %d>",
+                  kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], kAlgoWs, ws_grid_x(p),
+                  (p->g.cout + 63) / 64, p->g.m, p->g.k, p->in_esz, p->loader, ws_ksteps(p->g, p->in_esz, p->loader));
   } else if (p->path == PATH_SMALLK) {
     int fco, ks;
     smallk_shape(p->g, p->in_esz, &fco, &ks);

@@ -14,7 +14,8 @@ enum Path {
   PATH_DW = 2,     // depthwise 3x3, VALU stencil
   PATH_F32 = 3,    // true-fp32 direct convolution, VALU
   PATH_SMALLK = 4, // MFMA, operands straight from global memory: short K, odd Cin
-  PATH_XL = 6      // MFMA, direct-to-LDS loads, software-pipelined
+  PATH_XL = 6,     // MFMA, direct-to-LDS loads, software-pipelined
+  PATH_WS = 7      // MFMA, weights held in registers, short reductions
 };
 
 // How the implicit-GEMM kernel gathers its activation operand.
@@ -40,7 +41,9 @@ extern const TileCfg kTiles[kNumTiles];  // index = algo - 1
 // configuration i.
 constexpr int kNumXlTiles = 6;
 constexpr int kAlgoXl = kNumTiles + 1;
-constexpr int kAlgoLast = kAlgoXl + kNumXlTiles - 1;
+// desc.algo kAlgoWs forces the weight-stationary kernel.
+constexpr int kAlgoWs = kAlgoXl + kNumXlTiles;
+constexpr int kAlgoLast = kAlgoWs;
 extern const TileCfg kXlTiles[kNumXlTiles];
 
 struct Geometry {
@@ -81,6 +84,9 @@ hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const 
 bool xl_eligible(const Geometry& g, int esz, int loader, int tile);
 int igemm_stages(int loader, int tile);  // register stages of the implicit-GEMM kernel
 hipError_t launch_xl(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);
+int ws_ksteps(const Geometry& g, int esz, int loader);  // 0: not for the weight-stationary kernel
+int ws_grid_x(const conv_plan* p);
+hipError_t launch_ws(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);
 hipError_t launch_smallk(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                          hipStream_t s);
 void smallk_shape(const Geometry& g, int esz, int* fco, int* ks);

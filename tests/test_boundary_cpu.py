@@ -115,6 +115,13 @@ def test_prepare_null():
     (dict(n=16, h=80, w=80, c_in=128, c_out=128, dtype="i8"), "igemm dtype=i8 out=i8 loader=tap"),  # short K, 128 channels
     (dict(n=16, h=160, w=160, c_in=128, c_out=128, dtype="bf16"), "loader=tap tile=2 co128xpx128"),
     (dict(n=16, h=40, w=40, c_in=512, c_out=320, dtype="bf16"), "igemm dtype=bf16"),  # Cout % 128
+    # reductions of at most 256 bytes on the 64x64 tile: the weight-stationary kernel
+    (dict(c_in=64, c_out=64, kh=1, kw=1, pad=(0, 0), dtype="bf16"), "igemm_ws dtype=bf16 out=bf16 loader=1x1"),
+    (dict(c_in=128, c_out=64, kh=1, kw=1, pad=(0, 0), dtype="i8"), "igemm_ws dtype=i8 out=i8 loader=1x1"),
+    (dict(c_in=24, c_out=64, kh=1, kw=1, pad=(0, 0), stride=(2, 2), dtype="bf16"),
+     "igemm_ws dtype=bf16 out=bf16 loader=vec16"),
+    (dict(c_in=64, c_out=64, dtype="bf16"), "igemm dtype=bf16 out=bf16 loader=tap"),  # K = 1152 bytes
+    (dict(c_in=192, c_out=64, kh=1, kw=1, pad=(0, 0), dtype="bf16"), "igemm dtype=bf16 out=bf16 loader=1x1"),
 ])
 def test_path_selection(layer, expect):
     args = dict(n=1, h=16, w=16, kh=3, kw=3, stride=(1, 1), pad=(1, 1), groups=1, act="relu")
@@ -137,20 +144,23 @@ def test_out_shape_floor_rule_and_per_axis_pads():
 
 def test_forced_algo_and_count():
     """Every algo id forces its own kernel configuration on a layer all of them
-    accept (3x3, 128-byte channel blocks, Cout = 256); the large-layer kernel
-    refuses a Cout that is not a multiple of its channel tile."""
+    accept (1x1 over one 128-byte channel block, Cout = 256); the large-layer
+    kernel refuses a Cout that is not a multiple of its channel tile, the
+    weight-stationary kernel a reduction over 256 bytes."""
     n = _lib.lib().conv_algo_count()
     assert n >= 1
     kinds = set()
     for a in range(1, n + 1):
-        c = Conv2d(1, 20, 20, 64, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=a)
+        c = Conv2d(1, 20, 20, 64, 256, 1, 1, (1, 1), (0, 0), dtype="bf16", algo=a)
         d = c.describe()
         assert "tile=%d " % a in d
         kinds.add(d.split()[0])
         c.close()
-    assert kinds == {"igemm", "igemm_xl"}
+    assert kinds == {"igemm", "igemm_xl", "igemm_ws"}
+    with pytest.raises(ConvError):
+        Conv2d(1, 20, 20, 64, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=n)  # 1152-byte reduction
     xl = [a for a in range(1, n + 1)
-          if Conv2d(1, 20, 20, 64, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=a).describe().startswith("igemm_xl")]
+          if Conv2d(1, 20, 20, 64, 256, 1, 1, (1, 1), (0, 0), dtype="bf16", algo=a).describe().startswith("igemm_xl")]
     for a in xl:
         with pytest.raises(ConvError):
             Conv2d(1, 20, 20, 64, 64, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=a)   # Cout 64

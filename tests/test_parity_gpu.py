@@ -21,14 +21,16 @@ ALGO_COUNT = _lib.lib().conv_algo_count()
 
 
 def _algo_describe(algo):
-    # a layer every forced algorithm accepts: 3x3, 128-byte channel blocks, Cout = 256
-    return _lib.Conv2d(1, 20, 20, 64, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=algo).describe()
+    # a layer every forced algorithm accepts: 1x1 over one 128-byte channel
+    # block (a 128-byte reduction), Cout = 256
+    return _lib.Conv2d(1, 20, 20, 64, 256, 1, 1, (1, 1), (0, 0), dtype="bf16", algo=algo).describe()
 
 
 ALGO_DESC = {a: _algo_describe(a) for a in range(1, ALGO_COUNT + 1)}
 TILE_ALGOS = [a for a, d in ALGO_DESC.items() if d.startswith("igemm ")]
 XL_ALGOS = [a for a, d in ALGO_DESC.items() if d.startswith("igemm_xl ")]
-assert len(TILE_ALGOS) + len(XL_ALGOS) == ALGO_COUNT
+WS_ALGOS = [a for a, d in ALGO_DESC.items() if d.startswith("igemm_ws ")]
+assert len(TILE_ALGOS) + len(XL_ALGOS) + len(WS_ALGOS) == ALGO_COUNT and WS_ALGOS
 
 # Tiles wider than 256 rows on either side need a 16-byte-vector loader; the
 # element-wise gather refuses them at prepare time.
@@ -38,20 +40,24 @@ BIG_TILES = {a for a in TILE_ALGOS if max(map(int, re.search(r"co(\d+)xpx(\d+)",
 def forced_tiles(layer):
     """Every forced MFMA tile the layer accepts. Only the generic loader may
     refuse a tile wider than 256; the direct-to-LDS kernel refuses layers
-    without 128-byte channel blocks or with Cout not a multiple of its tile."""
+    without 128-byte channel blocks or with Cout not a multiple of its tile;
+    the weight-stationary kernel refuses element-wise gathers and reductions
+    over 256 bytes."""
     out = []
-    for a in TILE_ALGOS + XL_ALGOS:
+    for a in TILE_ALGOS + XL_ALGOS + WS_ALGOS:
         try:
             _lib.Conv2d.from_layer(layer, algo=a).close()
             out.append(a)
         except _lib.ConvError as e:
             assert "CONV_E_UNSUPPORTED" in str(e), (layer.name, a, str(e))
             d = _lib.Conv2d.from_layer(layer).describe()
+            cbytes = layer.cin * (2 if layer.dtype == "bf16" else 1)
             if a in BIG_TILES:
                 assert "loader=generic" in d or "smallk" in d, (layer.name, a, d)
+            elif a in WS_ALGOS:
+                assert cbytes % 16 or layer.kh * layer.kw * cbytes > 256 or layer.groups > 1, (layer.name, a, d)
             else:
                 assert a in XL_ALGOS, (layer.name, a, d)
-                cbytes = layer.cin * (2 if layer.dtype == "bf16" else 1)
                 tco = int(re.search(r"co(\d+)x", ALGO_DESC[a]).group(1))
                 assert cbytes % 128 or layer.cout % tco or layer.kh * layer.kw > 32, (layer.name, a, d)
     return out
