@@ -467,6 +467,17 @@ def secondary_measurements(peaks):
                          "frac_measured_mfma": round(fl / (us * 1e-6) / 1e12 / peaks["mfma_" + layer.dtype]["value"],
                                                      4),
                          "dtype": layer.dtype, "buffer_sets": nsets})
+            if layer.depthwise:
+                # the same bytes moved by the library's read+write stream, same
+                # buffer rotation and back-to-back launches: what a pure copy of
+                # this size reaches on this GPU (launch gaps and ramp included)
+                half = (xy_bytes // 2) // 16 * 16
+                cs = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+                cd = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+                cus = _time_graph([lambda i=i: _lib.probe_copy(cs[i], cd[i]) for i in range(nsets)])
+                rows[-1]["copy_same_bytes_us"] = round(cus, 2)
+                rows[-1]["frac_copy_same_bytes"] = round(cus / us, 4)
+                del cs, cd
             tot_flop += fl
             tot_us += us
             del xs, ys, g
