@@ -26,7 +26,7 @@ Prints ONE JSON line:
 
 Options: --gpus N (only 1 is supported), --steps K, --warmup W,
 --workload NAME (another stack, for information), --no-cpu-baseline,
---no-secondary,
+--no-secondary, --no-stacks (skip the small stacks of the secondary set),
 --calib-copy MIB (run only a plain device copy of known size, for the
 counter calibration of the traffic figure).
 """
@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the depthwise-probe and N=16-sweep measurements")
+    ap.add_argument("--no-stacks", action="store_true",
+                    help="skip the small-stack timings of the secondary measurements")
     return ap.parse_args()
 
 
@@ -207,7 +209,7 @@ def main():
         progress("CPU oracle ladder")
         cpu = cpu_baseline(wl)
 
-    secondary = None if args.no_secondary else secondary_measurements(peaks)
+    secondary = None if args.no_secondary else secondary_measurements(peaks, stacks=not args.no_stacks)
 
     dt = wl.layers[0].dtype
     out = {
@@ -388,7 +390,7 @@ def measured_peaks():
     return out
 
 
-def secondary_measurements(peaks):
+def secondary_measurements(peaks, stacks=True):
     """Per-layer rates of the depthwise probe (against the HBM peak) and of the
     N=16 YOLO sweep (against the MFMA peak), outside the step's timed region.
     Inputs are seeded device tensors of each layer's shape and value law;
@@ -493,8 +495,9 @@ def secondary_measurements(peaks):
         for row in sec.get("layers", []) if isinstance(sec, dict) else []:
             if "gbs" in row:
                 row["frac_measured_copy"] = round(row["gbs"] / copy, 4)
-    progress("small stacks")
-    out["stacks"] = stack_measurements()
+    if stacks:
+        progress("small stacks")
+        out["stacks"] = stack_measurements()
     out["measured_peaks"] = peaks
     return out
 
