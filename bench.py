@@ -3,9 +3,11 @@
 
 A step is one pass of the 640x640 YOLO layer stack (four 320x320x3 fp32
 tiles mosaic-packed into a 640x640x3 bf16 canvas, then nine bf16 convs with
-fused bias + Mish, N=1), captured once into a HIP graph and replayed. All
-inputs, weights and intermediate buffers are resident in device memory
-before the timed region starts.
+fused bias + Mish, N=1), captured once into a HIP graph and replayed. Each
+3x3 layer that is followed by a 1x1 layer the library can fuse (L2+L3,
+L5+L6) runs with it as one launch, so the graph has 8 nodes. All inputs,
+weights and intermediate buffers are resident in device memory before the
+timed region starts.
 
 Prints ONE JSON line:
   value         TFLOP/s of the stack (26.5 GFLOP per step, every tap counted)
@@ -14,7 +16,8 @@ Prints ONE JSON line:
                 HIP events on the stream it runs on, against MI355X peaks
   cpu_baseline  the CPU oracle on the same stack: all host threads (median
                 of 5 passes), with a 1-thread rung (median of 3)
-  layers        per-layer time and roofline fraction
+  layers        per-node time and roofline fraction (a fused pair's bytes
+                leave out the intermediate tensor it never stores)
 
   secondary     per-layer rates of the depthwise probe (vs the HBM peak) and
                 of the N=16 YOLO sweep (vs the MFMA peak), measured after the
@@ -27,6 +30,7 @@ Prints ONE JSON line:
 Options: --gpus N (only 1 is supported), --steps K, --warmup W,
 --workload NAME (another stack, for information), --no-cpu-baseline,
 --no-secondary, --no-stacks (skip the small stacks of the secondary set),
+--no-fuse (every layer its own launch),
 --calib-copy MIB (run only a plain device copy of known size, for the
 counter calibration of the traffic figure).
 """
@@ -60,6 +64,8 @@ def parse():
                     help="skip the depthwise-probe and N=16-sweep measurements")
     ap.add_argument("--no-stacks", action="store_true",
                     help="skip the small-stack timings of the secondary measurements")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="launch every layer on its own (no fused 3x3 + 1x1 pairs)")
     return ap.parse_args()
 
 
@@ -124,7 +130,8 @@ def main():
         sys.exit(2)
 
     # ---- resident inputs, weights and buffers; one step captured as a graph --
-    stack = Stack(wl)
+    # (a 3x3 layer and the 1x1 layer after it run as one fused launch)
+    stack = Stack(wl, fuse=not args.no_fuse)
     convs, canvas = stack.convs, stack.canvas
     graph = stack.capture()
 
@@ -159,14 +166,18 @@ def main():
                        "gflop": 0.0, "mbytes": mb / 1e6, "bound": "hbm",
                        "frac": (mb / (HBM_GBS * 1e9)) / (dur_us[0] * 1e-6)})
         j = 1
-    for i, layer in enumerate(wl.layers):
-        us = dur_us[j + i]
-        fl, by = layer.flops(), layer.bytes()
-        t_mfma = fl / (PEAK[layer.dtype] * 1e12)
+    for k, node in enumerate(stack.nodes()):
+        us = dur_us[j + k]
+        ls = [wl.layers[i] for i in node]
+        fl = sum(l.flops() for l in ls)
+        # a fused pair: the intermediate tensor is neither written nor read
+        by = sum(l.bytes() for l in ls) - 2 * sum(l.n * l.ho * l.wo * l.cout * 2 for l in ls[:-1])
+        dt = ls[0].dtype
+        t_mfma = fl / (PEAK[dt] * 1e12)
         t_hbm = by / (HBM_GBS * 1e9)
         bound = "mfma" if t_mfma >= t_hbm else "hbm"
-        desc = convs[i].describe()
-        layers.append({"name": layer.name, "kernel": desc.split(" kernel=")[-1] if " kernel=" in desc else desc,
+        desc = _lib.describe_fused(convs[node[0]], convs[node[1]]) if len(node) == 2 else convs[node[0]].describe()
+        layers.append({"name": "+".join(l.name for l in ls), "kernel": desc.split(" kernel=")[-1],
                        "desc": desc, "us": us, "gflop": fl / 1e9, "mbytes": by / 1e6,
                        "tflops": fl / (us * 1e-6) / 1e12, "gbs": by / (us * 1e-6) / 1e9, "bound": bound,
                        "frac": max(t_mfma, t_hbm) / (us * 1e-6)})
@@ -229,6 +240,8 @@ def main():
                    "input": "640x640x3 from 4x320x320x3" if wl.mosaic else "%dx%dx%d" % (
                        wl.layers[0].h, wl.layers[0].w, wl.layers[0].cin),
                    "gflop_per_step": total_flop / 1e9, "timing": "hipGraph replay, HIP events",
+                   "graph_nodes": len(stack.launches()), "fused_pairs": ["+".join(wl.layers[i].name for i in n)
+                                                                        for n in stack.nodes() if len(n) == 2],
                    "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -321,15 +334,15 @@ def stack_measurements():
     out = {}
     for name in ("mnist_f32", "kws_int8", "vww_bf16", "yolo640_bf16"):
         wl = workload(name)
-        st = Stack(wl)
+        st = Stack(wl, fuse=True)
         seq = st.launches()
         st.step()
         torch.cuda.synchronize()
         med, thr = graph_median_us(seq)
         durs, _ = per_launch_us(seq)
-        names = (["mosaic_pack"] if st.canvas is not None else []) + [l.name for l in wl.layers]
-        kern = (["mosaic_vec8_kernel"] if st.canvas is not None else []) + [
-            c.describe().split("kernel=")[-1] for c in st.convs]
+        names = (["mosaic_pack"] if st.canvas is not None else []) + [
+            "+".join(wl.layers[i].name for i in n) for n in st.nodes()]
+        kern = (["mosaic_vec8_kernel"] if st.canvas is not None else []) + [st.node_kernel(n) for n in st.nodes()]
         row = {"us_per_stack_median": round(med, 2), "us_per_stack_back_to_back": round(thr, 2),
                "replays": 200, "warmup": 20, "nodes": len(seq),
                "gflop": round(wl.flops() / 1e9, 5),

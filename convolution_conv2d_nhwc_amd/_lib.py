@@ -86,6 +86,12 @@ def lib():
     I32 = ctypes.c_int32
     L.conv_upsample_concat.argtypes = [P, I32, I32, P, I32, I32, I32, P, I32, I32, I32, P]
     L.conv_upsample_concat.restype = ctypes.c_int
+    L.conv_fuse_check.argtypes = [P, P]
+    L.conv_fuse_check.restype = ctypes.c_int
+    L.conv_describe_fused.argtypes = [P, P, ctypes.c_char_p, ctypes.c_int32]
+    L.conv_describe_fused.restype = ctypes.c_int
+    L.conv_run_fused.argtypes = [P] * 9
+    L.conv_run_fused.restype = ctypes.c_int
     L.conv_bfp8_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
     L.conv_bfp8_bytes.restype = ctypes.c_int64
     L.conv_pack_bfp8.argtypes = [P, I32, ctypes.c_int64, ctypes.c_int64, P, P]
@@ -357,3 +363,34 @@ def pack_bfp8(w: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) 
     _check(lib().conv_pack_bfp8(w.data_ptr(), DTYPES["f32" if w.dtype == torch.float32 else "bf16"], c_out, k,
                                 out.data_ptr(), _stream_handle(stream)), "conv_pack_bfp8")
     return out
+
+
+def fusable(c1: Conv2d, c2: Conv2d) -> bool:
+    """Whether conv_run_fused takes the pair (c1's layer, then c2's 1x1)."""
+    return lib().conv_fuse_check(c1._plan, c2._plan) == 0
+
+
+def describe_fused(c1: Conv2d, c2: Conv2d) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().conv_describe_fused(c1._plan, c2._plan, buf, 256), "conv_describe_fused")
+    return buf.value.decode()
+
+
+def run_fused(c1: Conv2d, c2: Conv2d, x: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor],
+              w2: torch.Tensor, b2: Optional[torch.Tensor], y: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """c2(c1(x)) in one launch; c1's output is never stored."""
+    c1._chk(x, "x", TORCH_DT[c1.dtype], c1.in_shape)
+    c1._chk(w1, "w1", c1._w_dtype(), c1.w_shape)
+    c2._chk(w2, "w2", c2._w_dtype(), c2.w_shape)
+    for b, n in ((b1, "b1"), (b2, "b2")):
+        if b is not None:
+            c1._chk(b, n, torch.float32, None)
+    if y is None:
+        y = c2.empty_output(x.device)
+    c2._chk(y, "y", TORCH_DT[c2.out_dtype], c2.out_shape)
+    st = lib().conv_run_fused(c1._plan, c2._plan, x.data_ptr(), w1.data_ptr(), None if b1 is None else b1.data_ptr(),
+                              w2.data_ptr(), None if b2 is None else b2.data_ptr(), y.data_ptr(),
+                              _stream_handle(stream))
+    _check(st, "conv_run_fused")
+    return y

@@ -425,6 +425,70 @@ conv_status conv_run_noalloc(const conv_desc* d, const void* x, const void* w, c
   return run_common(&p, x, w, b, r, y, stream);
 }
 
+namespace {
+
+// A KxK bf16 layer on the implicit-GEMM kernel, unsplit, whose output tile
+// can hold all its channels (64 or 128, one workgroup per 64 pixels),
+// followed by a 1x1 s1 p0 bf16 layer on exactly that output with at most 64
+// output channels.
+bool fused_1x1_ok(const conv_plan* p1, const conv_plan* p2) {
+  const conv_desc& a = p1->d;
+  const conv_desc& b = p2->d;
+  if (a.dtype != CONV_BF16 || a.out_dtype != CONV_BF16 || p1->path != PATH_IGEMM || p1->wq || p1->ksplit != 1)
+    return false;
+  if (p1->loader != LOAD_TAP && p1->loader != LOAD_VEC) return false;
+  if (p1->g.cout != 64 && p1->g.cout != 128) return false;
+  if (b.dtype != CONV_BF16 || b.out_dtype != CONV_BF16 || b.groups != 1 || p2->wq) return false;
+  if (b.kh != 1 || b.kw != 1 || b.stride_h != 1 || b.stride_w != 1 || b.pad_h != 0 || b.pad_w != 0) return false;
+  if (b.n != a.n || b.h != p1->g.ho || b.w != p1->g.wo || b.c_in != p1->g.cout) return false;
+  return p2->g.cout <= 64 && (p2->g.cout & 3) == 0;
+}
+
+}  // namespace
+
+conv_status conv_fuse_check(const conv_plan* p1, const conv_plan* p2) {
+  if (!p1 || !p2) return CONV_E_NULL;
+  return fused_1x1_ok(p1, p2) ? CONV_OK : CONV_E_UNSUPPORTED;
+}
+
+conv_status conv_describe_fused(const conv_plan* p1, const conv_plan* p2, char* buf, int32_t len) {
+  if (!p1 || !p2 || !buf || len <= 0) return CONV_E_NULL;
+  if (!fused_1x1_ok(p1, p2)) return CONV_E_UNSUPPORTED;
+  static const char* kLoader[] = {"generic", "vec16", "1x1", "tap"};
+  const int tco = p1->g.cout;
+  std::snprintf(buf, len,
+                "igemm fused_1x1 loader=%s co%dxpx64 then 1x1 %d->%d wgs=%d m=%d k=%d "
+                "kernel=igemm_kernel<2, %d, 64, 2, 2, %d, %d, 0, 1>",
+                kLoader[p1->loader], tco, tco, p2->g.cout, (p1->g.m + 63) / 64, p1->g.m, p1->g.k, tco, p1->loader,
+                (tco + 64 >= 512) ? 1 : 2);
+  return CONV_OK;
+}
+
+conv_status conv_run_fused(const conv_plan* p1, const conv_plan* p2, const void* x, const void* w1, const void* b1,
+                           const void* w2, const void* b2, void* y, void* stream) {
+  if (!p1 || !p2 || !x || !w1 || !w2 || !y) return CONV_E_NULL;
+  if (!fused_1x1_ok(p1, p2)) return CONV_E_UNSUPPORTED;
+  if (((uintptr_t)x | (uintptr_t)w1 | (uintptr_t)w2 | (uintptr_t)y) & 15) return CONV_E_ALIGN;
+  if (((uintptr_t)b1 | (uintptr_t)b2) & 3) return CONV_E_ALIGN;
+  if (ranges_overlap(y, p2->y_bytes, x, p1->x_bytes) || ranges_overlap(y, p2->y_bytes, w1, p1->w_bytes) ||
+      ranges_overlap(y, p2->y_bytes, w2, p2->w_bytes) || ranges_overlap(y, p2->y_bytes, b1, p1->b_bytes) ||
+      ranges_overlap(y, p2->y_bytes, b2, p2->b_bytes))
+    return CONV_E_ALIAS;
+  Epi e1, e2;
+  std::memset(&e1, 0, sizeof(e1));
+  std::memset(&e2, 0, sizeof(e2));
+  e1.bias = static_cast<const float*>(b1);
+  e1.act = p1->d.act;
+  e2.bias = static_cast<const float*>(b2);
+  e2.act = p2->d.act;
+  const hipError_t err = launch_igemm_fused(p1, p2, x, w1, e1, w2, e2, y, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(err));
+    return CONV_E_HIP;
+  }
+  return CONV_OK;
+}
+
 conv_status conv_destroy(conv_plan* p) {
   if (p && p->ws && p->ws_owned) {
     int cur = 0;
@@ -455,7 +519,7 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
     const long nwg = (long)((p->g.cout + t.tco - 1) / t.tco) * ((p->g.m + t.tpx - 1) / t.tpx);
     std::snprintf(buf, len,
                   "igemm dtype=%s out=%s%s loader=%s tile=%d co%dxpx%d waves=%dx%d wgs=%ld m=%d k=%d "
-                  "ksplit=%d kernel=igemm_kernel<%d, %d, %d, %d, %d, %d, %d, %d>",
+                  "ksplit=%d kernel=igemm_kernel<%d, %d, %d, %d, %d, %d, %d, %d, 0>",
                   kDt[p->d.dtype], kDt[p->d.out_dtype], p->wq ? " w=bfp8" : "", kLoader[p->loader], p->tile + 1,
                   t.tco, t.tpx, t.wco, t.wpx, nwg, p->g.m, p->g.k, p->ksplit, p->in_esz, t.tco, t.tpx, t.wco, t.wpx,
                   p->loader, igemm_stages(p->loader, p->tile), p->wq);

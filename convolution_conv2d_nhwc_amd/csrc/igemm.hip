@@ -34,6 +34,7 @@
 // 4*(l/16) .. 4*(l/16)+3 of column l % 16, i.e. four consecutive output
 // channels of one pixel, which the epilogue stores as one NHWC vector.
 #include <algorithm>
+#include <cstring>
 
 #include "igemm_common.h"
 
@@ -67,6 +68,12 @@ struct IgArgs {
   void* ws;      // [ksplit][m][cout] fp32 / int32 partial sums
   int kp;        // bfp8 weights: K padded to a multiple of 16 (mantissa row length)
   int w_exp_off; // bfp8 weights: byte offset of the exponent bytes in w
+  // FU: a following 1x1 layer (c_in = this layer's Cout = TCO) applied to
+  // the tile before anything is stored; y is then that layer's output
+  const char* w2;  // its weights [cout2][TCO] bf16
+  int w2_bytes;
+  int cout2;       // <= 64, a multiple of 4
+  Epi e2;          // its bias and activation
 };
 
 // bfp8 weights (WQ): eight consecutive mantissas of one block (two dwords)
@@ -98,7 +105,7 @@ __device__ __forceinline__ i32x4 bfp8_to_bf16x8(const i32x4& q) {
 #define IGEMM_WPE 2
 #endif
 
-template <int ESZ, int TCO, int TPX, int WCO, int WPX, int LOADER, int D, int WQ>
+template <int ESZ, int TCO, int TPX, int WCO, int WPX, int LOADER, int D, int WQ, int FU>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))) void igemm_kernel(IgArgs a) {
   constexpr int VE = 16 / ESZ;      // elements per 16-byte chunk
   constexpr int BKE = kBKB / ESZ;   // elements per K-tile row
@@ -109,6 +116,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
   static_assert(FCO >= 1 && FPX >= 1 && WCO * WPX == 4, "bad tile");
   static_assert(LOADER != LOAD_GENERIC || D == 1, "generic loader is single-stage");
   static_assert(WQ == 0 || (ESZ == 2 && LOADER != LOAD_GENERIC), "bfp8 weights: bf16, 16-byte loaders");
+  static_assert(FU == 0 || (ESZ == 2 && TPX == 64 && (TCO == 64 || TCO == 128) && WCO == 2 && WPX == 2 && WQ == 0),
+                "fused 1x1: bf16, tiles 64x64 or 128x64");
   typedef typename Mfma<ESZ>::acc_t acc_t;
 
   __shared__ __attribute__((aligned(16))) char smem[2 * (TCO + TPX) * kBKB];
@@ -408,6 +417,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
 #pragma unroll
     for (int j = 0; j < FPX; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
+  // FU: the second layer's weights as MFMA A fragments, loaded now: wave
+  // (wave >> 1) owns its output channels 32 (wave >> 1) + 16 i + (lane & 15);
+  // K-step s covers bytes 64 s .. 64 s + 63 of the TCO-channel reduction
+  constexpr int KS2 = FU ? TCO / 32 : 1;
+  i32x4 a2[2][KS2];
+  if constexpr (FU) {
+    const __amdgpu_buffer_rsrc_t rw2 = rsrc(a.w2, a.w2_bytes);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c2 = 32 * (wave >> 1) + 16 * i + (lane & 15);
+#pragma unroll
+      for (int s2 = 0; s2 < KS2; ++s2)
+        a2[i][s2] = bload16(rw2, c2 < a.cout2 ? (uint32_t)(c2 * TCO * 2 + 64 * s2 + 16 * (lane >> 4)) : kOOB);
+    }
+  }
+
   // MFMA operand addresses within a stage: row (lane & 15) of each 16-row
   // fragment, chunk 4*s + (lane >> 4) of the tile.
   const int a_row0 = wco * (TCO / WCO) + (lane & 15);
@@ -472,6 +497,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
   // ---- fused epilogue -------------------------------------------------
   const int co_w = co0 + wco * (TCO / WCO) + 4 * (lane >> 4);
   const int px_w = px0 + wpx * (TPX / WPX) + (lane & 15);
+  if constexpr (FU) {
+    // This layer's output tile, bias + activation + bf16 rounding as a store
+    // would do, goes into LDS as the B operand of the 1x1 layer: pixel rows
+    // of 128-byte channel blocks (block kt2 = channels 64 kt2 .. 64 kt2 + 63),
+    // the swizzled layout of the K loop's tiles.
+    __syncthreads();  // every wave is done with the K loop's buffers
+    char* const Y = smem;
+    with_epilogue<2>(OUT_BF16, a.e.act, [&](auto, auto ac) {
+      constexpr int ACT = decltype(ac)::value;
+#pragma unroll
+      for (int i = 0; i < FCO; ++i) {
+        const int col = wco * (TCO / WCO) + 4 * (lane >> 4) + 16 * i;  // channel within the tile
+        const QuadConsts q = load_quad_consts_t<2>(a.e, co0 + col, g.cout);
+#pragma unroll
+        for (int j = 0; j < FPX; ++j) {
+          const int row = wpx * (TPX / WPX) + (lane & 15) + 16 * j;
+          uint32_t h[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_bits(act_t<ACT>(acc[i][j][r] + q.bsf[r]));
+          *reinterpret_cast<u32x2*>(Y + (col >> 6) * TPX * kBKB + lds_off(row, (col & 63) >> 3) + (col & 4) * 2) =
+              u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        }
+      }
+    });
+    __syncthreads();
+    // the 1x1 layer: 64 (<= cout2) channels x 64 pixels, 2 x 2 waves of 32 x 32
+    acc_t acc2[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc2[i][j] = acc_t{0, 0, 0, 0};
+    const int row2 = 32 * (wave & 1) + (lane & 15);
+#pragma unroll
+    for (int kt2 = 0; kt2 < TCO / 64; ++kt2) {
+      const char* B2 = Y + kt2 * TPX * kBKB;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int c = 4 * s + (lane >> 4);
+        i32x4 bf[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const i32x4*>(B2 + lds_off(row2 + 16 * j, c));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc2[i][j] = Mfma<2>::run(a2[i][2 * kt2 + s], bf[j], acc2[i][j]);
+      }
+    }
+    const OutRef o2 = out_ref(a.y, g.m, a.cout2, 2, nullptr);
+    const int c2w = 32 * (wave >> 1) + 4 * (lane >> 4);
+    const int p2w = px0 + 32 * (wave & 1) + (lane & 15);
+    with_epilogue<2>(OUT_BF16, a.e2.act, [&](auto oc, auto ac) {
+      constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const QuadConsts q = load_quad_consts_t<2>(a.e2, c2w + 16 * i, a.cout2);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) store_quad_t<2, OUT, ACT>(acc2[i][j], q, c2w + 16 * i, p2w + 16 * j, o2);
+      }
+    });
+    return;
+  }
   if (a.ksplit > 1) {
     // raw partial sums of this split; Cout % 4 == 0 on this path
     acc_t* ws = reinterpret_cast<acc_t*>(a.ws) + (size_t)blockIdx.y * g.m * (g.cout / 4);
@@ -531,21 +617,21 @@ hipError_t launch_tile(int loader, const IgArgs& args, dim3 nwg, hipStream_t s) 
     case LOAD_GENERIC:
       // the element-wise gather maps at least one thread to each tile row
       if constexpr (TCO <= 256 && TPX <= 256 && WQ == 0)
-        hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_GENERIC, kStages<LOAD_GENERIC, TCO, TPX>, 0>),
+        hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_GENERIC, kStages<LOAD_GENERIC, TCO, TPX>, 0, 0>),
                            dim3(nwg), dim3(256), 0, s, args);
       else
         return hipErrorInvalidValue;  // refused by conv_prepare
       break;
     case LOAD_VEC:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_VEC, kStages<LOAD_VEC, TCO, TPX>, WQ>), dim3(nwg),
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_VEC, kStages<LOAD_VEC, TCO, TPX>, WQ, 0>), dim3(nwg),
                          dim3(256), 0, s, args);
       break;
     case LOAD_1X1:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_1X1, kStages<LOAD_1X1, TCO, TPX>, WQ>), dim3(nwg),
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_1X1, kStages<LOAD_1X1, TCO, TPX>, WQ, 0>), dim3(nwg),
                          dim3(256), 0, s, args);
       break;
     default:
-      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_TAP, kStages<LOAD_TAP, TCO, TPX>, WQ>), dim3(nwg),
+      hipLaunchKernelGGL((igemm_kernel<ESZ, TCO, TPX, WCO, WPX, LOAD_TAP, kStages<LOAD_TAP, TCO, TPX>, WQ, 0>), dim3(nwg),
                          dim3(256), 0, s, args);
       break;
   }
@@ -560,6 +646,13 @@ hipError_t launch_esz(int tile, int loader, const IgArgs& args, dim3 nwg, hipStr
     case 2: return launch_tile<ESZ, 64, 128, 2, 2, WQ>(loader, args, nwg, s);
     default: return launch_tile<ESZ, 128, 64, 2, 2, WQ>(loader, args, nwg, s);
   }
+}
+
+template <int TCO, int LOADER>
+hipError_t launch_fused_tile(const IgArgs& args, dim3 nwg, hipStream_t s) {
+  hipLaunchKernelGGL((igemm_kernel<2, TCO, 64, 2, 2, LOADER, kStages<LOADER, TCO, 64>, 0, 1>), dim3(nwg), dim3(256), 0,
+                     s, args);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -598,6 +691,38 @@ hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const 
                                   : launch_esz<2, 0>(p->tile, p->loader, args, grid, s);
   if (err != hipSuccess || p->ksplit == 1) return err;
   return launch_splitk_reduce(p, e, y, s);
+}
+
+// p1's layer with p2's 1x1 layer applied to each output tile before any
+// store (fused_1x1_ok has validated the pair): one workgroup per 64-pixel
+// tile holding all of p1's output channels.
+hipError_t launch_igemm_fused(const conv_plan* p1, const conv_plan* p2, const void* x, const void* w1, const Epi& e1,
+                              const void* w2, const Epi& e2, void* y, hipStream_t s) {
+  IgArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.x = static_cast<const char*>(x);
+  args.w = static_cast<const char*>(w1);
+  args.y = y;
+  args.e = e1;
+  args.g = p1->g;
+  args.out_kind = OUT_BF16;
+  args.x_bytes = (int)p1->x_bytes;
+  args.w_bytes = (int)p1->w_bytes;
+  args.rcp_c = 1.0f / (float)p1->g.c;
+  args.rcp_kw = 1.0f / (float)p1->g.kw;
+  args.x_shift = (p1->g.ph * p1->g.w + p1->g.pw) * p1->g.c * p1->in_esz;
+  args.nco_tiles = 1;
+  args.px_fastest = 0;
+  args.ksplit = 1;
+  args.kt_per = (p1->g.k * 2 + kBKB - 1) / kBKB;
+  args.w2 = static_cast<const char*>(w2);
+  args.w2_bytes = (int)p2->w_bytes;
+  args.cout2 = p2->g.cout;
+  args.e2 = e2;
+  const dim3 grid((p1->g.m + 63) / 64, 1);
+  const bool tap = p1->loader == LOAD_TAP;
+  if (p1->g.cout == 64) return tap ? launch_fused_tile<64, LOAD_TAP>(args, grid, s) : launch_fused_tile<64, LOAD_VEC>(args, grid, s);
+  return tap ? launch_fused_tile<128, LOAD_TAP>(args, grid, s) : launch_fused_tile<128, LOAD_VEC>(args, grid, s);
 }
 
 }  // namespace convnhwc

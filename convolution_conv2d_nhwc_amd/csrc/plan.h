@@ -84,6 +84,8 @@ hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const 
 bool xl_eligible(const Geometry& g, int esz, int loader, int tile);
 int igemm_stages(int loader, int tile);  // register stages of the implicit-GEMM kernel
 hipError_t launch_xl(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);
+hipError_t launch_igemm_fused(const conv_plan* p1, const conv_plan* p2, const void* x, const void* w1, const Epi& e1,
+                              const void* w2, const Epi& e2, void* y, hipStream_t s);
 int ws_ksteps(const Geometry& g, int esz, int loader);  // 0: not for the weight-stationary kernel
 int ws_grid_x(const conv_plan* p);
 hipError_t launch_ws(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);

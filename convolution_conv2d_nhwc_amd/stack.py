@@ -25,9 +25,14 @@ from .data import Workload, layer_params, network_input
 class Stack:
     """Plans, resident weights and buffers of a workload on the current
     device. ``step()`` enqueues one pass on the current stream;
-    ``capture()`` records one pass into a graph that ``replay()`` runs."""
+    ``capture()`` records one pass into a graph that ``replay()`` runs.
 
-    def __init__(self, wl: Workload, seed: int = 0, device: str = "cuda"):
+    With ``fuse``, a layer followed by a 1x1 layer that the library can run
+    in the same launch (``conv_run_fused``: the first layer's output tile
+    goes through the 1x1 layer before anything is stored) is launched as one
+    node; the first layer's output buffer is then never written."""
+
+    def __init__(self, wl: Workload, seed: int = 0, device: str = "cuda", fuse: bool = False):
         if not wl.chained and len(wl.layers) != 1:
             raise ValueError("%s is neither a chained stack nor a single layer" % wl.name)
         self.wl = wl
@@ -51,6 +56,16 @@ class Stack:
             m, th, tw, c = wl.mosaic
             self.canvas = torch.empty((m, 2 * th, 2 * tw, c), dtype=torch.bfloat16, device=device)
         self.graph: Optional[torch.cuda.CUDAGraph] = None
+        # fused[i]: layer i is launched together with layer i + 1
+        self.fused = [False] * len(self.convs)
+        if fuse:
+            i = 0
+            while i + 1 < len(self.convs):
+                if _lib.fusable(self.convs[i], self.convs[i + 1]):
+                    self.fused[i] = True
+                    i += 2
+                else:
+                    i += 1
 
     # each layer's input: the canvas (or the network input), then the
     # previous layer's output buffer
@@ -59,15 +74,43 @@ class Stack:
             return self.bufs[i - 1]
         return self.canvas if self.canvas is not None else self.x0
 
+    def nodes(self) -> List[tuple]:
+        """The layers of each launch: (i,) or (i, i + 1) for a fused pair."""
+        out, i = [], 0
+        while i < len(self.convs):
+            if self.fused[i]:
+                out.append((i, i + 1))
+                i += 2
+            else:
+                out.append((i,))
+                i += 1
+        return out
+
     def launches(self) -> List[Callable[[], None]]:
-        """The pass as a list of single-kernel-call closures, in order."""
+        """The pass as a list of library-call closures, in order (the mosaic,
+        then one per node of ``nodes()``)."""
         seq: List[Callable[[], None]] = []
         if self.canvas is not None:
             seq.append(lambda: _lib.mosaic_pack(self.x0, self.canvas, out_dtype=torch.bfloat16))
-        for i in range(len(self.convs)):
-            seq.append(lambda i=i: self.convs[i].run(self.layer_input(i), self.params[i]["w"], self.params[i]["b"],
-                                                     self.bufs[i]))
+        for node in self.nodes():
+            i = node[0]
+            if len(node) == 2:
+                seq.append(lambda i=i: _lib.run_fused(self.convs[i], self.convs[i + 1], self.layer_input(i),
+                                                      self.params[i]["w"], self.params[i]["b"],
+                                                      self.params[i + 1]["w"], self.params[i + 1]["b"],
+                                                      self.bufs[i + 1]))
+            else:
+                seq.append(lambda i=i: self.convs[i].run(self.layer_input(i), self.params[i]["w"],
+                                                         self.params[i]["b"], self.bufs[i]))
         return seq
+
+    def node_kernel(self, node) -> str:
+        """The kernel symbol a node launches."""
+        if len(node) == 2:
+            d = _lib.describe_fused(self.convs[node[0]], self.convs[node[1]])
+        else:
+            d = self.convs[node[0]].describe()
+        return d.split("kernel=")[-1]
 
     def step(self) -> torch.Tensor:
         for f in self.launches():

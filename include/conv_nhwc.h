@@ -115,8 +115,12 @@ typedef struct conv_desc {
                              k > 0 forces one kernel configuration of a
                              dense bf16/int8 layer (for tests and tuning):
                              1..4 the implicit-GEMM tiles, 5 up to
-                             conv_algo_count() the large-layer kernel's
-                             tiles (conv_describe names the one chosen). For a depthwise layer with stride 1 and
+                             conv_algo_count() - 1 the large-layer
+                             kernel's tiles, conv_algo_count() the
+                             weight-stationary kernel (reductions of at
+                             most 256 bytes per output; conv_describe
+                             names the one chosen). For a depthwise layer
+                             with stride 1 and
                              c_in % 4 == 0, k = 1..4 forces 1, 2, 4 or 8
                              output rows per lane of the row-window kernel.
                              A configuration that cannot run the layer gives
@@ -236,6 +240,29 @@ conv_status conv_pack_bfp8(const void* w, int32_t w_dtype, int64_t c_out, int64_
  * host threads on one stream without ordering) race on the array: order them. */
 conv_status conv_run_noalloc(const conv_desc* d, const void* x, const void* w, const void* b,
                              const void* r, void* y, void* stream);
+
+/* Two layers in one launch: p1's layer, then p2's 1x1 layer applied to each
+ * of p1's output tiles before anything is stored, so p1's output never goes
+ * to memory and the stack has one node less (YOLOv4 on Tenstorrent Wormhole,
+ * section 10, "Why reducing operation count matters": fewer graph operations
+ * and no intermediate write and read). y = layer2(layer1(x)) with layer1's
+ * output rounded to bf16 exactly as conv_run would store it; the result is
+ * the same as conv_run(p1) into a tensor t, then conv_run(p2) on t.
+ * Fusable pairs (conv_fuse_check): p1 bf16 -> bf16 on the implicit-GEMM
+ * kernel with the tap or vec16 gather, its reduction not split, 64 or 128
+ * output channels; p2 bf16 -> bf16, 1x1,
+ * stride 1, pad 0, groups 1, plain weights, on p1's output shape, at most 64
+ * output channels, a multiple of 4. No residual.
+ *   x, w1, b1 : as conv_run for p1; w2, b2 : as conv_run for p2;
+ *   y : p2's output, 16-byte aligned, overlapping none of the inputs.
+ * CONV_E_NULL, CONV_E_UNSUPPORTED (not a fusable pair), CONV_E_ALIGN,
+ * CONV_E_ALIAS, CONV_E_HIP. conv_fuse_check returns CONV_OK or
+ * CONV_E_UNSUPPORTED (CONV_E_NULL for a NULL plan). */
+conv_status conv_fuse_check(const conv_plan* p1, const conv_plan* p2);
+/* conv_describe for a fusable pair: the fused launch's kernel and shape. */
+conv_status conv_describe_fused(const conv_plan* p1, const conv_plan* p2, char* buf, int32_t len);
+conv_status conv_run_fused(const conv_plan* p1, const conv_plan* p2, const void* x, const void* w1,
+                           const void* b1, const void* w2, const void* b2, void* y, void* stream);
 
 /* Free a plan and the workspace conv_prepare allocated for it; all device
  * memory a plan holds is taken at preparation and given back here, none in

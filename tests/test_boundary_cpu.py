@@ -327,3 +327,64 @@ def test_python_binding_validates_tensors():
     with pytest.raises(ValueError):
         c.run(x, w)   # host tensors are refused before any library call
     c.close()
+
+
+def test_fuse_check_pairs():
+    """conv_fuse_check accepts a KxK bf16 layer with 64 or 128 output channels
+    followed by a 1x1 bf16 layer on its output with at most 64 channels (a
+    multiple of 4), and refuses everything else."""
+    def C(h, w, cin, cout, k, s=1, **kw):
+        return Conv2d(1, h, w, cin, cout, k, k, (s, s), (k // 2, k // 2), **dict(dict(dtype="bf16"), **kw))
+
+    ok = [(C(20, 20, 64, 64, 3), C(20, 20, 64, 64, 1)),
+          (C(20, 20, 64, 128, 3, s=2), C(10, 10, 128, 32, 1)),
+          (C(17, 9, 32, 64, 3), C(17, 9, 64, 4, 1)),
+          (C(12, 12, 128, 64, 5), C(12, 12, 64, 60, 1))]
+    bad = [(C(20, 20, 64, 96, 3), C(20, 20, 96, 64, 1)),            # 96 intermediate channels
+           (C(20, 20, 64, 64, 3), C(20, 20, 64, 128, 1)),           # 128 output channels
+           (C(20, 20, 64, 64, 3), C(20, 20, 64, 62, 1)),            # not a multiple of 4
+           (C(20, 20, 64, 64, 3), C(20, 20, 64, 64, 3)),            # second layer 3x3
+           (C(20, 20, 64, 64, 3), C(10, 10, 64, 64, 1, s=2)),       # wrong shape / stride
+           (C(20, 20, 64, 64, 3), C(20, 20, 64, 64, 1, act="none", dtype="f32")),
+           (C(20, 20, 3, 64, 3), C(20, 20, 64, 64, 1)),             # stem gather
+           (C(20, 20, 64, 64, 3, dtype="i8", out_dtype="i8"), C(20, 20, 64, 64, 1, dtype="i8", out_dtype="i8")),
+           (C(20, 20, 64, 64, 3, groups=64), C(20, 20, 64, 64, 1)),  # depthwise
+           (C(20, 20, 64, 64, 3, w_format="bfp8"), C(20, 20, 64, 64, 1)),
+           (C(20, 20, 64, 64, 3), C(20, 20, 64, 64, 1, w_format="bfp8"))]
+    for a, b in ok:
+        assert _lib.fusable(a, b), (a.describe(), b.describe())
+        d = _lib.describe_fused(a, b)
+        assert d.startswith("igemm fused_1x1 ") and d.endswith(", 0, 1>"), d
+    for a, b in bad:
+        assert not _lib.fusable(a, b), (a.describe(), b.describe())
+        with pytest.raises(ConvError):
+            _lib.describe_fused(a, b)
+    L = _lib.lib()
+    assert L.conv_fuse_check(None, ok[0][1]._plan) == -1
+    assert L.conv_fuse_check(ok[0][0]._plan, None) == -1
+    for a, b in ok + bad:
+        a.close()
+        b.close()
+
+
+def test_run_fused_pointer_checks_before_launch():
+    a = Conv2d(1, 8, 8, 64, 64, 3, 3, (1, 1), (1, 1), dtype="bf16")
+    b = Conv2d(1, 8, 8, 64, 64, 1, 1, (1, 1), (0, 0), dtype="bf16")
+    bad = Conv2d(1, 8, 8, 64, 128, 1, 1, (1, 1), (0, 0), dtype="bf16")
+    L = _lib.lib()
+    X, W1, B1, W2, B2, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000, 0x60000000
+    P1, P2 = a._plan, b._plan
+    assert L.conv_run_fused(None, P2, X, W1, B1, W2, B2, Y, None) == -1
+    assert L.conv_run_fused(P1, P2, None, W1, B1, W2, B2, Y, None) == -1
+    assert L.conv_run_fused(P1, P2, X, W1, B1, None, B2, Y, None) == -1
+    assert L.conv_run_fused(P1, P2, X, W1, B1, W2, B2, None, None) == -1
+    assert L.conv_run_fused(P1, bad._plan, X, W1, B1, W2, B2, Y, None) == -3
+    assert L.conv_run_fused(P1, P2, X + 8, W1, B1, W2, B2, Y, None) == -4
+    assert L.conv_run_fused(P1, P2, X, W1, B1, W2 + 4, B2, Y, None) == -4
+    assert L.conv_run_fused(P1, P2, X, W1, B1, W2, B2 + 2, Y, None) == -4
+    assert L.conv_run_fused(P1, P2, X, W1, B1, W2, B2, Y + 8, None) == -4
+    assert L.conv_run_fused(P1, P2, X, W1, B1, W2, B2, X + 1024, None) == -5  # y inside x
+    assert L.conv_run_fused(P1, P2, X, W1, B1, Y + 256, B2, Y, None) == -5    # w2 inside y
+    assert L.conv_run_fused(P1, P2, X, W1, Y + 64, W2, B2, Y, None) == -5     # b1 inside y
+    for c in (a, b, bad):
+        c.close()
