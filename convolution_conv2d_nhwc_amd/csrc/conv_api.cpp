@@ -285,6 +285,10 @@ conv_status build_plan(const conv_desc* d, conv_plan* p, void* scratch, int64_t 
     if (!xl_eligible(g, in_esz, loader, d->algo - kAlgoXl)) return CONV_E_UNSUPPORTED;
     path = PATH_XL;
   }
+  if (d->algo == kAlgoHalo) {
+    if (path != PATH_IGEMM || wq || !halo_eligible(*d, g)) return CONV_E_UNSUPPORTED;
+    path = PATH_HALO;
+  }
   if (path == PATH_IGEMM && d->algo == 0 && !wq) {
     const int xt = choose_xl(g, in_esz, loader);
     if (xt >= 0) {
@@ -292,6 +296,8 @@ conv_status build_plan(const conv_desc* d, conv_plan* p, void* scratch, int64_t 
       p->tile = xt;
     }
   }
+  // 3x3 bf16 layers over 32 or 64 channels where the halo kernel wins
+  if (path == PATH_IGEMM && d->algo == 0 && !wq && halo_preferred(*d, g)) path = PATH_HALO;
   // A reduction of at most 256 bytes on the 64x64 tile goes to the
   // weight-stationary kernel.
   if (path == PATH_IGEMM && ws_ok && (d->algo == kAlgoWs || (d->algo == 0 && choose_tile(g, in_esz) == 0)))
@@ -372,6 +378,7 @@ conv_status run_common(const conv_plan* p, const void* x, const void* w, const v
     case PATH_SMALLK: err = launch_smallk(p, x, w, e, y, s); break;
     case PATH_XL: err = launch_xl(p, x, w, e, y, s); break;
     case PATH_WS: err = launch_ws(p, x, w, e, y, s); break;
+    case PATH_HALO: err = launch_halo(p, x, w, e, y, s); break;
     default: err = launch_f32(p, x, w, e, y, s); break;
   }
   if (err != hipSuccess) {
@@ -434,14 +441,27 @@ namespace {
 bool fused_1x1_ok(const conv_plan* p1, const conv_plan* p2) {
   const conv_desc& a = p1->d;
   const conv_desc& b = p2->d;
-  if (a.dtype != CONV_BF16 || a.out_dtype != CONV_BF16 || p1->path != PATH_IGEMM || p1->wq || p1->ksplit != 1)
-    return false;
+  if (a.dtype != CONV_BF16 || a.out_dtype != CONV_BF16 || p1->wq || p1->ksplit != 1) return false;
+  if (p1->path != PATH_IGEMM && p1->path != PATH_HALO) return false;
+  if (p1->path == PATH_HALO && !halo_fusable(p1->d, p1->g)) return false;
   if (p1->loader != LOAD_TAP && p1->loader != LOAD_VEC) return false;
   if (p1->g.cout != 64 && p1->g.cout != 128) return false;
   if (b.dtype != CONV_BF16 || b.out_dtype != CONV_BF16 || b.groups != 1 || p2->wq) return false;
   if (b.kh != 1 || b.kw != 1 || b.stride_h != 1 || b.stride_w != 1 || b.pad_h != 0 || b.pad_w != 0) return false;
   if (b.n != a.n || b.h != p1->g.ho || b.w != p1->g.wo || b.c_in != p1->g.cout) return false;
   return p2->g.cout <= 64 && (p2->g.cout & 3) == 0;
+}
+
+}  // namespace
+
+namespace {
+
+// The fused launch runs on the halo kernel when the first layer does, or
+// when its kernel was left to the library and the halo kernel can fuse it
+// (it beats the implicit-GEMM fusion on every such pair measured); a first
+// layer forced onto an implicit-GEMM tile keeps that kernel.
+bool fused_on_halo(const conv_plan* p1) {
+  return p1->path == PATH_HALO || (p1->d.algo == 0 && halo_fusable(p1->d, p1->g));
 }
 
 }  // namespace
@@ -456,6 +476,14 @@ conv_status conv_describe_fused(const conv_plan* p1, const conv_plan* p2, char* 
   if (!fused_1x1_ok(p1, p2)) return CONV_E_UNSUPPORTED;
   static const char* kLoader[] = {"generic", "vec16", "1x1", "tap"};
   const int tco = p1->g.cout;
+  if (fused_on_halo(p1)) {
+    std::snprintf(buf, len,
+                  "halo fused_1x1 co%d patch=4x16 stride=%d cin=%d then 1x1 %d->%d wgs=%d m=%d k=%d "
+                  "kernel=halo_kernel<%d, %d, %d, 1>",
+                  tco, p1->g.sh, p1->g.c, tco, p2->g.cout, halo_grid(p1, tco), p1->g.m, p1->g.k, p1->g.sh,
+                  p1->g.c / 32, tco);
+    return CONV_OK;
+  }
   std::snprintf(buf, len,
                 "igemm fused_1x1 loader=%s co%dxpx64 then 1x1 %d->%d wgs=%d m=%d k=%d "
                 "kernel=igemm_kernel<2, %d, 64, 2, 2, %d, %d, 0, 1>",
@@ -481,7 +509,9 @@ conv_status conv_run_fused(const conv_plan* p1, const conv_plan* p2, const void*
   e1.act = p1->d.act;
   e2.bias = static_cast<const float*>(b2);
   e2.act = p2->d.act;
-  const hipError_t err = launch_igemm_fused(p1, p2, x, w1, e1, w2, e2, y, static_cast<hipStream_t>(stream));
+  const hipError_t err = fused_on_halo(p1)
+                             ? launch_halo_fused(p1, p2, x, w1, e1, w2, e2, y, static_cast<hipStream_t>(stream))
+                             : launch_igemm_fused(p1, p2, x, w1, e1, w2, e2, y, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) {
     std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(err));
     return CONV_E_HIP;
@@ -537,6 +567,11 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
                   "kernel=igemm_ws_kernel<%d, %d, %d>",
                   kDt[p->d.dtype], kDt[p->d.out_dtype], kLoader[p->loader], kAlgoWs, ws_grid_x(p),
                   (p->g.cout + 63) / 64, p->g.m, p->g.k, p->in_esz, p->loader, ws_ksteps(p->g, p->in_esz, p->loader));
+  } else if (p->path == PATH_HALO) {
+    std::snprintf(buf, len,
+                  "halo dtype=bf16 out=bf16 tile=%d co64 patch=4x16 stride=%d cin=%d wgs=%d m=%d k=%d "
+                  "kernel=halo_kernel<%d, %d, 64, 0>",
+                  kAlgoHalo, p->g.sh, p->g.c, halo_grid(p, 64), p->g.m, p->g.k, p->g.sh, p->g.c / 32);
   } else if (p->path == PATH_SMALLK) {
     int fco, ks;
     smallk_shape(p->g, p->in_esz, &fco, &ks);

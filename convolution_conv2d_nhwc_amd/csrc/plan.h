@@ -15,7 +15,8 @@ enum Path {
   PATH_F32 = 3,    // true-fp32 direct convolution, VALU
   PATH_SMALLK = 4, // MFMA, operands straight from global memory: short K, odd Cin
   PATH_XL = 6,     // MFMA, direct-to-LDS loads, software-pipelined
-  PATH_WS = 7      // MFMA, weights held in registers, short reductions
+  PATH_WS = 7,     // MFMA, weights held in registers, short reductions
+  PATH_HALO = 8    // MFMA, 3x3 over 32/64 channels: weights in registers, input windows in LDS
 };
 
 // How the implicit-GEMM kernel gathers its activation operand.
@@ -41,9 +42,11 @@ extern const TileCfg kTiles[kNumTiles];  // index = algo - 1
 // configuration i.
 constexpr int kNumXlTiles = 6;
 constexpr int kAlgoXl = kNumTiles + 1;
-// desc.algo kAlgoWs forces the weight-stationary kernel.
+// desc.algo kAlgoWs forces the weight-stationary kernel, kAlgoHalo the halo
+// kernel.
 constexpr int kAlgoWs = kAlgoXl + kNumXlTiles;
-constexpr int kAlgoLast = kAlgoWs;
+constexpr int kAlgoHalo = kAlgoWs + 1;
+constexpr int kAlgoLast = kAlgoHalo;
 extern const TileCfg kXlTiles[kNumXlTiles];
 
 struct Geometry {
@@ -89,6 +92,13 @@ hipError_t launch_igemm_fused(const conv_plan* p1, const conv_plan* p2, const vo
 int ws_ksteps(const Geometry& g, int esz, int loader);  // 0: not for the weight-stationary kernel
 int ws_grid_x(const conv_plan* p);
 hipError_t launch_ws(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);
+bool halo_eligible(const conv_desc& d, const Geometry& g);
+bool halo_preferred(const conv_desc& d, const Geometry& g);  // the automatic choice
+bool halo_fusable(const conv_desc& d, const Geometry& g);    // the fused launch can use the halo kernel
+int halo_grid(const conv_plan* p, int tco);  // workgroups of a launch with tco channels per workgroup
+hipError_t launch_halo(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);
+hipError_t launch_halo_fused(const conv_plan* p1, const conv_plan* p2, const void* x, const void* w1, const Epi& e1,
+                             const void* w2, const Epi& e2, void* y, hipStream_t s);
 hipError_t launch_smallk(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y,
                          hipStream_t s);
 void smallk_shape(const Geometry& g, int esz, int* fco, int* ks);

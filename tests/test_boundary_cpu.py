@@ -143,23 +143,38 @@ def test_out_shape_floor_rule_and_per_axis_pads():
 
 
 def test_forced_algo_and_count():
-    """Every algo id forces its own kernel configuration on a layer all of them
-    accept (1x1 over one 128-byte channel block, Cout = 256); the large-layer
-    kernel refuses a Cout that is not a multiple of its channel tile, the
-    weight-stationary kernel a reduction over 256 bytes."""
+    """Every algo id forces its own kernel configuration: all but the last on
+    a layer all of them accept (1x1 over one 128-byte channel block, Cout =
+    256), the last (the halo kernel) on a 3x3 layer over 64 channels. The
+    large-layer kernel refuses a Cout that is not a multiple of its channel
+    tile, the weight-stationary kernel a reduction over 256 bytes, the halo
+    kernel anything but a 3x3 bf16 layer over 32 or 64 channels at stride 1
+    or 2."""
     n = _lib.lib().conv_algo_count()
-    assert n >= 1
+    assert n >= 2
     kinds = set()
-    for a in range(1, n + 1):
+    for a in range(1, n):
         c = Conv2d(1, 20, 20, 64, 256, 1, 1, (1, 1), (0, 0), dtype="bf16", algo=a)
         d = c.describe()
         assert "tile=%d " % a in d
         kinds.add(d.split()[0])
         c.close()
     assert kinds == {"igemm", "igemm_xl", "igemm_ws"}
+    c = Conv2d(1, 20, 20, 64, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=n)
+    assert c.describe().startswith("halo ") and "tile=%d " % n in c.describe(), c.describe()
+    c.close()
+    ws = n - 1
     with pytest.raises(ConvError):
-        Conv2d(1, 20, 20, 64, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=n)  # 1152-byte reduction
-    xl = [a for a in range(1, n + 1)
+        Conv2d(1, 20, 20, 64, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=ws)  # 1152-byte reduction
+    for kw in (dict(cin=64, k=1), dict(cin=48, k=3), dict(cin=128, k=3), dict(cin=64, k=5), dict(cin=64, k=3, s=3),
+               dict(cin=64, k=3, dtype="i8", out_dtype="i8"), dict(cin=64, k=3, w_format="bfp8"),
+               dict(cin=64, k=3, cout=62)):
+        a = dict(kw)
+        cin, k, s = a.pop("cin"), a.pop("k"), a.pop("s", 1)
+        cout = a.pop("cout", 64)
+        with pytest.raises(ConvError):
+            Conv2d(1, 20, 20, cin, cout, k, k, (s, s), (k // 2, k // 2), **dict(dict(dtype="bf16"), **a), algo=n)
+    xl = [a for a in range(1, n)
           if Conv2d(1, 20, 20, 64, 256, 1, 1, (1, 1), (0, 0), dtype="bf16", algo=a).describe().startswith("igemm_xl")]
     for a in xl:
         with pytest.raises(ConvError):
@@ -329,6 +344,16 @@ def test_python_binding_validates_tensors():
     c.close()
 
 
+def _shape(c):
+    return " %dx%d" % (c.w_shape[1], c.w_shape[2])
+
+
+def _halo_fusable(c):
+    cout, kh, kw, cin = c.w_shape
+    stride = 2 if c.out_shape[1] * 2 <= c.in_shape[1] else 1
+    return kh == kw == 3 and cin in (32, 64) and cout in (64, 128) and not (cout == 64 and stride == 2 and cin == 64)
+
+
 def test_fuse_check_pairs():
     """conv_fuse_check accepts a KxK bf16 layer with 64 or 128 output channels
     followed by a 1x1 bf16 layer on its output with at most 64 channels (a
@@ -354,7 +379,15 @@ def test_fuse_check_pairs():
     for a, b in ok:
         assert _lib.fusable(a, b), (a.describe(), b.describe())
         d = _lib.describe_fused(a, b)
-        assert d.startswith("igemm fused_1x1 ") and d.endswith(", 0, 1>"), d
+        # 3x3 first layers over 32 / 64 channels fuse on the halo kernel
+        # (except 64 -> 64 at stride 2), the rest on the implicit GEMM
+        assert d.startswith("halo fused_1x1 " if " 3x3" in _shape(a) and _halo_fusable(a) else "igemm fused_1x1 "), d
+        assert d.endswith(", 1>"), d
+    # a first layer forced onto an implicit-GEMM tile keeps that kernel
+    a, b = C(20, 20, 64, 64, 3, algo=1), C(20, 20, 64, 64, 1)
+    assert _lib.describe_fused(a, b).startswith("igemm fused_1x1 ")
+    a.close()
+    b.close()
     for a, b in bad:
         assert not _lib.fusable(a, b), (a.describe(), b.describe())
         with pytest.raises(ConvError):

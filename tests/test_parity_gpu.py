@@ -21,16 +21,27 @@ ALGO_COUNT = _lib.lib().conv_algo_count()
 
 
 def _algo_describe(algo):
-    # a layer every forced algorithm accepts: 1x1 over one 128-byte channel
-    # block (a 128-byte reduction), Cout = 256
-    return _lib.Conv2d(1, 20, 20, 64, 256, 1, 1, (1, 1), (0, 0), dtype="bf16", algo=algo).describe()
+    # a layer every forced algorithm but the halo kernel accepts: 1x1 over one
+    # 128-byte channel block (a 128-byte reduction), Cout = 256; the halo
+    # kernel's is a 3x3 layer over 64 channels
+    try:
+        return _lib.Conv2d(1, 20, 20, 64, 256, 1, 1, (1, 1), (0, 0), dtype="bf16", algo=algo).describe()
+    except _lib.ConvError:
+        return _lib.Conv2d(1, 20, 20, 64, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", algo=algo).describe()
 
 
 ALGO_DESC = {a: _algo_describe(a) for a in range(1, ALGO_COUNT + 1)}
 TILE_ALGOS = [a for a, d in ALGO_DESC.items() if d.startswith("igemm ")]
 XL_ALGOS = [a for a, d in ALGO_DESC.items() if d.startswith("igemm_xl ")]
 WS_ALGOS = [a for a, d in ALGO_DESC.items() if d.startswith("igemm_ws ")]
-assert len(TILE_ALGOS) + len(XL_ALGOS) + len(WS_ALGOS) == ALGO_COUNT and WS_ALGOS
+HALO_ALGOS = [a for a, d in ALGO_DESC.items() if d.startswith("halo ")]
+assert len(TILE_ALGOS) + len(XL_ALGOS) + len(WS_ALGOS) + len(HALO_ALGOS) == ALGO_COUNT and WS_ALGOS and HALO_ALGOS
+
+
+def halo_accepts(layer):
+    return (layer.dtype == "bf16" and layer.groups == 1 and layer.kh == 3 and layer.kw == 3 and layer.sh == layer.sw
+            and layer.sh in (1, 2) and layer.cin in (32, 64) and layer.ph <= 2 and layer.pw <= 2
+            and layer.cout % 4 == 0)
 
 # Tiles wider than 256 rows on either side need a 16-byte-vector loader; the
 # element-wise gather refuses them at prepare time.
@@ -44,7 +55,7 @@ def forced_tiles(layer):
     the weight-stationary kernel refuses element-wise gathers and reductions
     over 256 bytes."""
     out = []
-    for a in TILE_ALGOS + XL_ALGOS + WS_ALGOS:
+    for a in TILE_ALGOS + XL_ALGOS + WS_ALGOS + HALO_ALGOS:
         try:
             _lib.Conv2d.from_layer(layer, algo=a).close()
             out.append(a)
@@ -56,6 +67,8 @@ def forced_tiles(layer):
                 assert "loader=generic" in d or "smallk" in d, (layer.name, a, d)
             elif a in WS_ALGOS:
                 assert cbytes % 16 or layer.kh * layer.kw * cbytes > 256 or layer.groups > 1, (layer.name, a, d)
+            elif a in HALO_ALGOS:
+                assert not halo_accepts(layer), (layer.name, a, d)
             else:
                 assert a in XL_ALGOS, (layer.name, a, d)
                 tco = int(re.search(r"co(\d+)x", ALGO_DESC[a]).group(1))
