@@ -115,11 +115,14 @@ typedef struct conv_desc {
                              k > 0 forces one kernel configuration of a
                              dense bf16/int8 layer (for tests and tuning):
                              1..4 the implicit-GEMM tiles, 5 up to
-                             conv_algo_count() - 1 the large-layer
-                             kernel's tiles, conv_algo_count() the
+                             conv_algo_count() - 2 the large-layer
+                             kernel's tiles, conv_algo_count() - 1 the
                              weight-stationary kernel (reductions of at
-                             most 256 bytes per output; conv_describe
-                             names the one chosen). For a depthwise layer
+                             most 256 bytes per output),
+                             conv_algo_count() the halo kernel (3x3 bf16
+                             over 32 or 64 input channels, stride 1 or 2,
+                             pad <= 2, c_out % 4 == 0); conv_describe
+                             names the one chosen. For a depthwise layer
                              with stride 1 and
                              c_in % 4 == 0, k = 1..4 forces 1, 2, 4 or 8
                              output rows per lane of the row-window kernel.
@@ -249,12 +252,16 @@ conv_status conv_run_noalloc(const conv_desc* d, const void* x, const void* w, c
  * output rounded to bf16 exactly as conv_run would store it; the result is
  * the same as conv_run(p1) into a tensor t, then conv_run(p2) on t.
  * Fusable pairs (conv_fuse_check): p1 bf16 -> bf16 on the implicit-GEMM
- * kernel with the tap or vec16 gather, its reduction not split, 64 or 128
- * output channels; p2 bf16 -> bf16, 1x1,
+ * or the halo kernel with the tap or vec16 gather, its reduction not split,
+ * 64 or 128 output channels; p2 bf16 -> bf16, 1x1,
  * stride 1, pad 0, groups 1, plain weights, on p1's output shape, at most 64
  * output channels, a multiple of 4. No residual.
  *   x, w1, b1 : as conv_run for p1; w2, b2 : as conv_run for p2;
  *   y : p2's output, 16-byte aligned, overlapping none of the inputs.
+ * The launch runs on the halo kernel when p1 does or when p1's kernel was
+ * left to the library and the halo kernel can fuse it (3x3 over 32 or 64
+ * input channels, except 64 -> 64 channels at stride 2 over 64), else on
+ * the implicit-GEMM kernel; conv_describe_fused names it.
  * CONV_E_NULL, CONV_E_UNSUPPORTED (not a fusable pair), CONV_E_ALIGN,
  * CONV_E_ALIAS, CONV_E_HIP. conv_fuse_check returns CONV_OK or
  * CONV_E_UNSUPPORTED (CONV_E_NULL for a NULL plan). */
