@@ -161,8 +161,10 @@ def main():
     j = 0
     if canvas is not None:
         m, th, tw, c = wl.mosaic
-        mb = 4 * m * th * tw * c * 4 + m * 4 * th * tw * c * 2
-        layers.append({"name": "mosaic_pack", "kernel": "mosaic_vec8_kernel", "us": dur_us[0],
+        # fp32 tiles read, the bf16 canvas written (padded to 8 channels for
+        # the window stem kernel)
+        mb = 4 * m * th * tw * c * 4 + m * 4 * th * tw * stack.canvas_c * 2
+        layers.append({"name": "mosaic_pack", "kernel": stack.mosaic_kernel(), "us": dur_us[0],
                        "gflop": 0.0, "mbytes": mb / 1e6, "bound": "hbm",
                        "frac": (mb / (HBM_GBS * 1e9)) / (dur_us[0] * 1e-6)})
         j = 1
@@ -342,7 +344,7 @@ def stack_measurements():
         durs, _ = per_launch_us(seq)
         names = (["mosaic_pack"] if st.canvas is not None else []) + [
             "+".join(wl.layers[i].name for i in n) for n in st.nodes()]
-        kern = (["mosaic_vec8_kernel"] if st.canvas is not None else []) + [st.node_kernel(n) for n in st.nodes()]
+        kern = ([st.mosaic_kernel()] if st.canvas is not None else []) + [st.node_kernel(n) for n in st.nodes()]
         row = {"us_per_stack_median": round(med, 2), "us_per_stack_back_to_back": round(thr, 2),
                "replays": 200, "warmup": 20, "nodes": len(seq),
                "gflop": round(wl.flops() / 1e9, 5),

@@ -40,7 +40,7 @@ class _Desc(ctypes.Structure):
                 ("pad_h", ctypes.c_int32), ("pad_w", ctypes.c_int32),
                 ("groups", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("act", ctypes.c_int32),
-                ("algo", ctypes.c_int32), ("w_format", ctypes.c_int32)]
+                ("algo", ctypes.c_int32), ("w_format", ctypes.c_int32), ("x_pixel_stride", ctypes.c_int32)]
 
 
 W_FORMATS = {"plain": 0, "bfp8": 1}
@@ -144,29 +144,30 @@ class Conv2d:
     def __init__(self, n: int, h: int, w: int, c_in: int, c_out: int, kh: int, kw: int,
                  stride: Sequence[int] = (1, 1), pad: Sequence[int] = (0, 0), groups: int = 1,
                  dtype: str = "bf16", out_dtype: Optional[str] = None, act: str = "none",
-                 algo: int = 0, w_format: str = "plain"):
+                 algo: int = 0, w_format: str = "plain", x_stride: int = 0):
         out_dtype = out_dtype or dtype
         self.dtype, self.out_dtype, self.act = dtype, out_dtype, act
         self.groups = groups
         self.w_format = w_format
         d = _Desc(n, h, w, c_in, c_out, kh, kw, stride[0], stride[1], pad[0], pad[1], groups,
-                  DTYPES[dtype], DTYPES[out_dtype], ACTS[act], algo, W_FORMATS[w_format])
+                  DTYPES[dtype], DTYPES[out_dtype], ACTS[act], algo, W_FORMATS[w_format], x_stride)
         self._desc = d
         self._plan = ctypes.c_void_p()
         _check(lib().conv_prepare(ctypes.byref(d), ctypes.byref(self._plan)), "conv_prepare")
         shp = (ctypes.c_int64 * 4)()
         _check(lib().conv_out_shape(self._plan, shp), "conv_out_shape")
         self.out_shape = tuple(int(v) for v in shp)
-        self.in_shape = (n, h, w, c_in)
+        # x_stride: elements per input pixel (channels past c_in ignored)
+        self.in_shape = (n, h, w, x_stride or c_in)
         self.w_shape = (c_out, kh, kw, c_in // groups)
         if w_format == "bfp8":
             self.w_shape = (int(lib().conv_bfp8_bytes(c_out, kh * kw * (c_in // groups))),)
 
     @classmethod
-    def from_layer(cls, layer, algo: int = 0, w_format: str = "plain") -> "Conv2d":
+    def from_layer(cls, layer, algo: int = 0, w_format: str = "plain", x_stride: int = 0) -> "Conv2d":
         return cls(layer.n, layer.h, layer.w, layer.cin, layer.cout, layer.kh, layer.kw,
                    (layer.sh, layer.sw), (layer.ph, layer.pw), layer.groups, layer.dtype,
-                   layer.out, layer.act, algo, w_format)
+                   layer.out, layer.act, algo, w_format, x_stride)
 
     def _w_dtype(self):
         return torch.uint8 if self.w_format == "bfp8" else TORCH_DT[self.dtype]

@@ -193,7 +193,10 @@ conv_status build_plan(const conv_desc* d, conv_plan* p, void* scratch, int64_t 
 
   const int in_esz = esz_of(dt), out_esz = esz_of(ot);
   const int64_t cg = d->c_in / d->groups;
-  const int64_t x_bytes = d->n * d->h * d->w * d->c_in * in_esz;
+  // elements from one input pixel to the next
+  const int64_t xs = d->x_pixel_stride == 0 ? d->c_in : d->x_pixel_stride;
+  if (xs < d->c_in) return CONV_E_SHAPE;
+  const int64_t x_bytes = d->n * d->h * d->w * xs * in_esz;
   // bfp8 weights: int8 mantissas [c_out][Kp] and one exponent byte per 16
   const bool wq = d->w_format == CONV_W_BFP8;
   if (d->w_format != CONV_W_PLAIN && !wq) return CONV_E_UNSUPPORTED;
@@ -296,6 +299,12 @@ conv_status build_plan(const conv_desc* d, conv_plan* p, void* scratch, int64_t 
       p->tile = xt;
     }
   }
+  // 16-byte (8-channel) input pixels: the window stem kernel, the only one
+  // that takes a pixel stride (and the best one for such layers)
+  if (xs == 8 && stem_eligible(*d, g, xs) && !wq && d->algo == 0 && (path == PATH_IGEMM || path == PATH_SMALLK))
+    path = PATH_STEM;
+  else if (xs != d->c_in)
+    return CONV_E_UNSUPPORTED;
   // 3x3 bf16 layers over 32 or 64 channels where the halo kernel wins
   if (path == PATH_IGEMM && d->algo == 0 && !wq && halo_preferred(*d, g)) path = PATH_HALO;
   // A reduction of at most 256 bytes on the 64x64 tile goes to the
@@ -379,6 +388,7 @@ conv_status run_common(const conv_plan* p, const void* x, const void* w, const v
     case PATH_XL: err = launch_xl(p, x, w, e, y, s); break;
     case PATH_WS: err = launch_ws(p, x, w, e, y, s); break;
     case PATH_HALO: err = launch_halo(p, x, w, e, y, s); break;
+    case PATH_STEM: err = launch_stem(p, x, w, e, y, s); break;
     default: err = launch_f32(p, x, w, e, y, s); break;
   }
   if (err != hipSuccess) {
@@ -572,6 +582,11 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
                   "halo dtype=bf16 out=bf16 tile=%d co64 patch=4x16 stride=%d cin=%d wgs=%d m=%d k=%d "
                   "kernel=halo_kernel<%d, %d, 64, 0>",
                   kAlgoHalo, p->g.sh, p->g.c, halo_grid(p, 64), p->g.m, p->g.k, p->g.sh, p->g.c / 32);
+  } else if (p->path == PATH_STEM) {
+    std::snprintf(buf, len,
+                  "stem_window dtype=bf16 out=bf16 cin=%d x_stride=%d patch=4x64 co32 wgs=%d m=%d k=%d "
+                  "kernel=stem_window_kernel",
+                  p->g.c, (int)(p->x_bytes / ((int64_t)p->g.n * p->g.h * p->g.w * 2)), stem_grid(p), p->g.m, p->g.k);
   } else if (p->path == PATH_SMALLK) {
     int fco, ks;
     smallk_shape(p->g, p->in_esz, &fco, &ks);

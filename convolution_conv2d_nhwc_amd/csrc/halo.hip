@@ -85,25 +85,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
 }
 
-// bf16(act(v + bias) [+ residual]) of channels co..co+3 of output pixel px
-// (px == o.m: outside the image, nothing is read), packed for one store.
-template <int ACT>
-__device__ __forceinline__ u32x2 pack_quad(const f32x4& v, const QuadConsts& q, int co, int px, const OutRef& o) {
-  float f[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) f[r] = act_t<ACT>(v[r] + q.bsf[r]);
-  if (o.has_res) {
-    const bool in = px < o.m && co < o.cout;
-    const u32x2 rv = __builtin_amdgcn_raw_buffer_load_b64(o.rr, in ? (uint32_t)(px * o.cout + co) * 2u : kOOB, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) f[r] += bf16_bits_to_f32((r & 1) ? (rv[r >> 1] >> 16) : (rv[r >> 1] & 0xffffu));
-  }
-  uint32_t h[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_bits(f[r]);
-  return u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-}
-
 __device__ __forceinline__ void store_packed(const u32x2& d, int co, int px, const OutRef& o) {
   const bool in = px < o.m && co < o.cout;
   __builtin_amdgcn_raw_buffer_store_b64(d, o.r, in ? (uint32_t)(px * o.cout + co) * 2u : kOOB, 0, 0);
@@ -342,7 +323,7 @@ __global__ __launch_bounds__(TCO * 4) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int i = 0; i < 2; ++i) {
           const int co = co0 + 32 * cg + 16 * i + 4 * (lane >> 4);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) d[i][j] = pack_quad<ACT>(acc[i][j], qc1[i], co, pxs[j], o);
+          for (int j = 0; j < 2; ++j) d[i][j] = pack_quad_bf16<ACT>(acc[i][j], qc1[i], co, pxs[j], o);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next window has landed
 #pragma unroll
@@ -419,7 +400,7 @@ __global__ __launch_bounds__(TCO * 4) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int i = 0; i < 2; ++i) {
           const int c2 = 32 * (wave & 1) + 16 * i + 4 * (lane >> 4);
 #pragma unroll
-          for (int j = 0; j < FP2; ++j) d[i][j] = pack_quad<ACT>(acc2[i][j], qc2[i], c2, pxs[j], o);
+          for (int j = 0; j < FP2; ++j) d[i][j] = pack_quad_bf16<ACT>(acc2[i][j], qc2[i], c2, pxs[j], o);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next window has landed
 #pragma unroll

@@ -193,6 +193,27 @@ __device__ __forceinline__ QuadConsts load_quad_consts_t(const Epi& e, int co, i
   return q;
 }
 
+// bf16(act(v + bias) [+ residual]) of channels co..co+3 of pixel px, packed
+// as one 8-byte quad (the residual quad is read only when px < m and
+// co < cout), for kernels that store through LDS or delay their stores.
+template <int ACT>
+__device__ __forceinline__ u32x2 pack_quad_bf16(const f32x4& v, const QuadConsts& q, int co, int px, const OutRef& o) {
+  float f[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) f[r] = act_t<ACT>(v[r] + q.bsf[r]);
+  if (o.has_res) {
+    const bool in = px < o.m && co < o.cout;
+    const u32x2 rv =
+        __builtin_amdgcn_raw_buffer_load_b64(o.rr, in ? (uint32_t)(px * o.cout + co) * 2u : 0x80000000u, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[r] += bf16_bits_to_f32((r & 1) ? (rv[r >> 1] >> 16) : (rv[r >> 1] & 0xffffu));
+  }
+  uint32_t h[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_bits(f[r]);
+  return u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+}
+
 // Store quad v (channels co..co+3 of pixel px); nothing is written when
 // px >= m or co >= cout. Requires cout % 4 == 0.
 template <int ESZ, int OUT, int ACT, typename acc_t>

@@ -6,7 +6,9 @@
 // Every canvas row is two contiguous half-rows, each a copy of one tile row.
 // When no channel padding is requested (c_pad == c) and a half-row holds a
 // multiple of 8 values, each lane converts 8 consecutive values with 16- and
-// 32-byte vector accesses; otherwise one lane writes one canvas pixel.
+// 32-byte vector accesses. A bf16 canvas padded to 8 channels (16 bytes per
+// pixel, the input of the window stem kernel) gets one 16-byte store per
+// pixel; otherwise one lane writes one canvas pixel value by value.
 #include "device_common.h"
 #include "plan.h"
 
@@ -95,6 +97,26 @@ __global__ __launch_bounds__(256) void mosaic_vec8_kernel(MosArgs a) {
   }
 }
 
+// One lane per canvas pixel of a bf16 canvas with c_pad == 8 (c <= 8): the
+// pixel's c values, zero-filled to 8, as one 16-byte store.
+__global__ __launch_bounds__(256) void mosaic_px16_kernel(MosArgs a) {
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.total) return;
+  const int cw = 2 * a.tw, chh = 2 * a.th;
+  const int x = (int)(t % cw);
+  long r = t / cw;
+  const int y = (int)(r % chh);
+  const int i = (int)(r / chh);
+  const int quad = 2 * (y >= a.th) + (x >= a.tw);
+  const int ty = y >= a.th ? y - a.th : y;
+  const int tx = x >= a.tw ? x - a.tw : x;
+  const long src = (((long)(4 * i + quad) * a.th + ty) * a.tw + tx) * a.c;
+  uint32_t wd[4] = {0, 0, 0, 0};
+  for (int ch = 0; ch < a.c; ++ch)
+    wd[ch >> 1] |= (uint32_t)f32_to_bf16_bits(load_in(a.tiles, src + ch, a.in_f32)) << (16 * (ch & 1));
+  *reinterpret_cast<i32x4*>(a.canvas + t * 16) = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+}
+
 }  // namespace
 
 hipError_t launch_mosaic(const void* tiles, int in_f32, void* canvas, int out_f32, int m, int th,
@@ -109,7 +131,11 @@ hipError_t launch_mosaic(const void* tiles, int in_f32, void* canvas, int out_f3
   a.tw = tw;
   a.c = c;
   a.c_pad = c_pad;
-  if (c_pad == c && ((long)tw * c) % 8 == 0) {
+  if (!out_f32 && c_pad == 8) {
+    a.total = (long)m * 2 * th * 2 * tw;
+    const long blocks = (a.total + 255) / 256;
+    hipLaunchKernelGGL(mosaic_px16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  } else if (c_pad == c && ((long)tw * c) % 8 == 0) {
     a.total = (long)m * 2 * th * 2 * ((long)tw * c / 8);
     const long blocks = (a.total + 255) / 256;
     hipLaunchKernelGGL(mosaic_vec8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);

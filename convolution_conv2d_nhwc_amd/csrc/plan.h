@@ -16,7 +16,8 @@ enum Path {
   PATH_SMALLK = 4, // MFMA, operands straight from global memory: short K, odd Cin
   PATH_XL = 6,     // MFMA, direct-to-LDS loads, software-pipelined
   PATH_WS = 7,     // MFMA, weights held in registers, short reductions
-  PATH_HALO = 8    // MFMA, 3x3 over 32/64 channels: weights in registers, input windows in LDS
+  PATH_HALO = 8,   // MFMA, 3x3 over 32/64 channels: weights in registers, input windows in LDS
+  PATH_STEM = 9    // MFMA, 3x3 stride-1 first layer on 16-byte (8-channel) pixels, windows in LDS
 };
 
 // How the implicit-GEMM kernel gathers its activation operand.
@@ -92,6 +93,9 @@ hipError_t launch_igemm_fused(const conv_plan* p1, const conv_plan* p2, const vo
 int ws_ksteps(const Geometry& g, int esz, int loader);  // 0: not for the weight-stationary kernel
 int ws_grid_x(const conv_plan* p);
 hipError_t launch_ws(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);
+bool stem_eligible(const conv_desc& d, const Geometry& g, int64_t x_stride);
+int stem_grid(const conv_plan* p);  // workgroups per 32 output channels
+hipError_t launch_stem(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);
 bool halo_eligible(const conv_desc& d, const Geometry& g);
 bool halo_preferred(const conv_desc& d, const Geometry& g);  // the automatic choice
 bool halo_fusable(const conv_desc& d, const Geometry& g);    // the fused launch can use the halo kernel

@@ -1,0 +1,210 @@
+// stem.hip -- the first convolution of a bf16 network on an input whose
+// pixels are padded to 8 channels (16 bytes): 3x3, stride 1, at most 8 real
+// input channels (the 640x640 mosaic canvas: 3 colour channels, padded by
+// the mosaic packer), fused bias + activation (+ residual) epilogue.
+//
+// The small-K kernel (smallk.hip) gathers every tap of every pixel from
+// global memory with per-element address arithmetic; on the 640x640 stem
+// that arithmetic, not the bytes, sets its time. With 16-byte pixels a
+// workgroup instead copies its output patch's input window (6 x 66 pixels
+// for 4 x 64 outputs) straight into LDS (`buffer_load ... lds`, one 16-byte
+// pixel per lane, whole rows per instruction), and each MFMA B fragment is
+// 16 lanes reading 16 consecutive window pixels at one tap: K = 9 taps x 8
+// channel slots, in three K-steps of four taps (tap slots 10 to 12 and the
+// channels past c_in are masked to zero, so whatever the pad channels hold
+// never reaches a sum). Each lane loads its six A fragments (the weights of
+// the workgroup's 32 output channels) once.
+//
+//   * workgroup: 4 waves, output patch of 4 rows x 64 columns; wave w owns
+//     row w: 4 fragments of 16 pixels x 2 of 16 channels (v_mfma_f32_16x16x32_bf16,
+//     A = weights, rows = channels; B = pixels, as in igemm.hip);
+//   * two patches per workgroup, both windows copied at once (800
+//     workgroups for the 640x640 stem: at the kernel's four waves per SIMD
+//     all are resident in one round); the time left is the epilogue (Mish
+//     on 32 outputs per lane per patch) and the 64-byte output pixels.
+#include "igemm_common.h"
+
+namespace convnhwc {
+
+namespace {
+
+constexpr int kSR = 4, kSC = 64;                 // output patch
+constexpr int kWR = kSR + 2, kWC = kSC + 2;      // input window (3x3, stride 1)
+constexpr int kWinPx = kWR * kWC;                // 396 pixels
+constexpr int kWinGroups = (kWinPx + 63) / 64;   // 1 KiB copies: 7
+constexpr int kStemTco = 32;                     // output channels per workgroup
+constexpr int kStemPatches = 2;                  // patches per workgroup
+
+struct StemArgs {
+  const char* x;
+  const char* w;
+  void* y;
+  Epi e;
+  Geometry g;
+  int x_bytes;
+  int w_bytes;
+  int npr, npc;  // patches per image: rows, columns
+  int npatch;    // n * npr * npc
+};
+
+__device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256) void stem_window_kernel(StemArgs a) {
+  __shared__ __attribute__((aligned(1024))) char win[kStemPatches][kWinGroups * 1024];
+
+  const Geometry g = a.g;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int per_img = a.npr * a.npc;
+  const int co0 = blockIdx.y * kStemTco;
+  // patch kStemPatches * blockIdx.x + t: image n, output rows r0 .., columns c0 ..
+  auto origin = [&](int p, int& n, int& r0, int& c0) {
+    n = p / per_img;
+    const int rem = p - n * per_img;
+    const int rb = rem / a.npc;
+    r0 = rb * kSR;
+    c0 = (rem - rb * a.npc) * kSC;
+  };
+
+  // the windows: group k (wave k and wave k + 4) covers window pixels 64 k ..
+  // 64 k + 63, lane l pixel 64 k + l (rows of kWC pixels); both patches'
+  // windows are copied at once
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, a.x_bytes);
+#pragma unroll
+  for (int t = 0; t < kStemPatches; ++t) {
+    const int p = kStemPatches * blockIdx.x + t;
+    if (p >= a.npatch) break;
+    int n, r0, c0;
+    origin(p, n, r0, c0);
+    const int hi0 = r0 - g.ph, wi0 = c0 - g.pw;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int k = wave + 4 * i;
+      if (k < kWinGroups) {
+        const int q = 64 * k + lane;
+        const int hr = q / kWC, hc = q - hr * kWC;
+        const int hi = hi0 + hr, wi = wi0 + hc;
+        const bool ok = q < kWinPx && (unsigned)hi < (unsigned)g.h && (unsigned)wi < (unsigned)g.w;
+        dma16_lds(rx, win[t] + k * 1024, ok ? (uint32_t)(((n * g.h + hi) * g.w + wi) * 16) : kOOB);
+      }
+    }
+  }
+  // A fragments: wa[ks][i] = channel row co0 + 16 i + (lane & 15), tap
+  // 4 ks + (lane >> 4), its 8 channel slots (zero past c_in and past tap 8),
+  // element by element from the OHWI weights (a tap's c_in values need not
+  // be 4-byte aligned); the loop over slots stops at c_in (uniform)
+  const int q = lane >> 4;
+  i32x4 wa[3][2];
+  {
+    const __amdgpu_buffer_rsrc_t rw = rsrc(a.w, a.w_bytes);
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int tap = 4 * ks + q;
+        const int co = co0 + 16 * i + (lane & 15);
+        const bool ok = tap < 9 && co < g.cout;
+        const uint32_t base = (uint32_t)((co * 9 + tap) * g.c) * 2;
+        uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int ci = 0; ci < 8; ++ci)
+          if (ci < g.c) h[ci] = bload_elem<2>(rw, ok ? base + 2 * ci : kOOB);
+        wa[ks][i] = i32x4{(int)(h[0] | (h[1] << 16)), (int)(h[2] | (h[3] << 16)), (int)(h[4] | (h[5] << 16)),
+                          (int)(h[6] | (h[7] << 16))};
+      }
+  }
+  // B masks: the channel slots c_in .. 7 of an input pixel read as zero
+  uint32_t bmask[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    bmask[d] = (2 * d < g.c ? 0xffffu : 0u) | (2 * d + 1 < g.c ? 0xffff0000u : 0u);
+  const QuadConsts qc0 = load_quad_consts_t<2>(a.e, co0 + 4 * q, g.cout);
+  const QuadConsts qc1 = load_quad_consts_t<2>(a.e, co0 + 16 + 4 * q, g.cout);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // B: lane (q, p = lane & 15) of fragment j reads window pixel (wave + kh,
+  // 16 j + p + kw) for its tap (taps past the ninth read tap 8's pixel and
+  // are masked to zero)
+  typedef f32x4 acc_t;
+  const int pbase = (wave * kWC + (lane & 15)) * 16;
+  const OutRef o = out_ref(a.y, g.m, g.cout, 2, a.e.res);
+  for (int t = 0; t < kStemPatches; ++t) {
+  const int p = kStemPatches * blockIdx.x + t;
+  if (p >= a.npatch) break;
+  int n, r0, c0;
+  origin(p, n, r0, c0);
+  acc_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < 3; ++ks) {
+    const int tap = min(4 * ks + q, 8);
+    const int kh = tap / 3, kw = tap - 3 * (tap / 3);
+    const int off = pbase + (kh * kWC + kw) * 16;
+    const bool live = 4 * ks + q < 9;
+    i32x4 bf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const i32x4 r = *reinterpret_cast<const i32x4*>(win[t] + off + j * 256);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) bf[j][d] = live ? (int)((uint32_t)r[d] & bmask[d]) : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<2>::run(wa[ks][i], bf[j], acc[i][j]);
+  }
+
+  // epilogue: channels co0 + 16 i + 4 (lane >> 4) .. +3 of pixel (r0 + wave,
+  // c0 + 16 j + (lane & 15)). (Restaging the tile through LDS so that every
+  // store is a 16-byte piece of a 1 KiB run measured no faster.)
+  const int r = r0 + wave;
+  with_epilogue<2>(OUT_BF16, a.e.act, [&](auto oc, auto ac) {
+    constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + 16 * j + (lane & 15);
+      const int px = (r < g.ho && c < g.wo) ? (n * g.ho + r) * g.wo + c : g.m;
+      store_quad_t<2, OUT, ACT>(acc[0][j], qc0, co0 + 4 * q, px, o);
+      store_quad_t<2, OUT, ACT>(acc[1][j], qc1, co0 + 16 + 4 * q, px, o);
+    }
+  });
+  }
+}
+
+}  // namespace
+
+bool stem_eligible(const conv_desc& d, const Geometry& g, int64_t x_stride) {
+  return d.dtype == CONV_BF16 && d.out_dtype == CONV_BF16 && d.groups == 1 && g.kh == 3 && g.kw == 3 && g.sh == 1 &&
+         g.sw == 1 && g.c <= 8 && x_stride == 8 && g.ph <= 1 && g.pw <= 1 && (g.cout & 3) == 0;
+}
+
+int stem_grid(const conv_plan* p) {
+  const int npatch = p->g.n * ((p->g.ho + kSR - 1) / kSR) * ((p->g.wo + kSC - 1) / kSC);
+  return (npatch + kStemPatches - 1) / kStemPatches;
+}
+
+hipError_t launch_stem(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s) {
+  StemArgs a;
+  a.x = static_cast<const char*>(x);
+  a.w = static_cast<const char*>(w);
+  a.y = y;
+  a.e = e;
+  a.g = p->g;
+  a.x_bytes = (int)p->x_bytes;
+  a.w_bytes = (int)p->w_bytes;
+  a.npr = (p->g.ho + kSR - 1) / kSR;
+  a.npc = (p->g.wo + kSC - 1) / kSC;
+  a.npatch = p->g.n * a.npr * a.npc;
+  const dim3 grid(stem_grid(p), (p->g.cout + kStemTco - 1) / kStemTco);
+  hipLaunchKernelGGL(stem_window_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace convnhwc

@@ -30,18 +30,35 @@ class Stack:
     With ``fuse``, a layer followed by a 1x1 layer that the library can run
     in the same launch (``conv_run_fused``: the first layer's output tile
     goes through the 1x1 layer before anything is stored) is launched as one
-    node; the first layer's output buffer is then never written."""
+    node; the first layer's output buffer is then never written.
 
-    def __init__(self, wl: Workload, seed: int = 0, device: str = "cuda", fuse: bool = False):
+    With ``pad_canvas`` (a stack with a mosaic), the canvas carries 8 channel
+    slots per pixel and the first layer reads it through the window stem
+    kernel when the library accepts that layer with an 8-element pixel
+    stride; otherwise the canvas is dense."""
+
+    def __init__(self, wl: Workload, seed: int = 0, device: str = "cuda", fuse: bool = False,
+                 pad_canvas: bool = True):
         if not wl.chained and len(wl.layers) != 1:
             raise ValueError("%s is neither a chained stack nor a single layer" % wl.name)
         self.wl = wl
         self.convs: List[_lib.Conv2d] = []
         self.params = []
         self.bufs: List[torch.Tensor] = []
+        # with a mosaic, the canvas carries 8 channel slots per pixel when the
+        # first layer can read them (the window stem kernel), else c_in
+        self.canvas_c = wl.mosaic[3] if wl.mosaic is not None else 0
         for i, layer in enumerate(wl.layers):
             p = layer_params(wl, i, seed)
-            conv = _lib.Conv2d.from_layer(layer)
+            conv = None
+            if i == 0 and wl.mosaic is not None and pad_canvas and layer.cin <= 8:
+                try:
+                    conv = _lib.Conv2d.from_layer(layer, x_stride=8)
+                    self.canvas_c = 8
+                except _lib.ConvError:
+                    conv = None
+            if conv is None:
+                conv = _lib.Conv2d.from_layer(layer)
             dev = {"w": p["w"].to(device)}
             if layer.dtype == "i8":
                 dev["b"] = _lib.pack_bias_scale(p["b"], p.get("s") if layer.out == "i8" else None).to(device)
@@ -54,7 +71,7 @@ class Stack:
         self.canvas: Optional[torch.Tensor] = None
         if wl.mosaic is not None:
             m, th, tw, c = wl.mosaic
-            self.canvas = torch.empty((m, 2 * th, 2 * tw, c), dtype=torch.bfloat16, device=device)
+            self.canvas = torch.empty((m, 2 * th, 2 * tw, self.canvas_c), dtype=torch.bfloat16, device=device)
         self.graph: Optional[torch.cuda.CUDAGraph] = None
         # fused[i]: layer i is launched together with layer i + 1
         self.fused = [False] * len(self.convs)
@@ -91,7 +108,7 @@ class Stack:
         then one per node of ``nodes()``)."""
         seq: List[Callable[[], None]] = []
         if self.canvas is not None:
-            seq.append(lambda: _lib.mosaic_pack(self.x0, self.canvas, out_dtype=torch.bfloat16))
+            seq.append(lambda: _lib.mosaic_pack(self.x0, self.canvas, c_pad=self.canvas_c, out_dtype=torch.bfloat16))
         for node in self.nodes():
             i = node[0]
             if len(node) == 2:
@@ -103,6 +120,13 @@ class Stack:
                 seq.append(lambda i=i: self.convs[i].run(self.layer_input(i), self.params[i]["w"],
                                                          self.params[i]["b"], self.bufs[i]))
         return seq
+
+    def mosaic_kernel(self) -> str:
+        """The kernel symbol of the mosaic launch (see csrc/mosaic.hip)."""
+        m, th, tw, c = self.wl.mosaic
+        if self.canvas_c == 8:
+            return "mosaic_px16_kernel"
+        return "mosaic_vec8_kernel" if self.canvas_c == c and (tw * c) % 8 == 0 else "mosaic_pixel_kernel"
 
     def node_kernel(self, node) -> str:
         """The kernel symbol a node launches."""

@@ -133,6 +133,15 @@ typedef struct conv_desc {
                              point as conv_pack_bfp8 writes it (BF16 layers
                              with groups == 1 and c_in * 2 a multiple of 16
                              only; others give CONV_E_UNSUPPORTED). */
+  int32_t x_pixel_stride; /* elements from one input pixel to the next: 0
+                             (or c_in) for dense NHWC. 8 with c_in <= 8 is
+                             the channel-padded input of a bf16 3x3
+                             stride-1 first layer (the mosaic packer's
+                             c_pad = 8 canvas): channels c_in .. 7 of each
+                             pixel are ignored, whatever they hold, and the
+                             layer runs on the window stem kernel. Any
+                             other value gives CONV_E_UNSUPPORTED (below
+                             c_in: CONV_E_SHAPE). */
 } conv_desc;
 
 typedef struct conv_plan conv_plan;

@@ -421,3 +421,23 @@ def test_run_fused_pointer_checks_before_launch():
     assert L.conv_run_fused(P1, P2, X, W1, Y + 64, W2, B2, Y, None) == -5     # b1 inside y
     for c in (a, b, bad):
         c.close()
+
+
+def test_pixel_stride_checks():
+    """x_pixel_stride: 8 with c_in <= 8 on a 3x3 stride-1 bf16 layer is the
+    window stem kernel; every other non-dense stride is refused."""
+    base = dict(n=1, h=20, w=20, c_in=3, c_out=32, kh=3, kw=3, stride=(1, 1), pad=(1, 1), dtype="bf16",
+                act="mish", x_stride=8)
+    c = Conv2d(**base)
+    assert c.describe().startswith("stem_window ") and c.in_shape == (1, 20, 20, 8), c.describe()
+    c.close()
+    c = Conv2d(**dict(base, c_in=16, x_stride=16))  # dense
+    assert not c.describe().startswith("stem_window ")
+    c.close()
+    for kw, code in ((dict(stride=(2, 2)), "CONV_E_UNSUPPORTED"), (dict(kh=5, kw=5, pad=(2, 2)), "CONV_E_UNSUPPORTED"),
+                     (dict(c_in=16, x_stride=8), "CONV_E_SHAPE"), (dict(x_stride=4), "CONV_E_UNSUPPORTED"),
+                     (dict(dtype="i8", out_dtype="i8"), "CONV_E_UNSUPPORTED"), (dict(algo=1), "CONV_E_UNSUPPORTED"),
+                     (dict(pad=(2, 2)), "CONV_E_UNSUPPORTED"), (dict(w_format="bfp8"), "CONV_E_UNSUPPORTED")):
+        with pytest.raises(ConvError) as e:
+            Conv2d(**dict(base, **kw))
+        assert e.value.name == code, (kw, e.value.name)
