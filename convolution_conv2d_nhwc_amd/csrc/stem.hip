@@ -51,7 +51,7 @@ __device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t r, char* lds, u
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(256) void stem_window_kernel(StemArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void stem_window_kernel(StemArgs a) {
   __shared__ __attribute__((aligned(1024))) char win[kStemPatches][kWinGroups * 1024];
 
   const Geometry g = a.g;
@@ -117,12 +117,16 @@ __global__ __launch_bounds__(256) void stem_window_kernel(StemArgs a) {
       }
   }
   // B masks: the channel slots c_in .. 7 of an input pixel read as zero
-  uint32_t bmask[4];
+  // (tap slots past the ninth: all zero)
+  uint32_t bmask[4], bmask2[4];
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int d = 0; d < 4; ++d) {
     bmask[d] = (2 * d < g.c ? 0xffffu : 0u) | (2 * d + 1 < g.c ? 0xffff0000u : 0u);
-  const QuadConsts qc0 = load_quad_consts_t<2>(a.e, co0 + 4 * q, g.cout);
-  const QuadConsts qc1 = load_quad_consts_t<2>(a.e, co0 + 16 + 4 * q, g.cout);
+    bmask2[d] = 8 + q < 9 ? bmask[d] : 0u;
+  }
+  // the bias is the accumulators' starting value
+  const QuadConsts qb0 = load_quad_consts_t<2>(a.e, co0 + 4 * q, g.cout);
+  const QuadConsts qb1 = load_quad_consts_t<2>(a.e, co0 + 16 + 4 * q, g.cout);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -141,19 +145,22 @@ __global__ __launch_bounds__(256) void stem_window_kernel(StemArgs a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) {
+      const QuadConsts& qb = i ? qb1 : qb0;
+      acc[i][j] = acc_t{qb.bsf[0], qb.bsf[1], qb.bsf[2], qb.bsf[3]};
+    }
 #pragma unroll
   for (int ks = 0; ks < 3; ++ks) {
     const int tap = min(4 * ks + q, 8);
     const int kh = tap / 3, kw = tap - 3 * (tap / 3);
     const int off = pbase + (kh * kWC + kw) * 16;
-    const bool live = 4 * ks + q < 9;
+    const uint32_t* const mk = ks == 2 ? bmask2 : bmask;  // taps 0-7 always exist
     i32x4 bf[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const i32x4 r = *reinterpret_cast<const i32x4*>(win[t] + off + j * 256);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) bf[j][d] = live ? (int)((uint32_t)r[d] & bmask[d]) : 0;
+      for (int d = 0; d < 4; ++d) bf[j][d] = (int)((uint32_t)r[d] & mk[d]);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -165,14 +172,32 @@ __global__ __launch_bounds__(256) void stem_window_kernel(StemArgs a) {
   // c0 + 16 j + (lane & 15)). (Restaging the tile through LDS so that every
   // store is a 16-byte piece of a 1 KiB run measured no faster.)
   const int r = r0 + wave;
-  with_epilogue<2>(OUT_BF16, a.e.act, [&](auto oc, auto ac) {
-    constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
+  // act(acc) [+ residual], bf16, one 8-byte store per quad (the bias is
+  // already in acc)
+  with_epilogue<2>(OUT_BF16, a.e.act, [&](auto, auto ac) {
+    constexpr int ACT = decltype(ac)::value;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = c0 + 16 * j + (lane & 15);
-      const int px = (r < g.ho && c < g.wo) ? (n * g.ho + r) * g.wo + c : g.m;
-      store_quad_t<2, OUT, ACT>(acc[0][j], qc0, co0 + 4 * q, px, o);
-      store_quad_t<2, OUT, ACT>(acc[1][j], qc1, co0 + 16 + 4 * q, px, o);
+      const bool pin = r < g.ho && c < g.wo;
+      const int px = pin ? (n * g.ho + r) * g.wo + c : 0;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int co = co0 + 16 * i + 4 * q;
+        const bool in = pin && co < g.cout;
+        const uint32_t off = in ? (uint32_t)(px * g.cout + co) * 2u : kOOB;
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = act_t<ACT>(acc[i][j][e]);
+        if (o.has_res) {
+          const u32x2 rv = __builtin_amdgcn_raw_buffer_load_b64(o.rr, off, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] += bf16_bits_to_f32((e & 1) ? (rv[e >> 1] >> 16) : (rv[e >> 1] & 0xffffu));
+        }
+        const u32x2 d = {(uint32_t)f32_to_bf16_bits(f[0]) | ((uint32_t)f32_to_bf16_bits(f[1]) << 16),
+                         (uint32_t)f32_to_bf16_bits(f[2]) | ((uint32_t)f32_to_bf16_bits(f[3]) << 16)};
+        __builtin_amdgcn_raw_buffer_store_b64(d, o.r, off, 0, 0);
+      }
     }
   });
   }
