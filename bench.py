@@ -174,12 +174,20 @@ def main():
         fl = sum(l.flops() for l in ls)
         # a fused pair: the intermediate tensor is neither written nor read
         by = sum(l.bytes() for l in ls) - 2 * sum(l.n * l.ho * l.wo * l.cout * 2 for l in ls[:-1])
+        name = "+".join(l.name for l in ls)
+        if node == (0,) and stack.mosaic_fused:
+            # the mosaic folded into the first layer: its input is the fp32
+            # tiles, the canvas is never written
+            m, th, tw, c = wl.mosaic
+            l0 = ls[0]
+            by += 4 * m * th * tw * c * 4 - l0.n * l0.h * l0.w * l0.cin * 2
+            name = "mosaic_pack+" + name
         dt = ls[0].dtype
         t_mfma = fl / (PEAK[dt] * 1e12)
         t_hbm = by / (HBM_GBS * 1e9)
         bound = "mfma" if t_mfma >= t_hbm else "hbm"
         desc = _lib.describe_fused(convs[node[0]], convs[node[1]]) if len(node) == 2 else convs[node[0]].describe()
-        layers.append({"name": "+".join(l.name for l in ls), "kernel": desc.split(" kernel=")[-1],
+        layers.append({"name": name, "kernel": stack.node_kernel(node),
                        "desc": desc, "us": us, "gflop": fl / 1e9, "mbytes": by / 1e6,
                        "tflops": fl / (us * 1e-6) / 1e12, "gbs": by / (us * 1e-6) / 1e9, "bound": bound,
                        "frac": max(t_mfma, t_hbm) / (us * 1e-6)})
@@ -244,6 +252,7 @@ def main():
                    "gflop_per_step": total_flop / 1e9, "timing": "hipGraph replay, HIP events",
                    "graph_nodes": len(stack.launches()), "fused_pairs": ["+".join(wl.layers[i].name for i in n)
                                                                         for n in stack.nodes() if len(n) == 2],
+                   "mosaic_folded_into_first_layer": stack.mosaic_fused,
                    "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,

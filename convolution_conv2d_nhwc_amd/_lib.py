@@ -92,6 +92,8 @@ def lib():
     L.conv_describe_fused.restype = ctypes.c_int
     L.conv_run_fused.argtypes = [P] * 9
     L.conv_run_fused.restype = ctypes.c_int
+    L.conv_run_mosaic.argtypes = [P, P, I32, I32, I32, P, P, P, P]
+    L.conv_run_mosaic.restype = ctypes.c_int
     L.conv_bfp8_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
     L.conv_bfp8_bytes.restype = ctypes.c_int64
     L.conv_pack_bfp8.argtypes = [P, I32, ctypes.c_int64, ctypes.c_int64, P, P]
@@ -394,4 +396,28 @@ def run_fused(c1: Conv2d, c2: Conv2d, x: torch.Tensor, w1: torch.Tensor, b1: Opt
                               w2.data_ptr(), None if b2 is None else b2.data_ptr(), y.data_ptr(),
                               _stream_handle(stream))
     _check(st, "conv_run_fused")
+    return y
+
+
+def run_mosaic(conv: Conv2d, tiles: torch.Tensor, w: torch.Tensor, b: Optional[torch.Tensor] = None,
+               y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """conv (a window-stem plan on the canvas) applied to the mosaic of tiles
+    [4m, th, tw, c] (float32 or bfloat16) without packing the canvas."""
+    if tiles.dim() != 4 or tiles.shape[0] % 4:
+        raise ValueError("tiles must be [4m, th, tw, c]")
+    conv._chk(tiles, "tiles", tiles.dtype if tiles.dtype in (torch.float32, torch.bfloat16) else torch.float32, None)
+    conv._chk(w, "w", conv._w_dtype(), conv.w_shape)
+    if b is not None:
+        conv._chk(b, "b", torch.float32, None)
+    if y is None:
+        y = conv.empty_output(tiles.device)
+    conv._chk(y, "y", TORCH_DT[conv.out_dtype], conv.out_shape)
+    q, th, tw, c = tiles.shape
+    n, h, wd = conv.in_shape[:3]
+    if q != 4 * n or 2 * th != h or 2 * tw != wd or c != conv.w_shape[3]:
+        raise ValueError("tiles %s do not make the layer's %s canvas" % (tuple(tiles.shape), conv.in_shape))
+    st = lib().conv_run_mosaic(conv._plan, tiles.data_ptr(), DTYPES["f32" if tiles.dtype == torch.float32 else "bf16"],
+                               th, tw, w.data_ptr(), None if b is None else b.data_ptr(), y.data_ptr(),
+                               _stream_handle(stream))
+    _check(st, "conv_run_mosaic")
     return y

@@ -529,6 +529,32 @@ conv_status conv_run_fused(const conv_plan* p1, const conv_plan* p2, const void*
   return CONV_OK;
 }
 
+conv_status conv_run_mosaic(const conv_plan* p, const void* tiles, int32_t tiles_dtype, int32_t th, int32_t tw,
+                            const void* w, const void* b, void* y, void* stream) {
+  if (!p || !tiles || !w || !y) return CONV_E_NULL;
+  if (tiles_dtype != CONV_F32 && tiles_dtype != CONV_BF16) return CONV_E_UNSUPPORTED;
+  if (!stem_mosaic_ok(p, th, tw)) return CONV_E_UNSUPPORTED;
+  const int esz = tiles_dtype == CONV_F32 ? 4 : 2;
+  const int64_t t_bytes = (int64_t)4 * p->g.n * th * tw * p->g.c * esz;
+  if (t_bytes >= kMaxBytes) return CONV_E_UNSUPPORTED;
+  if (((uintptr_t)w | (uintptr_t)y) & 15) return CONV_E_ALIGN;
+  if (((uintptr_t)tiles & (esz - 1)) || ((uintptr_t)b & 3)) return CONV_E_ALIGN;
+  if (ranges_overlap(y, p->y_bytes, tiles, t_bytes) || ranges_overlap(y, p->y_bytes, w, p->w_bytes) ||
+      ranges_overlap(y, p->y_bytes, b, p->b_bytes))
+    return CONV_E_ALIAS;
+  Epi e;
+  std::memset(&e, 0, sizeof(e));
+  e.act = p->d.act;
+  e.bias = static_cast<const float*>(b);
+  const hipError_t err =
+      launch_stem_mosaic(p, tiles, tiles_dtype == CONV_F32, th, tw, w, e, y, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(err));
+    return CONV_E_HIP;
+  }
+  return CONV_OK;
+}
+
 conv_status conv_destroy(conv_plan* p) {
   if (p && p->ws && p->ws_owned) {
     int cur = 0;
@@ -585,7 +611,7 @@ conv_status conv_describe(const conv_plan* p, char* buf, int32_t len) {
   } else if (p->path == PATH_STEM) {
     std::snprintf(buf, len,
                   "stem_window dtype=bf16 out=bf16 cin=%d x_stride=%d patch=4x64 co32 wgs=%d m=%d k=%d "
-                  "kernel=stem_window_kernel",
+                  "kernel=stem_window_kernel<0>",
                   p->g.c, (int)(p->x_bytes / ((int64_t)p->g.n * p->g.h * p->g.w * 2)), stem_grid(p), p->g.m, p->g.k);
   } else if (p->path == PATH_SMALLK) {
     int fco, ks;

@@ -96,6 +96,9 @@ hipError_t launch_ws(const conv_plan* p, const void* x, const void* w, const Epi
 bool stem_eligible(const conv_desc& d, const Geometry& g, int64_t x_stride);
 int stem_grid(const conv_plan* p);  // workgroups per 32 output channels
 hipError_t launch_stem(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);
+bool stem_mosaic_ok(const conv_plan* p, int64_t th, int64_t tw);  // the stem plan reads th x tw tiles
+hipError_t launch_stem_mosaic(const conv_plan* p, const void* tiles, int tiles_f32, int th, int tw, const void* w,
+                              const Epi& e, void* y, hipStream_t s);
 bool halo_eligible(const conv_desc& d, const Geometry& g);
 bool halo_preferred(const conv_desc& d, const Geometry& g);  // the automatic choice
 bool halo_fusable(const conv_desc& d, const Geometry& g);    // the fused launch can use the halo kernel

@@ -45,12 +45,21 @@ struct StemArgs {
   int w_bytes;
   int npr, npc;  // patches per image: rows, columns
   int npatch;    // n * npr * npc
+  // MOS: the input is the four-tile mosaic of each canvas, tiles
+  // [4 n][th][tw][c] (A top-left, B top-right, C bottom-left, D
+  // bottom-right), read and rounded to bf16 here instead of a packed canvas
+  int th, tw;
 };
 
 __device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
 }
 
+// MOS 0: x is the canvas padded to 16-byte pixels, copied into LDS;
+// MOS 1 / 2: x is the mosaic's fp32 / bf16 tiles, each window pixel gathered
+// from its tile, rounded to bf16 (as the mosaic packer rounds) and written
+// into LDS zero-padded to 16 bytes.
+template <int MOS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void stem_window_kernel(StemArgs a) {
   __shared__ __attribute__((aligned(1024))) char win[kStemPatches][kWinGroups * 1024];
 
@@ -80,15 +89,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     int n, r0, c0;
     origin(p, n, r0, c0);
     const int hi0 = r0 - g.ph, wi0 = c0 - g.pw;
+    if constexpr (MOS == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int k = wave + 4 * i;
-      if (k < kWinGroups) {
-        const int q = 64 * k + lane;
-        const int hr = q / kWC, hc = q - hr * kWC;
-        const int hi = hi0 + hr, wi = wi0 + hc;
-        const bool ok = q < kWinPx && (unsigned)hi < (unsigned)g.h && (unsigned)wi < (unsigned)g.w;
-        dma16_lds(rx, win[t] + k * 1024, ok ? (uint32_t)(((n * g.h + hi) * g.w + wi) * 16) : kOOB);
+      for (int i = 0; i < 2; ++i) {
+        const int k = wave + 4 * i;
+        if (k < kWinGroups) {
+          const int q = 64 * k + lane;
+          const int hr = q / kWC, hc = q - hr * kWC;
+          const int hi = hi0 + hr, wi = wi0 + hc;
+          const bool ok = q < kWinPx && (unsigned)hi < (unsigned)g.h && (unsigned)wi < (unsigned)g.w;
+          dma16_lds(rx, win[t] + k * 1024, ok ? (uint32_t)(((n * g.h + hi) * g.w + wi) * 16) : kOOB);
+        }
+      }
+    } else {
+      constexpr int ESZ_IN = MOS == 1 ? 4 : 2;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int q = tid + 256 * i;
+        if (q < kWinPx) {
+          const int hr = q / kWC, hc = q - hr * kWC;
+          const int hi = hi0 + hr, wi = wi0 + hc;
+          const bool ok = (unsigned)hi < (unsigned)g.h && (unsigned)wi < (unsigned)g.w;
+          const int qy = hi >= a.th, qx = wi >= a.tw;
+          const int src = (((4 * n + 2 * qy + qx) * a.th + hi - qy * a.th) * a.tw + wi - qx * a.tw) * g.c;
+          uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+          for (int ci = 0; ci < 8; ++ci)
+            if (ci < g.c) {
+              const uint32_t off = ok ? (uint32_t)(src + ci) * ESZ_IN : kOOB;
+              if constexpr (MOS == 1)
+                h[ci] = f32_to_bf16_bits(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0)));
+              else
+                h[ci] = bload_elem<2>(rx, off);
+            }
+          *reinterpret_cast<u32x4*>(win[t] + q * 16) =
+              u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        }
       }
     }
   }
@@ -210,6 +246,10 @@ bool stem_eligible(const conv_desc& d, const Geometry& g, int64_t x_stride) {
          g.sw == 1 && g.c <= 8 && x_stride == 8 && g.ph <= 1 && g.pw <= 1 && (g.cout & 3) == 0;
 }
 
+bool stem_mosaic_ok(const conv_plan* p, int64_t th, int64_t tw) {
+  return p->path == PATH_STEM && th > 0 && tw > 0 && p->g.h == 2 * th && p->g.w == 2 * tw;
+}
+
 int stem_grid(const conv_plan* p) {
   const int npatch = p->g.n * ((p->g.ho + kSR - 1) / kSR) * ((p->g.wo + kSC - 1) / kSC);
   return (npatch + kStemPatches - 1) / kStemPatches;
@@ -227,8 +267,32 @@ hipError_t launch_stem(const conv_plan* p, const void* x, const void* w, const E
   a.npr = (p->g.ho + kSR - 1) / kSR;
   a.npc = (p->g.wo + kSC - 1) / kSC;
   a.npatch = p->g.n * a.npr * a.npc;
+  a.th = a.tw = 0;
   const dim3 grid(stem_grid(p), (p->g.cout + kStemTco - 1) / kStemTco);
-  hipLaunchKernelGGL(stem_window_kernel, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(stem_window_kernel<0>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stem_mosaic(const conv_plan* p, const void* tiles, int tiles_f32, int th, int tw, const void* w,
+                              const Epi& e, void* y, hipStream_t s) {
+  StemArgs a;
+  a.x = static_cast<const char*>(tiles);
+  a.w = static_cast<const char*>(w);
+  a.y = y;
+  a.e = e;
+  a.g = p->g;
+  a.x_bytes = (int)((int64_t)4 * p->g.n * th * tw * p->g.c * (tiles_f32 ? 4 : 2));
+  a.w_bytes = (int)p->w_bytes;
+  a.npr = (p->g.ho + kSR - 1) / kSR;
+  a.npc = (p->g.wo + kSC - 1) / kSC;
+  a.npatch = p->g.n * a.npr * a.npc;
+  a.th = th;
+  a.tw = tw;
+  const dim3 grid(stem_grid(p), (p->g.cout + kStemTco - 1) / kStemTco);
+  if (tiles_f32)
+    hipLaunchKernelGGL(stem_window_kernel<1>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(stem_window_kernel<2>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

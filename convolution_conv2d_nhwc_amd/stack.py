@@ -35,7 +35,9 @@ class Stack:
     With ``pad_canvas`` (a stack with a mosaic), the canvas carries 8 channel
     slots per pixel and the first layer reads it through the window stem
     kernel when the library accepts that layer with an 8-element pixel
-    stride; otherwise the canvas is dense."""
+    stride; otherwise the canvas is dense. With ``fuse`` as well, the mosaic
+    is folded into that layer's input gather (``conv_run_mosaic``): one
+    launch reads the tiles and the canvas is never written."""
 
     def __init__(self, wl: Workload, seed: int = 0, device: str = "cuda", fuse: bool = False,
                  pad_canvas: bool = True):
@@ -73,6 +75,9 @@ class Stack:
             m, th, tw, c = wl.mosaic
             self.canvas = torch.empty((m, 2 * th, 2 * tw, self.canvas_c), dtype=torch.bfloat16, device=device)
         self.graph: Optional[torch.cuda.CUDAGraph] = None
+        self.mosaic_fused = bool(fuse and self.canvas is not None and self.canvas_c == 8)
+        if self.mosaic_fused:
+            self.canvas = None
         # fused[i]: layer i is launched together with layer i + 1
         self.fused = [False] * len(self.convs)
         if fuse:
@@ -89,7 +94,7 @@ class Stack:
     def layer_input(self, i: int) -> torch.Tensor:
         if i > 0:
             return self.bufs[i - 1]
-        return self.canvas if self.canvas is not None else self.x0
+        return self.canvas if self.canvas is not None else self.x0  # (the tiles when the mosaic is folded in)
 
     def nodes(self) -> List[tuple]:
         """The layers of each launch: (i,) or (i, i + 1) for a fused pair."""
@@ -116,6 +121,9 @@ class Stack:
                                                       self.params[i]["w"], self.params[i]["b"],
                                                       self.params[i + 1]["w"], self.params[i + 1]["b"],
                                                       self.bufs[i + 1]))
+            elif i == 0 and self.mosaic_fused:
+                seq.append(lambda: _lib.run_mosaic(self.convs[0], self.x0, self.params[0]["w"], self.params[0]["b"],
+                                                   self.bufs[0]))
             else:
                 seq.append(lambda i=i: self.convs[i].run(self.layer_input(i), self.params[i]["w"],
                                                          self.params[i]["b"], self.bufs[i]))
@@ -130,6 +138,8 @@ class Stack:
 
     def node_kernel(self, node) -> str:
         """The kernel symbol a node launches."""
+        if node == (0,) and self.mosaic_fused:
+            return "stem_window_kernel<1>"
         if len(node) == 2:
             d = _lib.describe_fused(self.convs[node[0]], self.convs[node[1]])
         else:

@@ -280,6 +280,26 @@ conv_status conv_describe_fused(const conv_plan* p1, const conv_plan* p2, char* 
 conv_status conv_run_fused(const conv_plan* p1, const conv_plan* p2, const void* x, const void* w1,
                            const void* b1, const void* w2, const void* b2, void* y, void* stream);
 
+/* The first layer of a stack fed by the mosaic, with the mosaic packing
+ * folded into the layer's input gather: the canvas never exists
+ * (YOLOv4/Wormhole section 4, the m640 layout of four photos in one canvas,
+ * and section 10, fewer operations and no intermediate write and read).
+ * p : a plan prepared with x_pixel_stride = 8 (the window stem kernel) for
+ *     the canvas: n = m canvases, h = 2 th, w = 2 tw, c_in = the tiles'
+ *     channels (<= 8).
+ * tiles : device [4 m][th][tw][c_in] of tiles_dtype (CONV_F32 or
+ *     CONV_BF16), A top-left, B top-right, C bottom-left, D bottom-right of
+ *     each canvas, as conv_mosaic_pack takes them; read and rounded to bf16
+ *     (RNE) exactly as conv_mosaic_pack writes the canvas.
+ * w, b, y : as conv_run. y = conv_run(p) on conv_mosaic_pack(tiles, bf16,
+ * c_pad = 8), bit for bit.
+ * CONV_E_NULL, CONV_E_UNSUPPORTED (not a window-stem plan, tiles that do not
+ * make its canvas, tile dtype), CONV_E_ALIGN (tiles to their element, w and
+ * y to 16 bytes, b to 4), CONV_E_ALIAS (y overlapping tiles, w or b),
+ * CONV_E_HIP. */
+conv_status conv_run_mosaic(const conv_plan* p, const void* tiles, int32_t tiles_dtype, int32_t th, int32_t tw,
+                            const void* w, const void* b, void* y, void* stream);
+
 /* Free a plan and the workspace conv_prepare allocated for it; all device
  * memory a plan holds is taken at preparation and given back here, none in
  * between (nanoinfer README, memory planner: no allocations in the forward

@@ -441,3 +441,23 @@ def test_pixel_stride_checks():
         with pytest.raises(ConvError) as e:
             Conv2d(**dict(base, **kw))
         assert e.value.name == code, (kw, e.value.name)
+
+
+def test_run_mosaic_checks_before_launch():
+    L = _lib.lib()
+    stem = Conv2d(1, 20, 30, 3, 32, 3, 3, (1, 1), (1, 1), dtype="bf16", act="mish", x_stride=8)
+    dense = Conv2d(1, 20, 30, 3, 32, 3, 3, (1, 1), (1, 1), dtype="bf16", act="mish")
+    T, W, B, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+    P = stem._plan
+    assert L.conv_run_mosaic(None, T, 0, 10, 15, W, B, Y, None) == -1
+    assert L.conv_run_mosaic(P, None, 0, 10, 15, W, B, Y, None) == -1
+    assert L.conv_run_mosaic(P, T, 0, 10, 15, W, B, None, None) == -1
+    assert L.conv_run_mosaic(P, T, 2, 10, 15, W, B, Y, None) == -3          # int8 tiles
+    assert L.conv_run_mosaic(dense._plan, T, 0, 10, 15, W, B, Y, None) == -3  # not a window-stem plan
+    assert L.conv_run_mosaic(P, T, 0, 10, 16, W, B, Y, None) == -3          # tiles do not make the canvas
+    assert L.conv_run_mosaic(P, T + 2, 0, 10, 15, W, B, Y, None) == -4      # fp32 tiles need 4-byte alignment
+    assert L.conv_run_mosaic(P, T + 2, 1, 10, 15, W, B, T + 64, None) == -5  # bf16 tiles: 2 is enough (then alias)
+    assert L.conv_run_mosaic(P, T, 0, 10, 15, W + 8, B, Y, None) == -4
+    assert L.conv_run_mosaic(P, T, 0, 10, 15, W, B, T + 64, None) == -5     # y inside the tiles
+    stem.close()
+    dense.close()

@@ -99,3 +99,50 @@ def test_stem_yolo640_full_size():
     rb, ab = H.oracle_full(band, xb, t)
     # output rows 301..306 depend only on input rows 300..307
     H.check_float(y[:, 301:307].float().numpy(), rb[:, 1:7], ab[:, 1:7], "bf16", "stem band rows 301-306")
+
+
+def _mosaic_layer(name, m, th, tw, c, cout, act):
+    return L(name, m, 2 * th, 2 * tw, c, cout, act=act)
+
+
+@pytest.mark.parametrize("tdt", ["f32", "bf16"])
+def test_mosaic_folded_vs_oracle_and_packed(tdt):
+    """conv_run_mosaic on four tiles per canvas: against the oracle's
+    mosaic + convolution, and bit-equal to packing the canvas first."""
+    layer = _mosaic_layer("mos_" + tdt, 2, 13, 37, 3, 48, "mish")
+    g = np.random.default_rng(86)
+    tiles = torch.from_numpy(g.random((8, 13, 37, 3)).astype(np.float32))
+    if tdt == "bf16":
+        tiles = tiles.to(torch.bfloat16)
+    t = random_layer_tensors(layer, "bf16", seed=87)
+    conv = _lib.Conv2d.from_layer(layer, x_stride=8)
+    tg, wg, bg = tiles.cuda(), t["w"].cuda(), t["b"].cuda()
+    y = conv.empty_output()
+    y.fill_(float("nan"))
+    _lib.run_mosaic(conv, tg, wg, bg, y)
+    can = _lib.mosaic_pack(tg, c_pad=8, out_dtype=torch.bfloat16)
+    y2 = conv.run(can, wg, bg)
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu().view(torch.int16), y2.cpu().view(torch.int16)), "folded vs packed"
+    if tdt == "f32":
+        bits = oracle.mosaic(tiles.numpy(), out="bf16")
+        x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    else:
+        # bf16 tiles are copied as they are: the canvas is the tiles placed 2x2
+        x = torch.cat([torch.cat([tiles[0::4], tiles[1::4]], 2), torch.cat([tiles[2::4], tiles[3::4]], 2)], 1)
+    H.check_layer_full(layer, x, t, y.cpu(), "%s [%s]" % (layer.name, conv.describe()))
+    conv.close()
+
+
+def test_mosaic_folded_yolo640_bit_equal_to_packed():
+    wl = workload("yolo640_bf16")
+    layer = wl.layers[0]
+    p = layer_params(wl, 0)
+    tiles = (torch.rand((4, 320, 320, 3), generator=torch.Generator().manual_seed(88))).cuda()
+    conv = _lib.Conv2d.from_layer(layer, x_stride=8)
+    w, b = p["w"].cuda(), p["b"].cuda()
+    y = _lib.run_mosaic(conv, tiles, w, b)
+    y2 = conv.run(_lib.mosaic_pack(tiles, c_pad=8, out_dtype=torch.bfloat16), w, b)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    conv.close()
