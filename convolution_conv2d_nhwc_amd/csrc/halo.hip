@@ -148,8 +148,12 @@ __global__ __launch_bounds__(TCO * 4) __attribute__((amdgpu_waves_per_eu(2))) vo
     c0 = (rem - rb * a.npc) * kPC;
   };
   // issue the window of patch p into buffer `buf` (a patch past the last
-  // writes zeros: every wave issues exactly NDMA copies per patch)
-  auto load_window = [&](int p, int buf) {
+  // writes zeros: every wave issues exactly NDMA copies per patch); returns
+  // the patch's origin, which the patch's epilogue uses later
+  struct Origin {
+    int n, r0, c0;
+  };
+  auto load_window = [&](int p, int buf) -> Origin {
     int n, r0, c0;
     patch_origin(p < a.npatch ? p : 0, n, r0, c0);
     const int hi0 = r0 * S - g.ph, wi0 = c0 * S - g.pw;
@@ -167,10 +171,11 @@ __global__ __launch_bounds__(TCO * 4) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
       dma16(rx, dst + (wave + NW * i) * 1024, ok ? (uint32_t)(base + d_rel[i]) : kOOB);
     }
+    return Origin{n, r0, c0};
   };
 
   int p = q0;
-  load_window(p, 0);
+  Origin cur = load_window(p, 0);
 
   // ---- this wave's weights: wa[tap][ks][i] = channel row co0 + 32 cg + 16 i
   // + (lane & 15), channels 32 ks + 8 (lane >> 4) .. +7 of tap `tap` (the
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(TCO * 4) __attribute__((amdgpu_waves_per_eu(2))) vo
     // are out of that buffer before anyone copies a window into it)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    load_window(p + a.gp, buf ^ 1);
+    const Origin nxt = load_window(p + a.gp, buf ^ 1);
 
     acc_t acc[2][2];
 #pragma unroll
@@ -307,8 +312,8 @@ __global__ __launch_bounds__(TCO * 4) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     });
 
-    int n, r0, c0;
-    patch_origin(p, n, r0, c0);
+    const int n = cur.n, r0 = cur.r0, c0 = cur.c0;
+    cur = nxt;
     if constexpr (FU == 0) {
       with_epilogue<2>(OUT_BF16, a.e.act, [&](auto, auto ac) {
         constexpr int ACT = decltype(ac)::value;
