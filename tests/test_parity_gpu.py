@@ -275,7 +275,8 @@ def test_zero_bias_pointer():
 
 
 # Few output tiles, long reduction: the plan splits K over workgroups and a
-# second kernel sums the partials in split order.
+# second kernel sums the partials in split order (the allocation-free entry
+# keeps them in the static scratch instead: the same bits).
 SPLITK = [
     L("splitk_bf16_mish", 1, 20, 20, 512, 1024, 3, 3, (2, 2), (1, 1)),
     L("splitk_bf16_1x1", 1, 12, 12, 2048, 96, 1, 1, act="relu"),
@@ -301,6 +302,16 @@ def test_split_k(layer):
         ys.append(y)
     torch.cuda.synchronize()
     assert torch.equal(ys[0].view(torch.uint8), ys[1].view(torch.uint8)), "split-K run-to-run difference"
+    # many launches back to back on the one workspace
+    yb = conv.empty_output()
+    for _ in range(20):
+        conv.run(x, w, b, yb)
+    yn = conv.empty_output()
+    yn.fill_(float("nan") if yn.dtype.is_floating_point else -77)
+    conv.run_noalloc(x, w, b, yn)
+    torch.cuda.synchronize()
+    assert torch.equal(yb.view(torch.uint8), ys[0].view(torch.uint8)), "split-K after 20 launches"
+    assert torch.equal(yn.view(torch.uint8), ys[0].view(torch.uint8)), "plan workspace vs static scratch"
     what = "%s [%s]" % (layer.name, desc)
     if layer.dtype == "i8":
         H.check_int(ys[0].cpu().numpy(), ref, layer, what)
