@@ -35,6 +35,7 @@
 // channels of one pixel, which the epilogue stores as one NHWC vector.
 #include <algorithm>
 #include <cstring>
+#include <vector>
 
 #include "igemm_common.h"
 
@@ -62,7 +63,7 @@ struct IgArgs {
   float rcp_c;   // 1.0f / Cin
   float rcp_kw;  // 1.0f / KW
   int x_shift;   // LOAD_TAP: bytes the x descriptor starts before x
-  int px_fastest;  // tile order: pixel tiles vary fastest (weights > activations)
+  int co_group;  // tile order: channel tiles per group (nco_tiles: channel tile fastest; 1: pixel tile fastest)
   int ksplit;    // K-splits (gridDim.y); > 1 writes raw partial sums to ws
   int kt_per;    // K-tiles per split
   void* ws;      // [ksplit][m][cout] fp32 / int32 partial sums
@@ -134,16 +135,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
   const __amdgpu_buffer_rsrc_t rw = rsrc(a.w, a.w_bytes);
 
   // Tiles are handed to the 8 XCDs round-robin by workgroup id; remap so each
-  // XCD (own L2) gets a contiguous run of tiles. With the channel tile varying
-  // fastest an XCD's run shares activation rows (layers whose activations
-  // outweigh their weights); with the pixel tile fastest it shares weight
-  // rows (deep layers whose weights are the larger operand).
-  int lin = blockIdx.x;
+  // XCD (own L2) gets a contiguous run of tiles: XCD x = id % 8 takes the
+  // q = nwg / 8 tiles (one more for x < nwg % 8) from x q + min(x, nwg % 8)
+  // on. The run walks groups of co_group channel tiles, the channel tile
+  // fastest within a group, then the pixel tile: an XCD's run touches about
+  // co_group channel tiles and run / co_group pixel tiles, so the group size
+  // trades weight rows against activation rows (co_group_for picks it).
   const int nwg = gridDim.x;
-  if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
+  const int xcd = blockIdx.x & 7;
+  const int lin = xcd * (nwg >> 3) + min(xcd, nwg & 7) + (blockIdx.x >> 3);
   const int npx_tiles = nwg / a.nco_tiles;
-  const int co0 = (a.px_fastest ? lin / npx_tiles : lin % a.nco_tiles) * TCO;
-  const int px0 = (a.px_fastest ? lin % npx_tiles : lin / a.nco_tiles) * TPX;
+  const int span = a.co_group * npx_tiles;
+  const int grp = lin / span;
+  const int first = grp * a.co_group;
+  const int gsz = min(a.nco_tiles - first, a.co_group);
+  const int rem = lin - grp * span;
+  const int co0 = (first + rem % gsz) * TCO;
+  const int px0 = (rem / gsz) * TPX;
   const int hw_o = g.ho * g.wo;
 
   // ---- per-thread loader state -------------------------------------
@@ -657,6 +665,47 @@ hipError_t launch_fused_tile(const IgArgs& args, dim3 nwg, hipStream_t s) {
 
 }  // namespace
 
+// Channel tiles per group of the implicit-GEMM kernels' tile order. XCD x
+// runs the workgroups [x q + min(x, r), ...) (q = nwg / 8, one more for
+// x < r = nwg % 8): the group size is the one whose runs touch the fewest
+// bytes in all, counting the weight rows of each channel tile (w_bytes /
+// nco) and the input share of each pixel tile (x_bytes / npx) once per XCD
+// that touches it. Grids too large to count keep one order: pixel tiles
+// fastest when the weights outweigh the input.
+int co_group_for(const conv_plan* p, int nco, int npx) {
+  const long nwg = (long)nco * npx;
+  const int fallback = p->w_bytes > p->x_bytes ? 1 : nco;
+  if (nwg * nco > (1L << 22)) return fallback;
+  const long q = nwg / 8, r = nwg % 8;
+  const double wt = (double)p->w_bytes / nco, xt = (double)p->x_bytes / npx;
+  std::vector<int> seen_c(nco), seen_p(npx);
+  int best = fallback;
+  double best_b = -1;
+  for (int g = 1; g <= nco; ++g) {
+    const long span = (long)g * npx;
+    double b = 0;
+    for (long x = 0; x < 8; ++x) {
+      std::fill(seen_c.begin(), seen_c.end(), 0);
+      std::fill(seen_p.begin(), seen_p.end(), 0);
+      long tc = 0, tp = 0;
+      const long lin0 = x * q + std::min(x, r), lin1 = lin0 + q + (x < r);
+      for (long lin = lin0; lin < lin1; ++lin) {
+        const long grp = lin / span, first = grp * g, rem = lin - grp * span;
+        const long gsz = std::min<long>(nco - first, g);
+        const long c = first + rem % gsz, t = rem / gsz;
+        if (!seen_c[c]) seen_c[c] = 1, ++tc;
+        if (!seen_p[t]) seen_p[t] = 1, ++tp;
+      }
+      b += tc * wt + tp * xt;
+    }
+    if (best_b < 0 || b < best_b - 1e-9 * best_b) {
+      best = g;
+      best_b = b;
+    }
+  }
+  return best;
+}
+
 int igemm_stages(int loader, int tile) {
   const TileCfg& t = kTiles[tile];
   return (loader == LOAD_GENERIC || t.tco + t.tpx >= 512) ? 1 : IGEMM_STAGES;
@@ -679,7 +728,7 @@ hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const 
   const TileCfg& t = kTiles[p->tile];
   args.nco_tiles = (p->g.cout + t.tco - 1) / t.tco;
   const int npx = (p->g.m + t.tpx - 1) / t.tpx;
-  args.px_fastest = p->w_bytes > p->x_bytes;
+  args.co_group = co_group_for(p, args.nco_tiles, npx);
   args.ksplit = p->ksplit;
   args.kt_per = p->kt_per;
   args.ws = p->ws;
@@ -712,7 +761,7 @@ hipError_t launch_igemm_fused(const conv_plan* p1, const conv_plan* p2, const vo
   args.rcp_kw = 1.0f / (float)p1->g.kw;
   args.x_shift = (p1->g.ph * p1->g.w + p1->g.pw) * p1->g.c * p1->in_esz;
   args.nco_tiles = 1;
-  args.px_fastest = 0;
+  args.co_group = 1;
   args.ksplit = 1;
   args.kt_per = (p1->g.k * 2 + kBKB - 1) / kBKB;
   args.w2 = static_cast<const char*>(w2);

@@ -58,7 +58,7 @@ struct XlArgs {
   int x_bytes;
   int w_bytes;
   int x_shift;     // LOAD_TAP: bytes the x descriptor starts before x
-  int px_fastest;  // tile order: pixel tiles vary fastest (weights > activations)
+  int co_group;    // tile order: channel tiles per group, as in igemm.hip
   int ksplit;      // K-splits (gridDim.y); > 1 writes raw partial sums to ws
   int kt_per;      // K-tiles per split
   void* ws;        // [ksplit][m][cout] fp32 / int32 partial sums
@@ -127,12 +127,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int wpx = wave & 1;
 
   // XCD-aware tile order, as in igemm.hip.
-  int lin = blockIdx.x;
   const int nwg = gridDim.x;
-  if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
+  const int xcd = blockIdx.x & 7;
+  const int lin = xcd * (nwg >> 3) + min(xcd, nwg & 7) + (blockIdx.x >> 3);
   const int npx_tiles = nwg / a.nco_tiles;
-  const int co0 = (a.px_fastest ? lin / npx_tiles : lin % a.nco_tiles) * TCO;
-  const int px0 = (a.px_fastest ? lin % npx_tiles : lin / a.nco_tiles) * TPX;
+  const int span = a.co_group * npx_tiles;
+  const int grp = lin / span;
+  const int first = grp * a.co_group;
+  const int gsz = min(a.nco_tiles - first, a.co_group);
+  const int rem = lin - grp * span;
+  const int co0 = (first + rem % gsz) * TCO;
+  const int px0 = (rem / gsz) * TPX;
   const int hw_o = g.ho * g.wo;
 
   // ---- loader state: chunk j of this thread is (row tid/8 + 32 j, column tid%8)
@@ -411,7 +416,7 @@ hipError_t launch_xl(const conv_plan* p, const void* x, const void* w, const Epi
   const TileCfg& t = kXlTiles[p->tile];
   args.nco_tiles = p->g.cout / t.tco;
   const int npx = (p->g.m + t.tpx - 1) / t.tpx;
-  args.px_fastest = p->w_bytes > p->x_bytes;
+  args.co_group = co_group_for(p, args.nco_tiles, npx);
   args.ksplit = p->ksplit;
   args.kt_per = p->kt_per;
   args.ws = p->ws;

@@ -87,6 +87,7 @@ hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const 
                         hipStream_t s);
 bool xl_eligible(const Geometry& g, int esz, int loader, int tile);
 int igemm_stages(int loader, int tile);  // register stages of the implicit-GEMM kernel
+int co_group_for(const conv_plan* p, int nco, int npx);  // tile order of the implicit-GEMM kernels
 hipError_t launch_xl(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);
 hipError_t launch_igemm_fused(const conv_plan* p1, const conv_plan* p2, const void* x, const void* w1, const Epi& e1,
                               const void* w2, const Epi& e2, void* y, hipStream_t s);
