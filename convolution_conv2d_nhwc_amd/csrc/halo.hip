@@ -54,6 +54,9 @@ namespace convnhwc {
 namespace {
 
 constexpr int kPR = 4, kPC = 16;  // output patch: 4 rows x 16 columns
+#ifndef HALO_XR
+#define HALO_XR 1
+#endif
 
 template <int S>
 struct Win {
@@ -74,6 +77,7 @@ struct HaloArgs {
   int npr, npc;  // patches per image: rows, columns
   int npatch;    // n * npr * npc
   int gp;        // workgroups per channel tile
+  int xr;        // 1: each XCD walks its own contiguous range of patches (gp % 8 == 0)
   // FU
   const char* w2;
   int w2_bytes;
@@ -174,8 +178,22 @@ __global__ __launch_bounds__(TCO * 4) __attribute__((amdgpu_waves_per_eu(2))) vo
     return Origin{n, r0, c0};
   };
 
-  int p = q0;
-  Origin cur = load_window(p, 0);
+  // Patches of this workgroup: p_begin, p_begin + step, ... below p_end.
+  // Workgroups go to the 8 XCDs round-robin by id; with xr, XCD x = q0 % 8
+  // owns the contiguous range [x per, (x+1) per) of patches (per = npatch /
+  // 8 rounded up) and its gp / 8 workgroups walk it together, so the window
+  // rows that vertically and horizontally neighbouring patches share are
+  // fetched through one L2. Otherwise the workgroups stride over all patches.
+  int p_begin = q0, p_end = a.npatch, step = a.gp;
+  if (a.xr) {
+    const int per = (a.npatch + 7) >> 3;
+    const int x = q0 & 7;
+    step = a.gp >> 3;
+    p_begin = x * per + (q0 >> 3);
+    p_end = min(a.npatch, (x + 1) * per);
+  }
+  int p = p_begin;
+  Origin cur = load_window(p < p_end ? p : a.npatch, 0);
 
   // ---- this wave's weights: wa[tap][ks][i] = channel row co0 + 32 cg + 16 i
   // + (lane & 15), channels 32 ks + 8 (lane >> 4) .. +7 of tap `tap` (the
@@ -272,14 +290,14 @@ __global__ __launch_bounds__(TCO * 4) __attribute__((amdgpu_waves_per_eu(2))) vo
   // wait, are never waited for inside the loop).
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   int it = 0;
-  for (; p < a.npatch; p += a.gp, ++it) {
+  for (; p < p_end; p += step, ++it) {
     const int buf = it & 1;
     // the barrier makes everyone's copies of window p visible and frees the
     // other buffer (lgkmcnt: the first time, every wave's weight fragments
     // are out of that buffer before anyone copies a window into it)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    const Origin nxt = load_window(p + a.gp, buf ^ 1);
+    const Origin nxt = load_window(p + step < p_end ? p + step : a.npatch, buf ^ 1);
 
     acc_t acc[2][2];
 #pragma unroll
@@ -440,6 +458,13 @@ void fill_args(const conv_plan* p, const void* x, const void* w, const Epi& e, v
   a.npatch = p->g.n * a.npr * a.npc;
 }
 
+// XCD ranges of patches need every XCD to hold the same number of a channel
+// tile's workgroups.
+void set_gp(HaloArgs& a, int gp) {
+  a.gp = gp;
+  a.xr = HALO_XR && gp % 8 == 0;
+}
+
 // Workgroups per channel tile: enough to give every CU its share (two
 // workgroups of 4 waves, or one of 8, per CU), at most one per patch.
 int halo_gp(const conv_plan* p, int tco, int npatch) {
@@ -497,7 +522,7 @@ int halo_grid(const conv_plan* p, int tco) {
 hipError_t launch_halo(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s) {
   HaloArgs a;
   fill_args(p, x, w, e, y, a);
-  a.gp = halo_gp(p, 64, a.npatch);
+  set_gp(a, halo_gp(p, 64, a.npatch));
   const int nwg = a.gp * ((p->g.cout + 63) / 64);
   return dispatch(p->g.sh, p->g.c / 32, 64, 0, a, nwg, s);
 }
@@ -507,7 +532,7 @@ hipError_t launch_halo_fused(const conv_plan* p1, const conv_plan* p2, const voi
   HaloArgs a;
   fill_args(p1, x, w1, e1, y, a);
   const int tco = p1->g.cout;  // 64 or 128: the whole intermediate per workgroup
-  a.gp = halo_gp(p1, tco, a.npatch);
+  set_gp(a, halo_gp(p1, tco, a.npatch));
   a.w2 = static_cast<const char*>(w2);
   a.w2_bytes = (int)p2->w_bytes;
   a.cout2 = p2->g.cout;
