@@ -33,7 +33,9 @@ constexpr int kWR = kSR + 2, kWC = kSC + 2;      // input window (3x3, stride 1)
 constexpr int kWinPx = kWR * kWC;                // 396 pixels
 constexpr int kWinGroups = (kWinPx + 63) / 64;   // 1 KiB copies: 7
 constexpr int kStemTco = 32;                     // output channels per workgroup
-constexpr int kStemPatches = 2;                  // patches per workgroup
+#ifndef STEM_WG_PER_CU
+#define STEM_WG_PER_CU 2
+#endif
 
 struct StemArgs {
   const char* x;
@@ -60,8 +62,8 @@ __device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t r, char* lds, u
 // from its tile, rounded to bf16 (as the mosaic packer rounds) and written
 // into LDS zero-padded to 16 bytes.
 template <int MOS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void stem_window_kernel(StemArgs a) {
-  __shared__ __attribute__((aligned(1024))) char win[kStemPatches][kWinGroups * 1024];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOS ? 3 : 4))) void stem_window_kernel(StemArgs a) {
+  __shared__ __attribute__((aligned(1024))) char win[2][kWinGroups * 1024];
 
   const Geometry g = a.g;
   const int tid = threadIdx.x;
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int per_img = a.npr * a.npc;
   const int co0 = blockIdx.y * kStemTco;
-  // patch kStemPatches * blockIdx.x + t: image n, output rows r0 .., columns c0 ..
+  // patch p: image n, output rows r0 .., columns c0 ..
   auto origin = [&](int p, int& n, int& r0, int& c0) {
     n = p / per_img;
     const int rem = p - n * per_img;
@@ -78,14 +80,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     c0 = (rem - rb * a.npc) * kSC;
   };
 
-  // the windows: group k (wave k and wave k + 4) covers window pixels 64 k ..
-  // 64 k + 63, lane l pixel 64 k + l (rows of kWC pixels); both patches'
-  // windows are copied at once
+  // Start the copy of patch p's window into win[buf]. MOS 0: group k (wave k
+  // and wave k + 4) covers window pixels 64 k .. 64 k + 63, lane l pixel
+  // 64 k + l (rows of kWC pixels), copied straight into LDS. MOS 1 / 2: this
+  // thread's pixels tid and tid + 256 are gathered from their tiles into
+  // `pre` (raw fp32 / bf16 bits; zero outside the image and past c_in), and
+  // land() writes them into LDS.
   const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, a.x_bytes);
-#pragma unroll
-  for (int t = 0; t < kStemPatches; ++t) {
-    const int p = kStemPatches * blockIdx.x + t;
-    if (p >= a.npatch) break;
+  uint32_t pre[2][8];
+  auto issue = [&](int p, int buf) {
     int n, r0, c0;
     origin(p, n, r0, c0);
     const int hi0 = r0 - g.ph, wi0 = c0 - g.pw;
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
           const int hr = q / kWC, hc = q - hr * kWC;
           const int hi = hi0 + hr, wi = wi0 + hc;
           const bool ok = q < kWinPx && (unsigned)hi < (unsigned)g.h && (unsigned)wi < (unsigned)g.w;
-          dma16_lds(rx, win[t] + k * 1024, ok ? (uint32_t)(((n * g.h + hi) * g.w + wi) * 16) : kOOB);
+          dma16_lds(rx, win[buf] + k * 1024, ok ? (uint32_t)(((n * g.h + hi) * g.w + wi) * 16) : kOOB);
         }
       }
     } else {
@@ -106,28 +109,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int q = tid + 256 * i;
-        if (q < kWinPx) {
-          const int hr = q / kWC, hc = q - hr * kWC;
-          const int hi = hi0 + hr, wi = wi0 + hc;
-          const bool ok = (unsigned)hi < (unsigned)g.h && (unsigned)wi < (unsigned)g.w;
-          const int qy = hi >= a.th, qx = wi >= a.tw;
-          const int src = (((4 * n + 2 * qy + qx) * a.th + hi - qy * a.th) * a.tw + wi - qx * a.tw) * g.c;
-          uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        const int hr = q / kWC, hc = q - hr * kWC;
+        const int hi = hi0 + hr, wi = wi0 + hc;
+        const bool ok = q < kWinPx && (unsigned)hi < (unsigned)g.h && (unsigned)wi < (unsigned)g.w;
+        const int qy = hi >= a.th, qx = wi >= a.tw;
+        const int src = (((4 * n + 2 * qy + qx) * a.th + hi - qy * a.th) * a.tw + wi - qx * a.tw) * g.c;
 #pragma unroll
-          for (int ci = 0; ci < 8; ++ci)
-            if (ci < g.c) {
-              const uint32_t off = ok ? (uint32_t)(src + ci) * ESZ_IN : kOOB;
-              if constexpr (MOS == 1)
-                h[ci] = f32_to_bf16_bits(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0)));
-              else
-                h[ci] = bload_elem<2>(rx, off);
-            }
-          *reinterpret_cast<u32x4*>(win[t] + q * 16) =
-              u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        for (int ci = 0; ci < 8; ++ci) {
+          pre[i][ci] = 0;
+          if (ci < g.c) {
+            const uint32_t off = ok ? (uint32_t)(src + ci) * ESZ_IN : kOOB;
+            if constexpr (MOS == 1)
+              pre[i][ci] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0);
+            else
+              pre[i][ci] = bload_elem<2>(rx, off);
+          }
         }
       }
     }
-  }
+  };
+  // MOS 1 / 2: the gathered pixels, rounded to bf16 (as the mosaic packer
+  // rounds), into win[buf], zero-padded to 16 bytes
+  auto land = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 256 * i;
+      if (q < kWinPx) {
+        uint32_t h[8];
+#pragma unroll
+        for (int ci = 0; ci < 8; ++ci)
+          h[ci] = MOS == 1 ? (uint32_t)f32_to_bf16_bits(__builtin_bit_cast(float, pre[i][ci])) : pre[i][ci];
+        *reinterpret_cast<u32x4*>(win[buf] + q * 16) =
+            u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      }
+    }
+  };
+
+  // Patches blockIdx.x, + gridDim.x, ... (the host makes the grid no larger
+  // than the patch count); the next patch's window is copied while the
+  // current one is computed.
+  int p = blockIdx.x;
+  if (p >= a.npatch) return;
+  issue(p, 0);
+
   // A fragments: wa[ks][i] = channel row co0 + 16 i + (lane & 15), tap
   // 4 ks + (lane >> 4), its 8 channel slots (zero past c_in and past tap 8),
   // element by element from the OHWI weights (a tap's c_in values need not
@@ -163,6 +187,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   // the bias is the accumulators' starting value
   const QuadConsts qb0 = load_quad_consts_t<2>(a.e, co0 + 4 * q, g.cout);
   const QuadConsts qb1 = load_quad_consts_t<2>(a.e, co0 + 16 + 4 * q, g.cout);
+  if constexpr (MOS != 0) land(0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -172,71 +197,90 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   typedef f32x4 acc_t;
   const int pbase = (wave * kWC + (lane & 15)) * 16;
   const OutRef o = out_ref(a.y, g.m, g.cout, 2, a.e.res);
-  for (int t = 0; t < kStemPatches; ++t) {
-  const int p = kStemPatches * blockIdx.x + t;
-  if (p >= a.npatch) break;
-  int n, r0, c0;
-  origin(p, n, r0, c0);
-  acc_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const QuadConsts& qb = i ? qb1 : qb0;
-      acc[i][j] = acc_t{qb.bsf[0], qb.bsf[1], qb.bsf[2], qb.bsf[3]};
-    }
-#pragma unroll
-  for (int ks = 0; ks < 3; ++ks) {
-    const int tap = min(4 * ks + q, 8);
-    const int kh = tap / 3, kw = tap - 3 * (tap / 3);
-    const int off = pbase + (kh * kWC + kw) * 16;
-    const uint32_t* const mk = ks == 2 ? bmask2 : bmask;  // taps 0-7 always exist
-    i32x4 bf[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const i32x4 r = *reinterpret_cast<const i32x4*>(win[t] + off + j * 256);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) bf[j][d] = (int)((uint32_t)r[d] & mk[d]);
-    }
+  for (int it = 0; p < a.npatch; p += gridDim.x, ++it) {
+    const int buf = it & 1;
+    const int pn = p + gridDim.x;
+    const bool more = pn < a.npatch;  // uniform
+    // win[buf ^ 1] was last read before the previous iteration's barrier
+    if (more) issue(pn, buf ^ 1);
+    int n, r0, c0;
+    origin(p, n, r0, c0);
+    acc_t acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<2>::run(wa[ks][i], bf[j], acc[i][j]);
-  }
-
-  // epilogue: channels co0 + 16 i + 4 (lane >> 4) .. +3 of pixel (r0 + wave,
-  // c0 + 16 j + (lane & 15)). (Restaging the tile through LDS so that every
-  // store is a 16-byte piece of a 1 KiB run measured no faster.)
-  const int r = r0 + wave;
-  // act(acc) [+ residual], bf16, one 8-byte store per quad (the bias is
-  // already in acc)
-  with_epilogue<2>(OUT_BF16, a.e.act, [&](auto, auto ac) {
-    constexpr int ACT = decltype(ac)::value;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = c0 + 16 * j + (lane & 15);
-      const bool pin = r < g.ho && c < g.wo;
-      const int px = pin ? (n * g.ho + r) * g.wo + c : 0;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int co = co0 + 16 * i + 4 * q;
-        const bool in = pin && co < g.cout;
-        const uint32_t off = in ? (uint32_t)(px * g.cout + co) * 2u : kOOB;
-        float f[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = act_t<ACT>(acc[i][j][e]);
-        if (o.has_res) {
-          const u32x2 rv = __builtin_amdgcn_raw_buffer_load_b64(o.rr, off, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) f[e] += bf16_bits_to_f32((e & 1) ? (rv[e >> 1] >> 16) : (rv[e >> 1] & 0xffffu));
-        }
-        const u32x2 d = {(uint32_t)f32_to_bf16_bits(f[0]) | ((uint32_t)f32_to_bf16_bits(f[1]) << 16),
-                         (uint32_t)f32_to_bf16_bits(f[2]) | ((uint32_t)f32_to_bf16_bits(f[3]) << 16)};
-        __builtin_amdgcn_raw_buffer_store_b64(d, o.r, off, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const QuadConsts& qb = i ? qb1 : qb0;
+        acc[i][j] = acc_t{qb.bsf[0], qb.bsf[1], qb.bsf[2], qb.bsf[3]};
       }
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      const int tap = min(4 * ks + q, 8);
+      const int kh = tap / 3, kw = tap - 3 * (tap / 3);
+      const int off = pbase + (kh * kWC + kw) * 16;
+      const uint32_t* const mk = ks == 2 ? bmask2 : bmask;  // taps 0-7 always exist
+      i32x4 bf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const i32x4 r = *reinterpret_cast<const i32x4*>(win[buf] + off + j * 256);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) bf[j][d] = (int)((uint32_t)r[d] & mk[d]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<2>::run(wa[ks][i], bf[j], acc[i][j]);
     }
-  });
+
+    // epilogue: channels co0 + 16 i + 4 (lane >> 4) .. +3 of pixel (r0 +
+    // wave, c0 + 16 j + (lane & 15)): act(acc) [+ residual], bf16, one 8-byte
+    // store per quad (the bias is already in acc). Every quad is computed
+    // before the next window is landed and before any store, so the window
+    // copy has the MFMAs and the activations to complete. (Restaging the
+    // tile through LDS so that every store is a 16-byte piece of a 1 KiB run
+    // measured no faster.)
+    const int r = r0 + wave;
+    // byte offset of quad (j, i) in y, or past every tensor
+    auto out_off = [&](int j, int i) {
+      const int c = c0 + 16 * j + (lane & 15);
+      const int co = co0 + 16 * i + 4 * q;
+      const bool in = r < g.ho && c < g.wo && co < g.cout;
+      return in ? (uint32_t)((((n * g.ho + r) * g.wo + c) * g.cout + co) * 2) : kOOB;
+    };
+    u32x2 d[4][2];
+    with_epilogue<2>(OUT_BF16, a.e.act, [&](auto, auto ac) {
+      constexpr int ACT = decltype(ac)::value;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          float f[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] = act_t<ACT>(acc[i][j][e]);
+          if (o.has_res) {
+            const u32x2 rv = __builtin_amdgcn_raw_buffer_load_b64(o.rr, out_off(j, i), 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[e] += bf16_bits_to_f32((e & 1) ? (rv[e >> 1] >> 16) : (rv[e >> 1] & 0xffffu));
+          }
+          d[j][i] = u32x2{(uint32_t)f32_to_bf16_bits(f[0]) | ((uint32_t)f32_to_bf16_bits(f[1]) << 16),
+                          (uint32_t)f32_to_bf16_bits(f[2]) | ((uint32_t)f32_to_bf16_bits(f[3]) << 16)};
+        }
+      }
+    });
+    if constexpr (MOS != 0) {
+      if (more) land(buf ^ 1);
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next window has landed
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b64(d[j][i], o.r, out_off(j, i), 0, 0);
+    // the next window is visible to every wave, and win[buf] is free
+    __syncthreads();
   }
+  // no copy into LDS is left in flight when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace
@@ -250,9 +294,12 @@ bool stem_mosaic_ok(const conv_plan* p, int64_t th, int64_t tw) {
   return p->path == PATH_STEM && th > 0 && tw > 0 && p->g.h == 2 * th && p->g.w == 2 * tw;
 }
 
+// Persistent grid: STEM_WG_PER_CU workgroups per CU for each 32-channel
+// tile, at most one per patch.
 int stem_grid(const conv_plan* p) {
   const int npatch = p->g.n * ((p->g.ho + kSR - 1) / kSR) * ((p->g.wo + kSC - 1) / kSC);
-  return (npatch + kStemPatches - 1) / kStemPatches;
+  const int nct = (p->g.cout + kStemTco - 1) / kStemTco;
+  return std::max(1, std::min(npatch, STEM_WG_PER_CU * p->cus / nct));
 }
 
 hipError_t launch_stem(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s) {
