@@ -177,11 +177,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOS ? 3 : 4
       }
   }
   // B masks: the channel slots c_in .. 7 of an input pixel read as zero
-  // (tap slots past the ninth: all zero)
+  // (tap slots past the ninth: all zero). The mosaic modes write those slots
+  // as zeros into LDS, so only the tap mask remains.
   uint32_t bmask[4], bmask2[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    bmask[d] = (2 * d < g.c ? 0xffffu : 0u) | (2 * d + 1 < g.c ? 0xffff0000u : 0u);
+    bmask[d] = MOS != 0 || 2 * d < g.c ? 0xffffu : 0u;
+    bmask[d] |= MOS != 0 || 2 * d + 1 < g.c ? 0xffff0000u : 0u;
     bmask2[d] = 8 + q < 9 ? bmask[d] : 0u;
   }
   // the bias is the accumulators' starting value
@@ -219,12 +221,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOS ? 3 : 4
       const int kh = tap / 3, kw = tap - 3 * (tap / 3);
       const int off = pbase + (kh * kWC + kw) * 16;
       const uint32_t* const mk = ks == 2 ? bmask2 : bmask;  // taps 0-7 always exist
+      const bool masked = MOS == 0 || ks == 2;
       i32x4 bf[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const i32x4 r = *reinterpret_cast<const i32x4*>(win[buf] + off + j * 256);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) bf[j][d] = (int)((uint32_t)r[d] & mk[d]);
+        for (int d = 0; d < 4; ++d) bf[j][d] = masked ? (int)((uint32_t)r[d] & mk[d]) : r[d];
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -240,12 +243,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOS ? 3 : 4
     // tile through LDS so that every store is a 16-byte piece of a 1 KiB run
     // measured no faster.)
     const int r = r0 + wave;
-    // byte offset of quad (j, i) in y, or past every tensor
-    auto out_off = [&](int j, int i) {
-      const int c = c0 + 16 * j + (lane & 15);
-      const int co = co0 + 16 * i + 4 * q;
-      const bool in = r < g.ho && c < g.wo && co < g.cout;
-      return in ? (uint32_t)((((n * g.ho + r) * g.wo + c) * g.cout + co) * 2) : kOOB;
+    // quad (j, i) of this lane lies at byte offset base + soff(j, i) in y
+    // (soff uniform); a quad outside y goes to an offset past every tensor
+    const int base = (((n * g.ho + r) * g.wo + c0 + (lane & 15)) * g.cout + co0 + 4 * q) * 2;
+    auto soff = [&](int j, int i) { return (16 * j * g.cout + 16 * i) * 2; };
+    auto voff = [&](int j, int i) {
+      const bool in = r < g.ho && c0 + 16 * j + (lane & 15) < g.wo && co0 + 16 * i + 4 * q < g.cout;
+      return in ? (uint32_t)base : kOOB;
     };
     u32x2 d[4][2];
     with_epilogue<2>(OUT_BF16, a.e.act, [&](auto, auto ac) {
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOS ? 3 : 4
 #pragma unroll
           for (int e = 0; e < 4; ++e) f[e] = act_t<ACT>(acc[i][j][e]);
           if (o.has_res) {
-            const u32x2 rv = __builtin_amdgcn_raw_buffer_load_b64(o.rr, out_off(j, i), 0, 0);
+            const u32x2 rv = __builtin_amdgcn_raw_buffer_load_b64(o.rr, voff(j, i), soff(j, i), 0);
 #pragma unroll
             for (int e = 0; e < 4; ++e) f[e] += bf16_bits_to_f32((e & 1) ? (rv[e >> 1] >> 16) : (rv[e >> 1] & 0xffffu));
           }
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOS ? 3 : 4
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b64(d[j][i], o.r, out_off(j, i), 0, 0);
+      for (int i = 0; i < 2; ++i) __builtin_amdgcn_raw_buffer_store_b64(d[j][i], o.r, voff(j, i), soff(j, i), 0);
     // the next window is visible to every wave, and win[buf] is free
     __syncthreads();
   }
