@@ -160,6 +160,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Two floats to a packed pair of bf16 (lo in the low half), each rounded to
+// nearest even exactly as f32_to_bf16_bits rounds it: one v_cvt_pk_bf16_f32
+// for the pair.
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }

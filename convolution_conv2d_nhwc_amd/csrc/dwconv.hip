@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void dw3x3_kernel(DwArgs a) {
           uint32_t wd[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            wd[q] = (uint32_t)f32_to_bf16_bits(v[2 * q]) | ((uint32_t)f32_to_bf16_bits(v[2 * q + 1]) << 16);
+            wd[q] = bf16x2_bits(v[2 * q], v[2 * q + 1]);
           *reinterpret_cast<i32x4*>(yp) = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
         } else {
 #pragma unroll
@@ -343,13 +343,6 @@ __device__ __forceinline__ typename Elt<T>::acc_t widen_word(uint32_t wd, int e)
   }
 }
 
-// two floats to a packed pair of bf16 (round to nearest even), one instruction
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 h = __builtin_convertvector((f32x2{lo, hi}), bf16x2);
-  return __builtin_bit_cast(uint32_t, h);
-}
 
 // Lane decomposition shared by the row-window kernels: channel vector
 // fastest, then the group of PW columns, then the block of TH rows, then the
@@ -511,7 +504,7 @@ __global__ __launch_bounds__(256) void dw3x3_rows_kernel(DwArgs a) {
         }
         uint32_t wd[VE / 2];
 #pragma unroll
-        for (int q = 0; q < VE / 2; ++q) wd[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+        for (int q = 0; q < VE / 2; ++q) wd[q] = bf16x2_bits(v[2 * q], v[2 * q + 1]);
         if constexpr (VE == 8)
           __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]}, ry, (int)off, 0, DW_ST_AUX);
         else

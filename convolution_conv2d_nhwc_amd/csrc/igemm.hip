@@ -521,11 +521,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
 #pragma unroll
         for (int j = 0; j < FPX; ++j) {
           const int row = wpx * (TPX / WPX) + (lane & 15) + 16 * j;
-          uint32_t h[4];
+          float f[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_bits(act_t<ACT>(acc[i][j][r] + q.bsf[r]));
+          for (int r = 0; r < 4; ++r) f[r] = act_t<ACT>(acc[i][j][r] + q.bsf[r]);
           *reinterpret_cast<u32x2*>(Y + (col >> 6) * TPX * kBKB + lds_off(row, (col & 63) >> 3) + (col & 4) * 2) =
-              u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+              u32x2{bf16x2_bits(f[0], f[1]), bf16x2_bits(f[2], f[3])};
         }
       }
     });

@@ -208,10 +208,7 @@ __device__ __forceinline__ u32x2 pack_quad_bf16(const f32x4& v, const QuadConsts
 #pragma unroll
     for (int r = 0; r < 4; ++r) f[r] += bf16_bits_to_f32((r & 1) ? (rv[r >> 1] >> 16) : (rv[r >> 1] & 0xffffu));
   }
-  uint32_t h[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_bits(f[r]);
-  return u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  return u32x2{bf16x2_bits(f[0], f[1]), bf16x2_bits(f[2], f[3])};
 }
 
 // Store quad v (channels co..co+3 of pixel px); nothing is written when
@@ -230,10 +227,7 @@ __device__ __forceinline__ void store_quad_t(const acc_t& v, const QuadConsts& q
 #pragma unroll
       for (int r = 0; r < 4; ++r) f[r] += bf16_bits_to_f32((r & 1) ? (rv[r >> 1] >> 16) : (rv[r >> 1] & 0xffffu));
     }
-    uint32_t h[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_bits(f[r]);
-    const u32x2 d = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    const u32x2 d = {bf16x2_bits(f[0], f[1]), bf16x2_bits(f[2], f[3])};
     __builtin_amdgcn_raw_buffer_store_b64(d, o.r, in ? idx * 2u : kNowhere, 0, 0);
   } else if constexpr (OUT == OUT_I32) {
     u32x4 d;

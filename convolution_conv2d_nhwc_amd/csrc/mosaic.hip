@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void mosaic_vec8_kernel(MosArgs a) {
   } else {
     uint32_t wd[4];
     for (int q = 0; q < 4; ++q)
-      wd[q] = (uint32_t)f32_to_bf16_bits(v[2 * q]) | ((uint32_t)f32_to_bf16_bits(v[2 * q + 1]) << 16);
+      wd[q] = bf16x2_bits(v[2 * q], v[2 * q + 1]);
     *reinterpret_cast<i32x4*>(reinterpret_cast<uint16_t*>(a.canvas) + dst) =
         i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
   }

@@ -135,12 +135,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOS ? 3 : 4
     for (int i = 0; i < 2; ++i) {
       const int q = tid + 256 * i;
       if (q < kWinPx) {
-        uint32_t h[8];
+        uint32_t h[4];
 #pragma unroll
-        for (int ci = 0; ci < 8; ++ci)
-          h[ci] = MOS == 1 ? (uint32_t)f32_to_bf16_bits(__builtin_bit_cast(float, pre[i][ci])) : pre[i][ci];
-        *reinterpret_cast<u32x4*>(win[buf] + q * 16) =
-            u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        for (int k = 0; k < 4; ++k)
+          h[k] = MOS == 1 ? bf16x2_bits(__builtin_bit_cast(float, pre[i][2 * k]), __builtin_bit_cast(float, pre[i][2 * k + 1]))
+                          : pre[i][2 * k] | (pre[i][2 * k + 1] << 16);
+        *reinterpret_cast<u32x4*>(win[buf] + q * 16) = u32x4{h[0], h[1], h[2], h[3]};
       }
     }
   };
@@ -266,8 +266,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOS ? 3 : 4
 #pragma unroll
             for (int e = 0; e < 4; ++e) f[e] += bf16_bits_to_f32((e & 1) ? (rv[e >> 1] >> 16) : (rv[e >> 1] & 0xffffu));
           }
-          d[j][i] = u32x2{(uint32_t)f32_to_bf16_bits(f[0]) | ((uint32_t)f32_to_bf16_bits(f[1]) << 16),
-                          (uint32_t)f32_to_bf16_bits(f[2]) | ((uint32_t)f32_to_bf16_bits(f[3]) << 16)};
+          d[j][i] = u32x2{bf16x2_bits(f[0], f[1]), bf16x2_bits(f[2], f[3])};
         }
       }
     });
