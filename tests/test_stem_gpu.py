@@ -7,9 +7,10 @@ The input handed to the kernel is the dense NHWC tensor with channels c_in
 reached a sum would show up as a non-finite output). The oracle runs the
 dense layer; every output is compared under the bf16 rule. Cases: 1, 3, 5 and
 8 input channels, ragged patch rows and columns, several images, a partial
-32-channel tile, pad 0 and 1, every activation, a residual; the 640x640x3 ->
-32 stem of the YOLO stack at full size on sampled outputs (plus one full
-band of rows element by element).
+32-channel tile, pad 0 and 1, every activation, a residual, more patches than the
+persistent grid holds (a workgroup walks two); the 640x640x3 -> 32 stem of
+the YOLO stack at full size on sampled outputs (plus one full band of rows
+element by element).
 """
 import numpy as np
 import pytest
@@ -99,6 +100,26 @@ def test_stem_yolo640_full_size():
     rb, ab = H.oracle_full(band, xb, t)
     # output rows 301..306 depend only on input rows 300..307
     H.check_float(y[:, 301:307].float().numpy(), rb[:, 1:7], ab[:, 1:7], "bf16", "stem band rows 301-306")
+
+
+def test_stem_several_patches_per_workgroup():
+    """More patches than the persistent grid holds (two workgroups per CU),
+    with ragged patch rows and columns: workgroups walk two patches, the
+    second window copied during the first patch; every output against the
+    oracle, and the folded-mosaic form of the same layer bit-equal to it."""
+    layer = L("st_multi_ragged", 1, 130, 1000, 3, 32)
+    t = random_layer_tensors(layer, "bf16", seed=89)
+    print("stem", layer.name, flush=True)
+    y, d = run_stem(layer, t)
+    H.check_layer_full(layer, t["x"], t, y, "%s [%s]" % (layer.name, d))
+    # the same canvas as four 65 x 500 bf16 tiles
+    x = t["x"][0]
+    tiles = torch.stack([x[:65, :500], x[:65, 500:], x[65:, :500], x[65:, 500:]]).contiguous()
+    conv = _lib.Conv2d.from_layer(layer, x_stride=8)
+    ym = _lib.run_mosaic(conv, tiles.cuda(), t["w"].cuda(), t["b"].cuda())
+    torch.cuda.synchronize()
+    conv.close()
+    assert torch.equal(ym.cpu().view(torch.int16), y.view(torch.int16)), "folded mosaic vs padded canvas"
 
 
 def _mosaic_layer(name, m, th, tw, c, cout, act):
