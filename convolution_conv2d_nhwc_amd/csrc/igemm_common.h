@@ -14,6 +14,7 @@ namespace {
 
 constexpr int kBKB = 128;         // bytes of K per tile row
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past any tensor: reads 0
+constexpr int kMaxSplits = 8;     // split-K: at most this many K ranges (plan_split_k)
 
 
 template <int ESZ>
@@ -89,8 +90,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const void* ws, int 
   with_epilogue<ESZ>(out_kind, e.act, [&](auto oc, auto ac) {
     constexpr int OUT = decltype(oc)::value, ACT = decltype(ac)::value;
     for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (long)gridDim.x * blockDim.x) {
-      acc_t acc = w[q];
-      for (int s = 1; s < ksplit; ++s) acc += w[(size_t)s * total + q];
+      // every split's quad is loaded before the first add (one memory
+      // latency, not ksplit of them); the adds keep split order
+      acc_t part[kMaxSplits];
+#pragma unroll
+      for (int s = 0; s < kMaxSplits; ++s)
+        if (s < ksplit) part[s] = w[(size_t)s * total + q];
+      acc_t acc = part[0];
+#pragma unroll
+      for (int s = 1; s < kMaxSplits; ++s)
+        if (s < ksplit) acc += part[s];
       const int px = (int)(q / nq);
       const int co = (int)(q - (long)px * nq) * 4;
       store_quad_t<ESZ, OUT, ACT>(acc, load_quad_consts_t<ESZ>(e, co, cout), co, px, o);
@@ -103,6 +112,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const void* ws, int 
 // The K-split partial sums [ksplit][m][cout] of plan p summed in split order,
 // then the fused epilogue into y.
 inline hipError_t launch_splitk_reduce(const conv_plan* p, const Epi& e, void* y, hipStream_t s) {
+  if (p->ksplit > kMaxSplits) return hipErrorInvalidValue;  // plan_split_k never makes more
   const long quads = (long)p->g.m * (p->g.cout / 4);
   const int blocks = (int)std::min<long>((quads + 255) / 256, 256L * 8);
   if (p->in_esz == 2)
