@@ -8,7 +8,8 @@ implicit-GEMM kernel.
   bit; the halo output is also checked against the oracle's fp64 result
   under the bf16 rule (every element). Cases: both strides and channel
   counts, ragged patch rows and columns, several images, two channel tiles
-  with a partial one, pad 0 and 2, a residual, no bias, every activation.
+  with a partial one, pad 0 and 2, a residual, no bias, every activation,
+  more patches than workgroups with some workgroups left without a patch.
 * The 320x320x64 -> 64 layer of the 640x640 stack at full size (bit-equal to
   the implicit-GEMM kernel, plus sampled outputs against the oracle) and its
   160x160x64 -> 256 stride-2 layer.
@@ -62,6 +63,9 @@ CASES = [
     L("h_s1_pad0", 1, 18, 18, 64, 64, p=0),
     L("h_s1_pad2_c32", 2, 9, 17, 32, 40, p=2, act="relu"),
     L("h_s2_pad0_n3", 3, 12, 15, 64, 64, s=2, p=0),
+    # 513 patches for 512 workgroups: the last XCD's range is shorter than
+    # its workgroup count, so some workgroups get no patch
+    L("h_s1_xcd_ranges_empty", 1, 36, 912, 64, 64, act="relu"),
 ]
 
 
@@ -117,6 +121,9 @@ PAIRS = [
     pair("hf_s2_c32_64to64", 2, 19, 36, 32, 64, 64, s=2, act1="relu", act2="relu6"),
     pair("hf_s2_c64_128to64", 1, 21, 33, 64, 128, 64, s=2),
     pair("hf_s1_c32_128to60", 1, 9, 20, 32, 128, 60, act1="none", act2="relu"),
+    # 261 patches for 256 workgroups (one per CU with 128 channels): empty
+    # XCD ranges in the fused launch
+    pair("hf_s1_c64_128to64_xcd", 1, 36, 464, 64, 128, 64),
 ]
 
 
