@@ -94,6 +94,8 @@ def lib():
     L.conv_run_fused.restype = ctypes.c_int
     L.conv_run_mosaic.argtypes = [P, P, I32, I32, I32, P, P, P, P]
     L.conv_run_mosaic.restype = ctypes.c_int
+    L.conv_run_upcat.argtypes = [P, P, I32, I32, P, I32, P, P, P, P]
+    L.conv_run_upcat.restype = ctypes.c_int
     L.conv_bfp8_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
     L.conv_bfp8_bytes.restype = ctypes.c_int64
     L.conv_pack_bfp8.argtypes = [P, I32, ctypes.c_int64, ctypes.c_int64, P, P]
@@ -420,4 +422,26 @@ def run_mosaic(conv: Conv2d, tiles: torch.Tensor, w: torch.Tensor, b: Optional[t
                                th, tw, w.data_ptr(), None if b is None else b.data_ptr(), y.data_ptr(),
                                _stream_handle(stream))
     _check(st, "conv_run_mosaic")
+    return y
+
+
+def run_upcat(conv: Conv2d, s0: torch.Tensor, up0: int, s1: torch.Tensor, up1: int, w: torch.Tensor,
+              b: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """conv (a 1x1 layer) applied to the channel concat of s0 and s1, each
+    repeated 2x in rows and columns when its up flag is 1, without writing
+    the joined map (conv_run_upcat)."""
+    n, h, wd, c = conv.in_shape
+    dt = TORCH_DT[conv.dtype]
+    c0 = s0.shape[-1] if s0.dim() == 4 else -1
+    conv._chk(s0, "s0", dt, (n, h >> up0, wd >> up0, c0))
+    conv._chk(s1, "s1", dt, (n, h >> up1, wd >> up1, c - c0))
+    conv._chk(w, "w", conv._w_dtype(), conv.w_shape)
+    if b is not None:
+        conv._chk(b, "b", torch.int32 if conv.dtype == "i8" else torch.float32, None)
+    if y is None:
+        y = conv.empty_output(s0.device)
+    conv._chk(y, "y", TORCH_DT[conv.out_dtype], conv.out_shape)
+    st = lib().conv_run_upcat(conv._plan, s0.data_ptr(), c0, up0, s1.data_ptr(), up1, w.data_ptr(),
+                              None if b is None else b.data_ptr(), y.data_ptr(), _stream_handle(stream))
+    _check(st, "conv_run_upcat")
     return y

@@ -555,6 +555,45 @@ conv_status conv_run_mosaic(const conv_plan* p, const void* tiles, int32_t tiles
   return CONV_OK;
 }
 
+conv_status conv_run_upcat(const conv_plan* p, const void* s0, int32_t c0, int32_t up0, const void* s1, int32_t up1,
+                           const void* w, const void* b, void* y, void* stream) {
+  if (!p || !s0 || !s1 || !w || !y) return CONV_E_NULL;
+  const conv_desc& d = p->d;
+  if ((d.dtype != CONV_BF16 && d.dtype != CONV_I8) || d.groups != 1 || d.kh != 1 || d.kw != 1 || d.stride_h != 1 ||
+      d.stride_w != 1 || d.pad_h != 0 || d.pad_w != 0 || p->wq)
+    return CONV_E_UNSUPPORTED;
+  if ((up0 != 0 && up0 != 1) || (up1 != 0 && up1 != 1)) return CONV_E_SHAPE;
+  if ((up0 || up1) && ((p->g.h & 1) || (p->g.w & 1))) return CONV_E_SHAPE;
+  if (c0 <= 0 || c0 >= p->g.c) return CONV_E_SHAPE;
+  const int esz = p->in_esz;
+  const int c0b = c0 * esz, c1b = (p->g.c - c0) * esz;
+  if (c0b % 128 || c1b % 128) return CONV_E_UNSUPPORTED;  // each 128-byte K-tile inside one map
+  const bool i8out = d.dtype == CONV_I8 && d.out_dtype == CONV_I8;
+  if (i8out && !b) return CONV_E_NULL;
+  if (((uintptr_t)s0 | (uintptr_t)s1 | (uintptr_t)w | (uintptr_t)y) & 15) return CONV_E_ALIGN;
+  if ((uintptr_t)b & 3) return CONV_E_ALIGN;
+  const int64_t s0_bytes = (int64_t)p->g.n * (p->g.h >> up0) * (p->g.w >> up0) * c0b;
+  const int64_t s1_bytes = (int64_t)p->g.n * (p->g.h >> up1) * (p->g.w >> up1) * c1b;
+  if (ranges_overlap(y, p->y_bytes, s0, s0_bytes) || ranges_overlap(y, p->y_bytes, s1, s1_bytes) ||
+      ranges_overlap(y, p->y_bytes, w, p->w_bytes) || ranges_overlap(y, p->y_bytes, b, p->b_bytes))
+    return CONV_E_ALIAS;
+  Epi e;
+  std::memset(&e, 0, sizeof(e));
+  e.act = d.act;
+  if (d.dtype == CONV_I8) {
+    e.ibias = static_cast<const int32_t*>(b);
+    e.scale = i8out && b ? reinterpret_cast<const float*>(static_cast<const int32_t*>(b) + d.c_out) : nullptr;
+  } else {
+    e.bias = static_cast<const float*>(b);
+  }
+  const hipError_t err = launch_igemm_cat(p, s0, c0b, up0, s1, up1, w, e, y, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(err));
+    return CONV_E_HIP;
+  }
+  return CONV_OK;
+}
+
 conv_status conv_destroy(conv_plan* p) {
   if (p && p->ws && p->ws_owned) {
     int cur = 0;

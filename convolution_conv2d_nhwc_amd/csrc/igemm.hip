@@ -75,6 +75,13 @@ struct IgArgs {
   int w2_bytes;
   int cout2;       // <= 64, a multiple of 4
   Epi e2;          // its bias and activation
+  // LOAD_CAT: the input is the channel concat of x (c0b bytes per pixel) and
+  // x2 (the other g.c * ESZ - c0b), each at half resolution when its up flag
+  // is set
+  const char* x2;
+  int x2_bytes;
+  int c0b;
+  int up0, up1;
 };
 
 // bfp8 weights (WQ): eight consecutive mantissas of one block (two dwords)
@@ -133,6 +140,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
   const int wpx = wave % WPX;
   const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t rw = rsrc(a.w, a.w_bytes);
+  const __amdgpu_buffer_rsrc_t rx2 = rsrc(LOADER == LOAD_CAT ? a.x2 : a.x, LOADER == LOAD_CAT ? a.x2_bytes : 0);
 
   // Tiles are handed to the 8 XCDs round-robin by workgroup id; remap so each
   // XCD (own L2) gets a contiguous run of tiles: XCD x = id % 8 takes the
@@ -174,6 +182,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
         b_base[j] = p * g.c;
         b_hi0[j] = 0;
         b_wi0[j] = 0;
+      } else if constexpr (LOADER == LOAD_CAT) {
+        // pixel index of (n, ho, wo) in each map (b_base: x, b_wi0: x2)
+        const int h0 = g.h >> a.up0, w0 = g.w >> a.up0, h1 = g.h >> a.up1, w1 = g.w >> a.up1;
+        b_base[j] = (n * h0 + (ho >> a.up0)) * w0 + (wo >> a.up0);
+        b_wi0[j] = (n * h1 + (ho >> a.up1)) * w1 + (wo >> a.up1);
+        b_hi0[j] = 0;
       } else {
         const int hi0 = ho * g.sh - g.ph;
         const int wi0 = wo * g.sw - g.pw;
@@ -207,6 +221,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
     t_cb = kb0 - tap0 * cbytes;
     t_kh = tap0 / g.kw;
     t_kw = tap0 - t_kh * g.kw;
+  }
+  uint32_t voff_b2[LOADER == LOAD_CAT ? BCH : 1];
+  if constexpr (LOADER == LOAD_CAT) {
+    const int c16 = (tid & 7) * 16;
+    const int c1b = cbytes - a.c0b;
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) {
+      const int co = co0 + (tid >> 3) + 32 * j;
+      voff_a[j] = co < g.cout ? (uint32_t)(co * g.k * ESZ + c16) : kOOB;
+    }
+#pragma unroll
+    for (int j = 0; j < BCH; ++j) {
+      voff_b[j] = b_hi0[j] == 0 ? (uint32_t)(b_base[j] * a.c0b + c16) : kOOB;
+      voff_b2[j] = b_hi0[j] == 0 ? (uint32_t)(b_wi0[j] * c1b + c16) : kOOB;
+    }
   }
   if constexpr (LOADER == LOAD_TAP || LOADER == LOAD_1X1) {
     const int c16 = (tid & 7) * 16;
@@ -348,6 +377,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IGEMM_WPE))
           t_kw = 0;
           ++t_kh;
         }
+      }
+    } else if constexpr (LOADER == LOAD_CAT) {
+      // K = Cin; K-tile kt lies in x (kt * 128 < c0b) or in x2, whole (both
+      // parts are multiples of 128 bytes); tiles past K read zeros
+      const int soff = kt * kBKB;
+      const bool live = kt < nkt_all;
+      const bool second = soff >= a.c0b;
+      const int so = second ? soff - a.c0b : soff;
+#pragma unroll
+      for (int j = 0; j < ACH; ++j) ra[j] = bload16s(rw, live ? voff_a[j] : kOOB, live ? soff : 0);
+      if (second) {
+#pragma unroll
+        for (int j = 0; j < BCH; ++j) rb[j] = bload16s(rx2, live ? voff_b2[j] : kOOB, live ? so : 0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < BCH; ++j) rb[j] = bload16s(rx, live ? voff_b[j] : kOOB, live ? so : 0);
       }
     } else if constexpr (LOADER == LOAD_1X1) {
       // K = Cin: chunk c of tile kt is valid while kt*128 + 16c < Cin*ESZ.
@@ -656,6 +701,29 @@ hipError_t launch_esz(int tile, int loader, const IgArgs& args, dim3 nwg, hipStr
   }
 }
 
+template <int ESZ>
+hipError_t launch_cat_esz(int tile, const IgArgs& args, dim3 nwg, hipStream_t s) {
+  switch (tile) {
+    case 0:
+      hipLaunchKernelGGL((igemm_kernel<ESZ, 64, 64, 2, 2, LOAD_CAT, kStages<LOAD_CAT, 64, 64>, 0, 0>), nwg, dim3(256), 0,
+                         s, args);
+      break;
+    case 1:
+      hipLaunchKernelGGL((igemm_kernel<ESZ, 128, 128, 2, 2, LOAD_CAT, kStages<LOAD_CAT, 128, 128>, 0, 0>), nwg,
+                         dim3(256), 0, s, args);
+      break;
+    case 2:
+      hipLaunchKernelGGL((igemm_kernel<ESZ, 64, 128, 2, 2, LOAD_CAT, kStages<LOAD_CAT, 64, 128>, 0, 0>), nwg, dim3(256),
+                         0, s, args);
+      break;
+    default:
+      hipLaunchKernelGGL((igemm_kernel<ESZ, 128, 64, 2, 2, LOAD_CAT, kStages<LOAD_CAT, 128, 64>, 0, 0>), nwg, dim3(256),
+                         0, s, args);
+      break;
+  }
+  return hipGetLastError();
+}
+
 template <int TCO, int LOADER>
 hipError_t launch_fused_tile(const IgArgs& args, dim3 nwg, hipStream_t s) {
   hipLaunchKernelGGL((igemm_kernel<2, TCO, 64, 2, 2, LOADER, kStages<LOADER, TCO, 64>, 0, 1>), dim3(nwg), dim3(256), 0,
@@ -740,6 +808,38 @@ hipError_t launch_igemm(const conv_plan* p, const void* x, const void* w, const 
                                   : launch_esz<2, 0>(p->tile, p->loader, args, grid, s);
   if (err != hipSuccess || p->ksplit == 1) return err;
   return launch_splitk_reduce(p, e, y, s);
+}
+
+int cat_tile(const conv_plan* p) { return p->path == PATH_IGEMM ? p->tile : 0; }
+
+hipError_t launch_igemm_cat(const conv_plan* p, const void* s0, int c0b, int up0, const void* s1, int up1,
+                            const void* w, const Epi& e, void* y, hipStream_t s) {
+  IgArgs args;
+  std::memset(&args, 0, sizeof(args));
+  const Geometry& g = p->g;
+  const int c1b = g.c * p->in_esz - c0b;
+  args.x = static_cast<const char*>(s0);
+  args.x_bytes = (int)((int64_t)g.n * (g.h >> up0) * (g.w >> up0) * c0b);
+  args.x2 = static_cast<const char*>(s1);
+  args.x2_bytes = (int)((int64_t)g.n * (g.h >> up1) * (g.w >> up1) * c1b);
+  args.c0b = c0b;
+  args.up0 = up0;
+  args.up1 = up1;
+  args.w = static_cast<const char*>(w);
+  args.y = y;
+  args.e = e;
+  args.g = g;
+  args.out_kind = p->out_kind;
+  args.w_bytes = (int)p->w_bytes;
+  const int tile = cat_tile(p);
+  const TileCfg& t = kTiles[tile];
+  args.nco_tiles = (g.cout + t.tco - 1) / t.tco;
+  const int npx = (g.m + t.tpx - 1) / t.tpx;
+  args.co_group = co_group_for(p, args.nco_tiles, npx);
+  args.ksplit = 1;
+  args.kt_per = (g.k * p->in_esz + kBKB - 1) / kBKB;
+  const dim3 grid(npx * args.nco_tiles, 1);
+  return p->in_esz == 1 ? launch_cat_esz<1>(tile, args, grid, s) : launch_cat_esz<2>(tile, args, grid, s);
 }
 
 // p1's layer with p2's 1x1 layer applied to each output tile before any

@@ -25,8 +25,10 @@ enum Loader {
   LOAD_GENERIC = 0,  // element-wise gather: any channel count
   LOAD_VEC = 1,      // 16-byte channel vectors: c_in * elem_size % 16 == 0
   LOAD_1X1 = 2,      // 1x1, stride 1, pad 0: the input is the GEMM operand
-  LOAD_TAP = 3       // Cin * elem_size % 128 == 0 and KH*KW <= 32: every K-tile
+  LOAD_TAP = 3,      // Cin * elem_size % 128 == 0 and KH*KW <= 32: every K-tile
                      // lies in one tap, so the tap offset is wave-uniform
+  LOAD_CAT = 4       // 1x1 over the channel concat of two maps, each optionally
+                     // upsampled x2 (conv_run_upcat): every K-tile lies in one map
 };
 
 // One tile configuration of the implicit-GEMM kernel: a workgroup of four
@@ -89,6 +91,11 @@ bool xl_eligible(const Geometry& g, int esz, int loader, int tile);
 int igemm_stages(int loader, int tile);  // register stages of the implicit-GEMM kernel
 int co_group_for(const conv_plan* p, int nco, int npx);  // tile order of the implicit-GEMM kernels
 hipError_t launch_xl(const conv_plan* p, const void* x, const void* w, const Epi& e, void* y, hipStream_t s);
+// p's 1x1 layer over the concat of s0 (c0b bytes per pixel, upsampled x2
+// when up0) and s1 (the rest of the channels, upsampled when up1), unsplit,
+// on p's implicit-GEMM tile when p has one, else the 64x64 tile.
+hipError_t launch_igemm_cat(const conv_plan* p, const void* s0, int c0b, int up0, const void* s1, int up1,
+                            const void* w, const Epi& e, void* y, hipStream_t s);
 hipError_t launch_igemm_fused(const conv_plan* p1, const conv_plan* p2, const void* x, const void* w1, const Epi& e1,
                               const void* w2, const Epi& e2, void* y, hipStream_t s);
 int ws_ksteps(const Geometry& g, int esz, int loader);  // 0: not for the weight-stationary kernel

@@ -368,6 +368,29 @@ conv_status conv_upsample_concat(const void* s0, int32_t c0, int32_t up0,
                                  int32_t dtype, void* y, int32_t n, int32_t ho,
                                  int32_t wo, void* stream);
 
+/* The YOLOv4 neck join read straight by the convolution that follows it
+ * (YOLOv4 on Tenstorrent Wormhole, section 9 "Four custom Tensix kernels",
+ * K4: the join is written in the next convolution's layout; here the
+ * convolution reads the two maps itself and the joined map is never
+ * written). p is a 1x1, stride-1, unpadded, dense layer (BF16 or I8, plain
+ * weights) whose input is the channel concat of conv_upsample_concat:
+ *   x[n][i][j][k]      = s0[n][i >> up0][j >> up0][k]       k < c0
+ *   x[n][i][j][c0 + k] = s1[n][i >> up1][j >> up1][k]       k < c_in - c0
+ *   s0 : device [n][h >> up0][w >> up0][c0] of p's dtype
+ *   s1 : device [n][h >> up1][w >> up1][c_in - c0] of p's dtype
+ *   w, b, y, stream : as for conv_run (y [n][h][w][c_out]).
+ * up flags 0 or 1, h and w even when either is 1, 0 < c0 < c_in
+ * (CONV_E_SHAPE otherwise); c0 and c_in - c0 whole 128-byte blocks (multiples
+ * of 64 for BF16, 128 for I8; CONV_E_UNSUPPORTED otherwise, as for other
+ * layers). s0, s1, w, y 16-byte aligned (b 4-byte); y must not overlap s0,
+ * s1, w or b (CONV_E_ALIAS). Runs the implicit-GEMM kernel with p's tile (the
+ * 64x64 tile when p chose another kernel), the reduction unsplit: the result
+ * equals conv_upsample_concat + conv_run up to the order of the fp32 sums
+ * (bit-equal when p runs that tile unsplit; int8 always). Enqueues one kernel
+ * on `stream`. */
+conv_status conv_run_upcat(const conv_plan* p, const void* s0, int32_t c0, int32_t up0, const void* s1,
+                           int32_t up1, const void* w, const void* b, void* y, void* stream);
+
 /* Name and meaning of a status code ("CONV_OK", "CONV_E_SHAPE: ..."), so a
  * refusal reads as a named failure rather than quiet garbage (nanoinfer
  * README, the bug list). For CONV_E_HIP the text of the last HIP error seen

@@ -461,3 +461,31 @@ def test_run_mosaic_checks_before_launch():
     assert L.conv_run_mosaic(P, T, 0, 10, 15, W, B, T + 64, None) == -5     # y inside the tiles
     stem.close()
     dense.close()
+
+
+def test_run_upcat_checks_before_launch():
+    """conv_run_upcat refuses, before any launch, missing pointers, plans that
+    are not a dense 1x1 stride-1 unpadded bf16/int8 layer, bad up flags and
+    channel splits, splits that are not whole 128-byte blocks, misalignment
+    and an output overlapping an input."""
+    L = _lib.lib()
+    c = Conv2d(1, 40, 40, 512, 256, 1, 1, (1, 1), (0, 0), dtype="bf16", act="mish")
+    odd = Conv2d(1, 41, 40, 512, 256, 1, 1, (1, 1), (0, 0), dtype="bf16", act="mish")
+    k3 = Conv2d(1, 40, 40, 512, 256, 3, 3, (1, 1), (1, 1), dtype="bf16", act="mish")
+    S0, S1, W, B, Y = 0x10000000, 0x20000000, 0x30000000, 0x38000000, 0x40000000
+    P = c._plan
+    assert L.conv_run_upcat(None, S0, 256, 1, S1, 0, W, B, Y, None) == -1
+    assert L.conv_run_upcat(P, None, 256, 1, S1, 0, W, B, Y, None) == -1
+    assert L.conv_run_upcat(P, S0, 256, 1, None, 0, W, B, Y, None) == -1
+    assert L.conv_run_upcat(P, S0, 256, 1, S1, 0, W, B, None, None) == -1
+    assert L.conv_run_upcat(k3._plan, S0, 256, 1, S1, 0, W, B, Y, None) == -3   # not a 1x1 layer
+    assert L.conv_run_upcat(P, S0, 256, 2, S1, 0, W, B, Y, None) == -2         # up flag
+    assert L.conv_run_upcat(odd._plan, S0, 256, 1, S1, 0, W, B, Y, None) == -2  # odd height, upsampled
+    assert L.conv_run_upcat(P, S0, 0, 1, S1, 0, W, B, Y, None) == -2           # empty first map
+    assert L.conv_run_upcat(P, S0, 512, 1, S1, 0, W, B, Y, None) == -2         # empty second map
+    assert L.conv_run_upcat(P, S0, 96, 1, S1, 0, W, B, Y, None) == -3          # 192-byte channel split
+    assert L.conv_run_upcat(P, S0 + 8, 256, 1, S1, 0, W, B, Y, None) == -4
+    assert L.conv_run_upcat(P, S0, 256, 1, S1, 0, W, B + 2, Y, None) == -4
+    assert L.conv_run_upcat(P, S0, 256, 1, S1, 0, W, B, S1 + 4096, None) == -5  # y inside s1
+    for x in (c, odd, k3):
+        x.close()
