@@ -513,6 +513,7 @@ def secondary_measurements(peaks, stacks=True):
     progress("spp, upsample+concat, residual")
     out["spp_bf16"] = spp_measurements(gen)
     out["upcat_bf16"] = upcat_measurements(gen)
+    out["upcat_conv_bf16"] = upcat_conv_measurements(gen)
     out["residual_bf16"] = residual_measurements(gen)
     copy = peaks["copy"]["value"]
     for sec in out.values():
@@ -605,6 +606,49 @@ def upcat_measurements(gen):
                      "us": round(us, 2), "gbs": round(by / (us * 1e-6) / 1e9, 1), "bound": "hbm",
                      "frac_hbm_peak": round(by / (us * 1e-6) / 1e9 / HBM_GBS, 4), "buffer_sets": nsets})
         del srcs, ys
+        torch.cuda.empty_cache()
+    return {"layers": rows}
+
+
+def upcat_conv_measurements(gen):
+    """The neck joins of upcat_measurements followed by their 1x1 convolution
+    (2c -> c channels, Mish): the two-step path (conv_upsample_concat, then
+    conv_run) against conv_run_upcat, which reads both maps itself and never
+    writes the joined map. Same plan, cold buffer sets; bytes_saved = the
+    joined map's write and read."""
+    import torch
+
+    from convolution_conv2d_nhwc_amd import _lib
+    from convolution_conv2d_nhwc_amd.data import Layer
+
+    rows = []
+    for n, (hs, cs) in [(1, (20, 256)), (1, (40, 128)), (16, (20, 256)), (16, (40, 128))]:
+        h = 2 * hs
+        layer = Layer("join_1x1", n, h, h, 2 * cs, cs, 1, 1, 1, 1, 0, 0, 1, "bf16", "bf16", "mish", h, h)
+        conv = _lib.Conv2d.from_layer(layer)
+        w = (torch.randn((cs, 1, 1, 2 * cs), generator=gen, device="cuda") * (1.0 / cs) ** 0.5).to(torch.bfloat16)
+        b = (torch.rand(cs, generator=gen, device="cuda") * 0.2 - 0.1).float()
+        joined = 2 * n * h * h * 2 * cs
+        by = 2 * (n * hs * hs * cs + n * h * h * cs) + w.numel() * 2 + 2 * n * h * h * cs
+        nsets = max(2, min(64, -(-768 * 2 ** 20 // (by + joined))))
+        srcs = [((torch.randn((n, hs, hs, cs), generator=gen, device="cuda")).to(torch.bfloat16),
+                 (torch.randn((n, h, h, cs), generator=gen, device="cuda")).to(torch.bfloat16)) for _ in range(nsets)]
+        xs = [torch.empty((n, h, h, 2 * cs), dtype=torch.bfloat16, device="cuda") for _ in range(nsets)]
+        ys = [conv.empty_output() for _ in range(nsets)]
+
+        def two_step(i):
+            _lib.upsample_concat(srcs[i][0], 1, srcs[i][1], 0, xs[i])
+            conv.run(xs[i], w, b, ys[i])
+
+        us2 = _time_graph([lambda i=i: two_step(i) for i in range(nsets)])
+        usf = _time_graph([lambda i=i: _lib.run_upcat(conv, srcs[i][0], 1, srcs[i][1], 0, w, b, ys[i])
+                           for i in range(nsets)])
+        rows.append({"shape": "%dx%dx%dx%d up + %dx%dx%dx%d -> 1x1 %d" % (n, hs, hs, cs, n, h, h, cs, cs),
+                     "plan": conv.describe().split(" kernel=")[0], "us_two_step": round(us2, 2),
+                     "us_fused": round(usf, 2), "bytes_saved": joined, "buffer_sets": nsets,
+                     "fused_gbs": round(by / (usf * 1e-6) / 1e9, 1)})
+        conv.close()
+        del srcs, xs, ys
         torch.cuda.empty_cache()
     return {"layers": rows}
 
