@@ -64,6 +64,9 @@ CASES = [
     ("yolo640_join_40", 1, 40, 40, 256, 256, 256, 1, 0, "mish"),
     ("yolo640_join_80", 1, 80, 80, 128, 128, 128, 1, 0, "mish"),
     ("second_up_n2_ragged", 2, 18, 26, 64, 128, 96, 0, 1, "relu"),
+    # a 256-byte reduction: the automatic plan is the weight-stationary
+    # kernel, so the join runs on the 64x64 tile
+    ("ws_plan_join", 1, 32, 34, 64, 64, 64, 1, 0, "relu6"),
 ]
 
 
@@ -78,8 +81,11 @@ def test_upcat_conv_bf16(case):
     same_bits(yf, y2, "%s fused vs two-step [%s]" % (name, d))
     xt = torch.from_numpy(xc.view(np.int16)).view(torch.bfloat16)
     H.check_layer_full(lay, xt, t, yf, "%s [%s]" % (name, d))
-    # the automatic plan (any kernel for the two-step path; the fused read on its tile)
+    # the automatic plan (any kernel for the two-step path; the fused read on
+    # its implicit-GEMM tile, or the 64x64 tile)
     xc, t, y2, yf, d = two_step_and_fused(lay, c0, up0, up1, seed=92)
+    if name == "ws_plan_join":
+        assert d.startswith("igemm_ws "), d
     xt = torch.from_numpy(xc.view(np.int16)).view(torch.bfloat16)
     H.check_layer_full(lay, xt, t, yf, "%s auto [%s]" % (name, d))
 
