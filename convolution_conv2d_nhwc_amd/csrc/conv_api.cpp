@@ -104,7 +104,9 @@ int choose_xl(const Geometry& g, int esz, int loader) {
 
 // Split the reduction when the output tiles alone would fill fewer than half
 // of the 256 CUs (under 128 workgroups) and each split still has >= 8 K-tiles
-// of 128 bytes: aim at ~512 workgroups, at most 8 splits. (Splitting layers
+// of 128 bytes: aim at ~448 workgroups, at most 8 splits (the 20x20x512 ->
+// 1024 3x3 layer of the 640x640 stack, 112 tiles: 4 splits measured 0.7 us
+// faster than 5, 6 to 8 slower). (Splitting layers
 // of 128..255 tiles measured slower on MI355X: the partial sums' extra write
 // and read outweigh the occupancy gained, e.g. 177 against 120 us for the
 // 16x40x40x512 3x3 layer on the large-layer kernel.) The splits' raw partial sums go to a
@@ -119,7 +121,7 @@ int choose_xl(const Geometry& g, int esz, int loader) {
 conv_status plan_split_k(conv_plan* p, void* scratch, int64_t scratch_bytes) {
   const Geometry& g = p->g;
   const TileCfg& t = p->path == PATH_XL ? kXlTiles[p->tile] : kTiles[p->tile];
-  const int tco = t.tco, tpx = t.tpx, target = 512, min_per = 8;
+  const int tco = t.tco, tpx = t.tpx, target = 448, min_per = 8;
   const long nwg = (long)((g.cout + tco - 1) / tco) * ((g.m + tpx - 1) / tpx);
   const int nkt = p->kt_per;
   if (nwg >= 128 || nkt < 16 || (g.cout & 3)) return CONV_OK;
