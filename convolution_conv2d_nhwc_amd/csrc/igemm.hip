@@ -35,7 +35,6 @@
 // channels of one pixel, which the epilogue stores as one NHWC vector.
 #include <algorithm>
 #include <cstring>
-#include <vector>
 
 #include "igemm_common.h"
 
@@ -733,37 +732,51 @@ hipError_t launch_fused_tile(const IgArgs& args, dim3 nwg, hipStream_t s) {
 
 }  // namespace
 
+// Distinct channel tiles (*tc) and pixel tiles (*tp) of the run of tile
+// indices [l0, l1) in the grouped order with group size g (see the kernel),
+// counted group by group without visiting the tiles: consecutive indices
+// inside a group cycle through its channel tiles, and the pixel tiles of a
+// run that spans two groups are the union of a tail and a head.
+static void run_tiles(long nco, long npx, long g, long l0, long l1, long* tc, long* tp) {
+  const long span = g * npx;
+  const long g0 = l0 / span, g1 = (l1 - 1) / span;
+  long c = 0;
+  for (long k = g0; k <= g1; ++k) {
+    const long lo = std::max(l0, k * span) - k * span, hi = std::min(l1, (k + 1) * span) - k * span;
+    c += std::min(std::min(nco - k * g, g), hi - lo);
+  }
+  *tc = c;
+  if (g0 == g1) {
+    const long gsz = std::min(nco - g0 * g, g);
+    *tp = (l1 - 1 - g0 * span) / gsz - (l0 - g0 * span) / gsz + 1;
+  } else if (g1 == g0 + 1) {
+    const long a = (l0 - g0 * span) / std::min(nco - g0 * g, g);
+    const long b = (l1 - 1 - g1 * span) / std::min(nco - g1 * g, g);
+    *tp = std::min(npx, (b + 1) + (npx - a));
+  } else {
+    *tp = npx;
+  }
+}
+
 // Channel tiles per group of the implicit-GEMM kernels' tile order. XCD x
 // runs the workgroups [x q + min(x, r), ...) (q = nwg / 8, one more for
 // x < r = nwg % 8): the group size is the one whose runs touch the fewest
 // bytes in all, counting the weight rows of each channel tile (w_bytes /
 // nco) and the input share of each pixel tile (x_bytes / npx) once per XCD
-// that touches it. Grids too large to count keep one order: pixel tiles
-// fastest when the weights outweigh the input.
+// that touches it. Allocation-free (it runs at every launch).
 int co_group_for(const conv_plan* p, int nco, int npx) {
   const long nwg = (long)nco * npx;
-  const int fallback = p->w_bytes > p->x_bytes ? 1 : nco;
-  if (nwg * nco > (1L << 22)) return fallback;
   const long q = nwg / 8, r = nwg % 8;
   const double wt = (double)p->w_bytes / nco, xt = (double)p->x_bytes / npx;
-  std::vector<int> seen_c(nco), seen_p(npx);
-  int best = fallback;
+  int best = p->w_bytes > p->x_bytes ? 1 : nco;
   double best_b = -1;
   for (int g = 1; g <= nco; ++g) {
-    const long span = (long)g * npx;
     double b = 0;
     for (long x = 0; x < 8; ++x) {
-      std::fill(seen_c.begin(), seen_c.end(), 0);
-      std::fill(seen_p.begin(), seen_p.end(), 0);
-      long tc = 0, tp = 0;
       const long lin0 = x * q + std::min(x, r), lin1 = lin0 + q + (x < r);
-      for (long lin = lin0; lin < lin1; ++lin) {
-        const long grp = lin / span, first = grp * g, rem = lin - grp * span;
-        const long gsz = std::min<long>(nco - first, g);
-        const long c = first + rem % gsz, t = rem / gsz;
-        if (!seen_c[c]) seen_c[c] = 1, ++tc;
-        if (!seen_p[t]) seen_p[t] = 1, ++tp;
-      }
+      if (lin1 <= lin0) continue;
+      long tc, tp;
+      run_tiles(nco, npx, g, lin0, lin1, &tc, &tp);
       b += tc * wt + tp * xt;
     }
     if (best_b < 0 || b < best_b - 1e-9 * best_b) {
